@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark: verified draft positions per second on one MI355X, with the HBM
+roofline of the dominant kernel and the CPU oracle timed beside it.
+
+One step = the whole hot path on one batch already resident in HBM:
+  sv_allocate_budget (prefix-confidence products + LDS bitonic top-K)
+  -> sv_verify_batch (row statistics, acceptance rates, accept scan, draw)
+  -> sv_accept_stats.
+Default workload: the 64 x 16 x 151936 bf16 batch at T = 1 with the budget
+keeping every position (K = 1024).  Inputs are synthetic (seeded Gaussian
+logits shaped like the AngelSpec pages' block-drafting workload).  Two input
+copies alternate between steps so that no step finds its logits in the
+256 MB Infinity Cache.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4full]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4full",
+                    choices=["c4full", "c4", "c3", "c3_t0", "c2", "c5"])
+    ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU work budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lossless_draft_verification_softmax_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_digest") != digest:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_packed, depth, tr0, dr0, seconds: float):
+    """The oracle, as it stands, on whole requests of the same batch until
+    about `seconds` of single-threaded CPU work: verified positions per
+    second."""
+    import numpy as np
+    import oracle
+    th = target_packed.float().cpu().numpy().reshape(-1, w.V)
+    dh = w.draft.float().cpu().numpy().reshape(-1, w.V)
+    tok = w.draft_tokens.cpu().numpy()
+    temps = w.temperature.cpu().numpy()
+    dep = depth.cpu().numpy()
+    tr = tr0.cpu().numpy()
+    dr = dr0.cpu().numpy()
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.allocate_budget(w.conf.numpy(), w.K)
+    budget_s = time.perf_counter() - t0
+    positions, elapsed, done = 0, 0.0, 0
+    t0 = time.perf_counter()
+    for r in range(w.B):
+        oracle.verify_batch(th, dh, tr[r:r + 1], dr[r:r + 1], tok[r:r + 1], dep[r:r + 1],
+                            temps[r:r + 1], request_id=np.array([r], np.uint32), D_max=w.D)
+        positions += int(dep[r])
+        done += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= seconds:
+            break
+    return dict(value=positions / elapsed, unit="positions/s", cores=1, kind="oracle",
+                sample=f"{done} of {w.B} requests ({positions} verified positions) of the "
+                       f"{w.name} batch, single-threaded, {elapsed:.1f} s; budget "
+                       f"{budget_s * 1e3:.2f} ms")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(every step fits one MI355X, see the sharding note in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, ROOT)
+    from lossless_draft_verification_softmax_amd import specverify as sv
+    from lossless_draft_verification_softmax_amd import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sv.load()
+    w = synth.make(args.workload, device=dev)
+    B, D, V = w.B, w.D, w.V
+    esize = 2 if w.dtype == torch.bfloat16 else 4
+
+    conf = (w.conf if w.conf is not None else torch.ones((B, D))).to(dev).contiguous()
+    K = w.K if w.K is not None else B * D
+    bud = sv.allocate_budget(conf, K)
+    torch.cuda.synchronize()
+    depth_h = bud["depth"].cpu()
+    # Target logits only for the kept positions, packed in the budget's order
+    # (what a target forward over the surviving tokens produces); the drafter
+    # produced all D positions, so draft rows stay padded.
+    idx = torch.cat([torch.arange(int(n) + 1, device=dev) + r * (D + 1)
+                     for r, n in enumerate(depth_h.tolist())])
+    copies = []
+    for c in range(args.copies):
+        tgt = w.target.reshape(-1, V).index_select(0, idx).contiguous()
+        dft = w.draft.clone() if c else w.draft
+        copies.append((tgt, dft))
+    dr0 = torch.arange(B, dtype=torch.int64, device=dev) * D
+    verifiers = []
+    for tgt, dft in copies:
+        v = sv.Verifier(B, D, V, dev, alpha=True, diag=True)
+        v.prepare(tgt, dft, bud["target_row0"], dr0, w.draft_tokens, bud["depth"], w.temperature,
+                  seed=0, step=0)
+        verifiers.append(v)
+    stats_out = None
+
+    n_pos = int(depth_h.sum())
+    n_t0 = int((w.temperature == 0).sum())
+    temps_h = w.temperature.cpu()
+    draft_rows = int(sum(int(n) for n, t in zip(depth_h.tolist(), temps_h.tolist()) if t > 0))
+    target_rows = n_pos + B
+    rowstats_bytes = (target_rows + draft_rows) * V * esize
+    alpha_rows = draft_rows
+    step_bytes = rowstats_bytes + n_pos * 4  # + draft token ids
+
+    def step(v):
+        nonlocal stats_out
+        sv.allocate_budget(conf, K, out=bud)
+        out = v.run()
+        stats_out = sv.accept_stats(bud["depth"], out.alpha, out.accepted_len, D)
+
+    for i in range(args.warmup):
+        step(verifiers[i % len(verifiers)])
+    torch.cuda.synchronize()
+
+    nev = sv.SV_NUM_STAGE_EVENTS
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+              for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    for evs in events:
+        for e in evs:
+            e.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        v = verifiers[i % len(verifiers)]
+        v.set_stage_events(events[i])
+        step(v)
+    stop.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    for v in verifiers:
+        v.set_stage_events(None)
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    stage_ms = [sum(evs[j].elapsed_time(evs[j + 1]) for evs in events) / args.steps
+                for j in range(nev - 1)]
+    rowstats_ms = stage_ms[0]
+
+    achieved = rowstats_bytes / (rowstats_ms * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = measured_traffic("k_rowstats", args.workload, digest)
+    value = n_pos * args.steps / (total_ms * 1e-3)
+    res = {
+        "metric": "verified draft positions/sec @ V=151,936 bf16 + % of MI355X HBM roofline",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if esize == 2 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={B} requests x D={D} draft positions, "
+                               f"V={V} {'bf16' if esize == 2 else 'fp32'} logits, "
+                               f"T={'mixed' if w.temperature.unique().numel() > 1 else float(temps_h[0])}, "
+                               f"budget K={K}",
+                   "batch": B, "depth": D, "vocab": V, "verified_positions": n_pos,
+                   "budget_K": K, "greedy_requests": n_t0},
+        "roofline": {"bound": "hbm", "kernel": "k_rowstats",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": rowstats_bytes,
+                     "avg_launch_us": round(rowstats_ms * 1e3, 2)},
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "stages_us": {"rowstats": round(stage_ms[0] * 1e3, 2), "alpha": round(stage_ms[1] * 1e3, 2),
+                      "accept": round(stage_ms[2] * 1e3, 2), "draw": round(stage_ms[3] * 1e3, 2)},
+        "alpha_pass_GBps": round(alpha_rows * 2 * V * esize / max(stage_ms[1], 1e-9) / 1e6, 1),
+        "wall_s": round(wall_s, 3),
+        "mean_accepted_length": round(float(stats_out["summary"][0]), 4),
+        "expected_mean_accepted_length": round(float(stats_out["summary"][1]), 4),
+        "source_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, copies[0][0], bud["depth"], bud["target_row0"],
+                                           dr0, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

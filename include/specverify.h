@@ -1,0 +1,218 @@
+/*
+ * specverify.h -- C ABI of libspecverify: batched lossless verification of
+ * speculative-decoding drafts and the batch-shared verification budget, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the AngelSpec pages:
+ *  - "AngelSpec: specialize the drafter, share the verification budget"
+ *    (ai.thesatyajit.com): intro (the target verifies every draft in one pass
+ *    and only emits what it would have sampled), section "MTP: fix position 2
+ *    and 3" (equation L_e2e: one rejection invalidates every later position,
+ *    so accepted length is a sum of prefix products of acceptance rates),
+ *    section "D-cut" (Figure 3, equations A-hat and K_rho: prefix-confidence
+ *    products, flattened over the batch, global top-K).
+ *  - "Tencent open-sources AngelSpec" (tradepoint.io): section "Why one
+ *    universal drafter underperforms" (lossless rejection sampling in one
+ *    target forward), section "The MTP path" (greedy T = 0 results, MAL).
+ * The accept rule u < min(1, p/q), the correction draw from
+ * normalize(max(0, p - q)) and the bonus draw from p are the standard
+ * speculative-sampling rule that the pages call lossless rejection sampling.
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *    asynchronous and stream-ordered; the library never synchronises the
+ *    host.  Results are ready when the stream reaches them.
+ *  - Host-checkable argument problems return an error status before any GPU
+ *    work is queued (nothing is written).  Launch failures return
+ *    SV_ERR_DEVICE.  Problems that only the data reveal (a NaN row, a token
+ *    id out of range) are reported per request in sv_diag.bits, with that
+ *    request's outputs set to "nothing emitted".
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, negative size, D_max > 64 ... */
+  SV_ERR_UNSUPPORTED = 2,        /* misaligned rows, unknown dtype or flag         */
+  SV_ERR_WORKSPACE_TOO_SMALL = 3,
+  SV_ERR_DEVICE = 4              /* a HIP launch failed                            */
+} sv_status;
+
+typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
+
+/* Largest draft depth per request (the first-rejection scan is one 64-lane
+ * wavefront ballot). */
+#define SV_MAX_DEPTH 64
+/* Largest B * D_max the single-workgroup budget sort accepts. */
+#define SV_MAX_BUDGET_POSITIONS 4096
+
+/* Number of stage events sv_verify_batch records when asked to. */
+#define SV_NUM_STAGE_EVENTS 5
+
+/* sv_verify_args.flags */
+#define SV_FLAG_FORCE_FP64_DRAW 1u /* take every T > 0 draw on the float64 path */
+
+/* sv_diag.bits */
+#define SV_BIT_BAD_DEPTH 1u        /* depth[r] outside [0, D_max]                      */
+#define SV_BIT_BAD_TOKEN 2u        /* a draft token outside [0, V)                     */
+#define SV_BIT_BAD_ROW 4u          /* a verified row has NaN / +inf or is all -inf     */
+#define SV_BIT_RESIDUAL_ZERO 8u    /* residual mass was zero: the draw used p          */
+#define SV_BIT_BAD_TEMPERATURE 16u /* temperature[r] negative, NaN or infinite         */
+#define SV_BIT_FP64_DRAW 32u       /* the draw was recomputed in float64               */
+
+/* Per-request diagnostics (written when sv_verify_args.diag != NULL). */
+typedef struct sv_diag {
+  float accept_margin; /* min over tested positions of |u - p(d)/q(d)| (T > 0), else +inf */
+  float draw_margin;   /* distance of u*R to the nearest CDF boundary of the draw (T > 0) */
+  uint32_t bits;       /* SV_BIT_* */
+  int32_t reserved;
+} sv_diag;
+
+/* Human-readable name of a status code (static string). */
+const char* sv_status_string(sv_status status);
+
+/* Library version string (static). */
+const char* sv_version(void);
+
+/* K_rho(B) = max(B, ceil(rho * B * (D + 1))): the verification budget of
+ * equation K_rho ("AngelSpec: specialize the drafter...", section "D-cut").
+ * Returns -1 for B < 0, D < 0 or rho outside [0, 1]. */
+int64_t sv_k_rho(int32_t B, int32_t D, double rho);
+
+/* ---------------------------------------------------------------------------
+ * sv_allocate_budget -- the D-cut budget ("AngelSpec: specialize the
+ * drafter...", section "D-cut", Figure 3 and equation A-hat).
+ *
+ * For request r and draft position k (0-based) the score is the prefix
+ * confidence product s[r][k] = c[r][0] * c[r][1] * ... * c[r][k], multiplied
+ * left to right in float32 (confidences are clamped to [0, 1], NaN reads as
+ * 0).  All (r, k < max_depth[r]) are ranked by score, ties by lower r then
+ * lower k, and the first K are kept (K clamped to [0, sum max_depth]).  Since
+ * scores never increase along a request, each request keeps a prefix:
+ *   depth[r]       = number of kept positions of r,
+ *   draft_row0[r]  = sum_{i<r} depth[i]         (packed draft rows),
+ *   target_row0[r] = sum_{i<r} (depth[i] + 1)   (packed target rows: the
+ *                    kept positions plus the bonus row).
+ * utility (optional, float[2]) = (sum of kept scores, sum of all scores).
+ *
+ * conf: float [B, D_max] row-major.  max_depth: int32 [B] or NULL (= D_max).
+ * Requires B >= 0, D_max >= 0, B * D_max <= SV_MAX_BUDGET_POSITIONS.
+ * ------------------------------------------------------------------------- */
+sv_status sv_allocate_budget(const float* conf, int32_t B, int32_t D_max,
+                             const int32_t* max_depth, int64_t K, int32_t* depth,
+                             int64_t* draft_row0, int64_t* target_row0, float* utility,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sv_verify_batch -- lossless verification of a batch of drafted blocks
+ * (tradepoint.io page, "Why one universal drafter underperforms": the target
+ * verifies the drafts in one pass with rejection sampling; "AngelSpec:
+ * specialize the drafter...", section "MTP": one rejection invalidates every
+ * later position).
+ *
+ * Request r has n = depth[r] draft tokens d_k = draft_tokens[r * D_max + k]
+ * (k < n), target rows target_row0[r] + k for k = 0..n (row n scores the
+ * token after the block: the bonus row) and draft rows draft_row0[r] + k for
+ * k < n.  Row i of a logits buffer starts at element i * row_stride.  With
+ * s = 1 / temperature[r], p_k = softmax(s * target row k),
+ * q_k = softmax(s * draft row k) over all V entries (-inf entries are
+ * masked tokens).
+ *
+ * T > 0: position k keeps d_k if u_k < p_k(d_k) / q_k(d_k), where
+ *   (w0, w1, w2, w3) = Philox4x32-10(key = (seed low, seed high),
+ *                                    counter = (k, request_id[r], step, 0))
+ *   and u_k = (w0 >> 8) * 2^-24.  tau = first rejected position, or n.
+ *   If tau < n the token emitted at tau is drawn from normalize(max(0, p - q))
+ *   of position tau, else from p_n (the bonus row); the draw takes the
+ *   smallest y whose cumulative mass exceeds u' * R, u' = (w1 >> 8) * 2^-24
+ *   of counter (tau, ...), R the total mass.  The draw is computed in
+ *   float32 and recomputed in float64 whenever the float32 distance to a CDF
+ *   boundary is below 1e-5.
+ * T = 0: position k keeps d_k if d_k == argmax p_k (lowest index on ties);
+ *   the token at tau is argmax of target row tau.  Draft rows are not read
+ *   (draft_logits may be NULL when every temperature is 0).
+ *
+ * Outputs: accepted_len[r] = tau; out_tokens[r * (D_max + 1) + i] = d_i for
+ * i < tau, the drawn token at i = tau, -1 after; num_out[r] = tau + 1.
+ * alpha (optional, float [B, D_max]): the acceptance rate
+ * sum_y min(p_k(y), q_k(y)) = 1 - TV(p_k, q_k) of every k < n (at T = 0:
+ * 1 if d_k == argmax p_k else 0); 0 for k >= n.  diag (optional, [B]).
+ * An invalid request (see SV_BIT_*) gets accepted_len 0, num_out 0 and
+ * out_tokens all -1.
+ *
+ * Layout requirements: logits base pointers 16-byte aligned and row_stride
+ * a multiple of 8 elements (bf16) / 4 elements (fp32), row_stride >= V;
+ * 1 <= V < 2^31; 0 <= D_max <= SV_MAX_DEPTH; row indices must address rows
+ * inside the caller's buffers.  workspace: device memory of at least
+ * sv_verify_workspace_bytes(B, D_max, V) bytes, 256-byte aligned; its
+ * contents need no initialisation and are scratch after the call.
+ * ------------------------------------------------------------------------- */
+typedef struct sv_verify_args {
+  sv_dtype dtype;
+  int32_t B;
+  int32_t D_max;
+  int32_t reserved0;
+  int64_t V;
+  int64_t row_stride;
+  const void* target_logits;
+  const int64_t* target_row0;  /* [B] */
+  const void* draft_logits;
+  const int64_t* draft_row0;   /* [B]; may be NULL when every temperature is 0 */
+  const int32_t* draft_tokens; /* [B, D_max] */
+  const int32_t* depth;        /* [B] */
+  const float* temperature;    /* [B] */
+  const uint32_t* request_id;  /* [B] or NULL: request_id = r */
+  uint64_t seed;
+  uint32_t step;
+  uint32_t flags;              /* SV_FLAG_* */
+  int32_t* accepted_len;       /* [B] */
+  int32_t* out_tokens;         /* [B, D_max + 1] */
+  int32_t* num_out;            /* [B] */
+  float* alpha;                /* [B, D_max] or NULL */
+  sv_diag* diag;               /* [B] or NULL */
+  void* workspace;
+  size_t workspace_bytes;
+  /* NULL, or SV_NUM_STAGE_EVENTS hipEvent_t handles (created by the caller)
+   * that are recorded on `stream` at the stage boundaries: [0] before the
+   * row-statistics pass, [1] after it, [2] after the acceptance-rate pass,
+   * [3] after the accept scan, [4] after the draw.  For timing only. */
+  void* const* stage_events;
+} sv_verify_args;
+
+/* Device scratch needed by sv_verify_batch for these sizes (0 on bad sizes). */
+size_t sv_verify_workspace_bytes(int32_t B, int32_t D_max, int64_t V);
+
+sv_status sv_verify_batch(const sv_verify_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sv_accept_stats -- acceptance statistics of one verified batch (equation
+ * L_e2e of "AngelSpec: specialize the drafter...", section "MTP", and the
+ * MAL / mean-acceptance figures of the tradepoint.io page, "The MTP path",
+ * which satisfy MAL = 1 + D * mean acceptance).
+ *
+ * Inputs (device): depth[B], alpha[B, D_max] (may be NULL), accepted_len[B].
+ * Outputs (device float, each optional):
+ *   expected_len[B]    E[tau_r] = sum_{m < n_r} prod_{k <= m} alpha[r][k]
+ *   per_depth[3*D_max] #requests that tested position k, #that kept it,
+ *                      mean alpha at k over requests with depth > k
+ *   summary[4]         (mean(tau + 1), 1 + mean E[tau], sum tau / sum n, sum n)
+ * ------------------------------------------------------------------------- */
+sv_status sv_accept_stats(const int32_t* depth, const float* alpha, const int32_t* accepted_len,
+                          int32_t B, int32_t D_max, float* expected_len, float* per_depth,
+                          float* summary, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,181 @@
+// sv_device.hpp -- device helpers shared by the specverify kernels (gfx950).
+//
+// Wave64 cross-lane reductions use DPP row operations for the 16-lane rows
+// and the gfx950 permlane swaps across rows; 16-byte vector loads feed the
+// streaming loops.  Nothing here allocates or synchronises the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Element access.  bfloat16 is the upper half of an IEEE float32, so a packed
+// pair widens with one shift (low half) or one mask (high half).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+struct Bf16 {
+  using Storage = uint16_t;
+  static constexpr int kPerVec = 8;  // elements per 16-byte load
+  static constexpr uint32_t kNegInfWord = 0xff80ff80u;  // two bf16 -inf
+  __device__ static __forceinline__ float load1(const Storage* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+  }
+  __device__ static __forceinline__ void unpack(const uint4& v, float f[8]) {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+  }
+};
+
+struct F32 {
+  using Storage = float;
+  static constexpr int kPerVec = 4;
+  static constexpr uint32_t kNegInfWord = 0xff800000u;  // fp32 -inf
+  __device__ static __forceinline__ float load1(const Storage* p, int64_t i) { return p[i]; }
+  __device__ static __forceinline__ void unpack(const uint4& v, float f[4]) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+};
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// IEEE 754-2019 maximum (NaN-propagating): v_maximum3_f32 on gfx950, so a
+// NaN anywhere in a row survives into its maximum.
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// Raw hardware 2^x (v_exp_f32): about 1 ulp; results below 2^-126 may flush,
+// which is far under what any sum here can resolve.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16 lanes
+
+// The other row of a row pair (lanes 0-15 <-> 16-31, 32-47 <-> 48-63) and
+// the other half of the wave (0-31 <-> 32-63), via the gfx950 permlane
+// swaps.  Each swap returns the two operands with rows exchanged; combining
+// both results gives every lane the pair's two values.
+template <typename Op>
+__device__ __forceinline__ float combine_rows16(float v, Op op) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename Op>
+__device__ __forceinline__ float combine_halves32(float v, Op op) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// All-reduce of a commutative, associative op across the 64 lanes; every lane
+// gets the result.  The reduction tree is fixed, so results are reproducible.
+template <typename Op>
+__device__ __forceinline__ float wave_allreduce(float v, Op op) {
+  v = op(v, dpp_f<kDppQuadXor1>(v));
+  v = op(v, dpp_f<kDppQuadXor2>(v));
+  v = op(v, dpp_f<kDppHalfMirror>(v));
+  v = op(v, dpp_f<kDppMirror>(v));
+  v = combine_rows16(v, op);
+  v = combine_halves32(v, op);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  return wave_allreduce(v, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_allreduce(v, [](float a, float b) { return vmax(a, b); });
+}
+
+// Shuffle-based fallback for 64-bit payloads (ds_bpermute, no LDS storage).
+__device__ __forceinline__ double shfl_xor_d(double v, int mask) {
+  int2 p = *reinterpret_cast<int2*>(&v);
+  p.x = __shfl_xor(p.x, mask);
+  p.y = __shfl_xor(p.y, mask);
+  return *reinterpret_cast<double*>(&p);
+}
+
+// ---------------------------------------------------------------------------
+// Online softmax state over a row slice, in the log2 domain: the slice's
+// maximum m (raw logit units) and z = sum 2^((x - m) * sl), sl = log2(e) / T.
+struct SoftmaxPart {
+  float m;
+  float z;
+};
+
+// Merge of two partial states (the associative (max, rescaled sum) rule).
+__device__ __forceinline__ SoftmaxPart merge_parts(SoftmaxPart a, SoftmaxPart b, float sl) {
+  float m = vmax(a.m, b.m);
+  if (m == -INFINITY) return {m, 0.0f};
+  // A part whose max is -inf holds only masked entries: it adds nothing.
+  float za = (a.m == -INFINITY) ? 0.0f : a.z * exp2_fast((a.m - m) * sl);
+  float zb = (b.m == -INFINITY) ? 0.0f : b.z * exp2_fast((b.m - m) * sl);
+  return {m, za + zb};
+}
+
+__device__ __forceinline__ SoftmaxPart wave_merge(SoftmaxPart p, float sl) {
+  float m = wave_max(p.m);
+  float z = (p.m == -INFINITY || m == -INFINITY) ? 0.0f : p.z * exp2_fast((p.m - m) * sl);
+  // NaN maxima propagate through vmax; keep the NaN so the row reads invalid.
+  if (m != m) z = m;
+  return {m, wave_sum(z)};
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies whose high words are xored with the other two counter
+// words and the round key, the key advancing by the Weyl increments
+// 0x9E3779B9 (golden ratio) and 0xBB67AE85 (sqrt 3 - 1) between rounds.
+struct Philox4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t a_lo = 0xD2511F53u * c0;
+    const uint32_t a_hi = __umulhi(0xD2511F53u, c0);
+    const uint32_t b_lo = 0xCD9E8D57u * c2;
+    const uint32_t b_hi = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = b_hi ^ c1 ^ k0;
+    const uint32_t n2 = a_hi ^ c3 ^ k1;
+    c0 = n0;
+    c1 = b_lo;
+    c2 = n2;
+    c3 = a_lo;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {{c0, c1, c2, c3}};
+}
+
+// Uniform on the 2^-24 grid from the top 24 bits of a word (exact in fp32).
+__device__ __forceinline__ float u24(uint32_t w) {
+  return static_cast<float>(w >> 8) * (1.0f / 16777216.0f);
+}
+
+}  // namespace sv

@@ -1,0 +1,127 @@
+// sv_internal.hpp -- launch parameters, per-request draw state and the
+// workspace layout of libspecverify.  Used by the library's own sources only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+enum DrawMode : int32_t { kDrawNone = 0, kDrawResidual = 1, kDrawBonus = 2 };
+
+// What k_accept leaves for the draw kernels of one request.
+struct DrawState {
+  int32_t mode;     // DrawMode
+  int32_t tau;      // position of the emitted draw
+  int64_t prow;     // target row of the draw
+  int64_t qrow;     // draft row (residual draws)
+  float sl;         // log2(e) / T
+  float T;          // temperature
+  float mp, lzp;    // target row: max and log2 of sum 2^((x - max) sl)
+  float mq, lzq;    // draft row: the same
+  float zp;         // target row: sum 2^((x - max) sl)
+  float u;          // draw uniform (word 1 of the Philox block at tau)
+  int32_t need64;   // set when the float32 draw must be recomputed in float64
+  float margin;     // float32 CDF margin of the draw
+  uint32_t bits;
+  int32_t pad;
+};
+
+struct VerifyParams {
+  sv_dtype dtype;
+  int32_t B, D;            // batch, D_max
+  int64_t V, stride;       // vocabulary, row stride (elements)
+  int32_t S1, seg1;        // statistics pass: segments per row, segment length
+  int32_t S2, seg2;        // draw: segments per row, segment length
+  uint32_t seed_lo, seed_hi, step, flags;
+  const void* target;
+  const void* draft;
+  const int64_t* target_row0;
+  const int64_t* draft_row0;
+  const int32_t* tokens;
+  const int32_t* depth;
+  const float* temperature;
+  const uint32_t* request_id;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  int32_t* num_out;
+  float* alpha;
+  sv_diag* diag;
+  void* const* events;     // SV_NUM_STAGE_EVENTS hipEvent_t or null
+  // workspace
+  float2* part_p;    // [U][S1]  (max, sum) or (max, arg max bits) at T = 0
+  float2* part_q;    // [U][S1]
+  float* part_a;     // [U][S1]  partial sum min(p, q)
+  DrawState* req;    // [B]
+  float* seg_w32;    // [B][S2]
+  double* seg_zp64;  // [B][S2]
+  double* seg_zq64;  // [B][S2]
+  double* seg_w64;   // [B][S2]
+};
+
+// ---- launch geometry (host) -------------------------------------------------
+
+// Statistics pass: enough (row, segment) workgroups to fill 256 CUs several
+// times over, but segments of at least 2048 elements.
+inline void stats_geometry(int32_t B, int32_t D, int64_t V, int32_t* S1, int32_t* seg1) {
+  const int64_t units = (int64_t)B * (D + 1);
+  int64_t s = units > 0 ? (4096 + units - 1) / units : 1;
+  int64_t by_len = V / 2048;
+  if (by_len < 1) by_len = 1;
+  if (s > by_len) s = by_len;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  int64_t len = (V + s - 1) / s;
+  len = (len + 7) / 8 * 8;
+  *S1 = (int32_t)s;
+  *seg1 = (int32_t)len;
+}
+
+// Draw: segments of about one to two 2048-element tiles, at most 64.
+inline void draw_geometry(int64_t V, int32_t* S2, int32_t* seg2) {
+  int64_t s = (V + 2047) / 2048;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  int64_t len = (V + s - 1) / s;
+  len = (len + 7) / 8 * 8;
+  *S2 = (int32_t)s;
+  *seg2 = (int32_t)len;
+}
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct WorkspaceLayout {
+  size_t part_p, part_q, part_a, req, seg_w32, seg_zp64, seg_zq64, seg_w64, total;
+};
+
+inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
+  int32_t S1, seg1, S2, seg2;
+  stats_geometry(B, D, V, &S1, &seg1);
+  draw_geometry(V, &S2, &seg2);
+  const size_t U = (size_t)B * (size_t)(D + 1);
+  WorkspaceLayout L;
+  size_t off = 0;
+  L.part_p = off; off += align256(U * S1 * sizeof(float2));
+  L.part_q = off; off += align256(U * S1 * sizeof(float2));
+  L.part_a = off; off += align256(U * S1 * sizeof(float));
+  L.req = off; off += align256((size_t)B * sizeof(DrawState));
+  L.seg_w32 = off; off += align256((size_t)B * S2 * sizeof(float));
+  L.seg_zp64 = off; off += align256((size_t)B * S2 * sizeof(double));
+  L.seg_zq64 = off; off += align256((size_t)B * S2 * sizeof(double));
+  L.seg_w64 = off; off += align256((size_t)B * S2 * sizeof(double));
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_verify(const VerifyParams& p, hipStream_t stream);
+hipError_t launch_budget(const float* conf, int32_t B, int32_t D, const int32_t* max_depth,
+                         int64_t K, int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
+                         float* utility, hipStream_t stream);
+hipError_t launch_stats(const int32_t* depth, const float* alpha, const int32_t* accepted_len,
+                        int32_t B, int32_t D, float* expected_len, float* per_depth,
+                        float* summary, hipStream_t stream);
+
+}  // namespace sv

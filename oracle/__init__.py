@@ -26,6 +26,7 @@ BIT_BAD_DEPTH = 1
 BIT_BAD_TOKEN = 2
 BIT_BAD_ROW = 4
 BIT_RESIDUAL_ZERO = 8
+BIT_BAD_TEMPERATURE = 16
 
 
 def build() -> str:

@@ -318,6 +318,7 @@ int svo_verify_batch(const float* target, const float* draft, int64_t V, int64_t
     if (draws) draws[r] = 0;
 
     if (n < 0 || n > D_max) b |= SVO_BIT_BAD_DEPTH;
+    if (!(T >= 0.0f) || isinf(T)) b |= SVO_BIT_BAD_TEMPERATURE;
     if (!b) {
       for (int32_t k = 0; k < n; ++k)
         if (d[k] < 0 || (int64_t)d[k] >= V) b |= SVO_BIT_BAD_TOKEN;

@@ -51,7 +51,8 @@ enum {
   SVO_BIT_BAD_DEPTH = 1u,      /* depth outside [0, D_max]                       */
   SVO_BIT_BAD_TOKEN = 2u,      /* a draft token id outside [0, V)                */
   SVO_BIT_BAD_ROW = 4u,        /* a verified row holds NaN / +inf, or only -inf  */
-  SVO_BIT_RESIDUAL_ZERO = 8u   /* residual mass was zero; the target row was used */
+  SVO_BIT_RESIDUAL_ZERO = 8u,  /* residual mass was zero; the target row was used */
+  SVO_BIT_BAD_TEMPERATURE = 16u /* temperature negative, NaN or infinite         */
 };
 
 /* ---- counter-based random numbers ---------------------------------------- */

@@ -1,0 +1,110 @@
+"""The C ABI library loads and exports every entry point include/specverify.h
+declares; argument validation (which runs before any HIP call) returns the
+documented status codes.  No compute call is made: this runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def sv():
+    from lossless_draft_verification_softmax_amd import specverify
+    if not os.path.exists(specverify.LIB_PATH):
+        from lossless_draft_verification_softmax_amd import build
+        build.build()
+    return specverify
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(sv):
+    lib = sv.load()
+    names = declared_functions()
+    assert set(names) == set(sv.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(sv):
+    assert sv.status_string(0) == "ok"
+    assert "workspace" in sv.status_string(3)
+    assert "gfx950" in sv.load().sv_version().decode()
+
+
+def test_k_rho_matches_equation(sv):
+    path = os.path.join(ROOT, "tests", "golden", "k_rho.txt")
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            B, D, rho, K = line.split()
+            assert sv.k_rho(int(B), int(D), float(rho)) == int(K)
+    assert sv.k_rho(-1, 3, 0.5) == -1
+    assert sv.k_rho(4, 3, 1.5) == -1
+
+
+def test_workspace_bytes(sv):
+    assert sv.workspace_bytes(64, 16, 151936) > 0
+    assert sv.workspace_bytes(64, 16, 151936) % 256 == 0
+    assert sv.workspace_bytes(64, 65, 151936) == 0
+    assert sv.workspace_bytes(-1, 3, 10) == 0
+    assert sv.workspace_bytes(4, 3, 0) == 0
+
+
+def _args(sv, **kw):
+    a = sv.SvVerifyArgs()
+    a.dtype = sv.SV_DTYPE_BF16
+    a.B, a.D_max, a.V, a.row_stride = 2, 3, 64, 64
+    fake = 1 << 20  # 16-byte aligned, never dereferenced: validation fails first
+    for f in ("target_logits", "target_row0", "draft_logits", "draft_row0", "draft_tokens",
+              "depth", "temperature", "accepted_len", "out_tokens", "num_out"):
+        setattr(a, f, fake)
+    a.workspace = fake
+    a.workspace_bytes = 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def call(sv, a):
+    return sv.load().sv_verify_batch(ctypes.byref(a), None)
+
+
+def test_verify_validation_codes(sv):
+    lib = sv.load()
+    assert lib.sv_verify_batch(None, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv, B=-1)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv, D_max=65)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv, V=0)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv, row_stride=32)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv, dtype=7)) == sv.SV_ERR_UNSUPPORTED
+    assert call(sv, _args(sv, flags=2)) == sv.SV_ERR_UNSUPPORTED
+    assert call(sv, _args(sv, target_logits=None)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv, draft_row0=None)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv, target_logits=(1 << 20) + 2)) == sv.SV_ERR_UNSUPPORTED
+    assert call(sv, _args(sv, V=60, row_stride=60)) == sv.SV_ERR_UNSUPPORTED
+    assert call(sv, _args(sv, workspace=None)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv, workspace=(1 << 20) + 16)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(sv, _args(sv)) == sv.SV_ERR_WORKSPACE_TOO_SMALL
+    assert call(sv, _args(sv, B=0)) == sv.SV_OK  # empty batch: nothing to do
+
+
+def test_budget_and_stats_validation_codes(sv):
+    lib = sv.load()
+    fake = 1 << 20
+    assert lib.sv_allocate_budget(fake, -1, 3, None, 4, fake, None, None, None, None) == 1
+    assert lib.sv_allocate_budget(fake, 64, 65, None, 4, fake, None, None, None, None) == 1
+    assert lib.sv_allocate_budget(fake, 5000, 0, None, 4, fake, None, None, None, None) == 1
+    assert lib.sv_allocate_budget(None, 4, 3, None, 4, fake, None, None, None, None) == 1
+    assert lib.sv_allocate_budget(fake, 4, 3, None, 4, None, None, None, None, None) == 1
+    assert lib.sv_allocate_budget(fake, 0, 3, None, 4, None, None, None, None, None) == 0
+    assert lib.sv_accept_stats(fake, None, fake, 4, 65, None, None, None, None) == 1
+    assert lib.sv_accept_stats(None, None, fake, 4, 3, None, None, None, None) == 1
+    assert lib.sv_accept_stats(None, None, None, 0, 3, None, None, None, None) == 0
