@@ -184,8 +184,9 @@ typedef struct sv_verify_args {
   size_t workspace_bytes;
   /* NULL, or SV_NUM_STAGE_EVENTS hipEvent_t handles (created by the caller)
    * that are recorded on `stream` at the stage boundaries: [0] before the
-   * row-statistics pass, [1] after it, [2] after the acceptance-rate pass,
-   * [3] after the accept scan, [4] after the draw.  For timing only. */
+   * work-list planner, [1] after it, [2] after the row pass (row statistics
+   * and acceptance rates), [3] after the accept scan, [4] after the draw.
+   * For timing only. */
   void* const* stage_events;
 } sv_verify_args;
 

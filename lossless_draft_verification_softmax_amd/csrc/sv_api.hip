@@ -4,12 +4,33 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "specverify.h"
 #include "sv_internal.hpp"
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device (one persistent row-pass workgroup
+// each); cached per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 sv_status validate_verify(const sv_verify_args* a, size_t* need) {
   if (!a) return SV_ERR_INVALID_ARGUMENT;
@@ -108,7 +129,14 @@ sv_status sv_verify_batch(const sv_verify_args* a, void* stream) {
   p.seg_zp64 = reinterpret_cast<double*>(ws + L.seg_zp64);
   p.seg_zq64 = reinterpret_cast<double*>(ws + L.seg_zq64);
   p.seg_w64 = reinterpret_cast<double*>(ws + L.seg_w64);
-  const hipError_t e = sv::launch_verify(p, static_cast<hipStream_t>(stream));
+  p.fb_count = reinterpret_cast<int32_t*>(ws + L.fb_count);
+  p.fb_list = reinterpret_cast<int32_t*>(ws + L.fb_list);
+  p.plan_pairs = reinterpret_cast<uint32_t*>(ws + L.plan_pairs);
+  p.plan_singles = reinterpret_cast<uint32_t*>(ws + L.plan_singles);
+  p.plan_counts = reinterpret_cast<int32_t*>(ws + L.plan_counts);
+  const int grid = device_cu_count();
+  if (grid <= 0) return SV_ERR_DEVICE;
+  const hipError_t e = sv::launch_verify(p, grid, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 

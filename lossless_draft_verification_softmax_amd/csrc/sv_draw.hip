@@ -1,0 +1,520 @@
+// sv_draw.hip -- the emitted token at the stop position: inverse-CDF draw
+// from normalize(max(0, p - q)) after a rejection, or from p after a fully
+// accepted block (the standard rejection-sampling rule behind the lossless
+// verification of the tradepoint.io page, "Why one universal drafter
+// underperforms").
+//
+// The row is cut into tiles of 2048 elements (one 16-byte load of bf16 per
+// thread of a 256-thread workgroup).  A tile's mass is the last value of a
+// fixed-order block scan of its weights, so the pass that finds the crossing
+// tile and the pass that scans inside it agree bit for bit.
+//   k_draw_mass32   float32 mass of every tile of every request's draw row
+//   k_draw_pick32   scan of the tile masses -> crossing tile -> LDS block scan
+//                   inside it -> token.  A draw whose float32 CDF margin is
+//                   under 1e-5 (or that rounding leaves undecided) is queued
+//                   for float64.
+//   k_draw_z64      float64 normalisers (tile partials) of queued requests
+//   k_draw_mass64   float64 tile masses of queued requests
+//   k_draw_pick64   the float64 pick
+// The float64 kernels walk the queue on a fixed grid, so an empty queue costs
+// one short dispatch each.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "specverify.h"
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+
+namespace sv {
+
+constexpr int kDrawThreads = 256;
+constexpr int kPer = 8;  // elements per thread per tile
+constexpr float kDrawMargin32 = 1e-5f;
+constexpr int kQueueGrid = 2048;
+
+// Eight consecutive logits starting at i0 (< hi); entries at or past hi read
+// as -inf, which gives them weight 0.
+template <typename E>
+__device__ __forceinline__ void load8(const typename E::Storage* row, int64_t i0, int64_t hi,
+                                      float (&x)[kPer]) {
+  if (i0 + kPer <= hi) {
+    if constexpr (E::kPerVec == 8) {
+      E::unpack(load16(row + i0), x);
+    } else {
+      float a[4], b[4];
+      E::unpack(load16(row + i0), a);
+      E::unpack(load16(row + i0 + 4), b);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = a[j];
+        x[4 + j] = b[j];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) x[j] = (i0 + j < hi) ? E::load1(row, i0 + j) : -INFINITY;
+  }
+}
+
+// Fixed-order block scan (Hillis-Steele in each wavefront, wave totals in
+// order).  Returns the inclusive value; *total gets the block total.
+template <typename T>
+__device__ __forceinline__ T scan256(T v, T* lds, T* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    T o;
+    if constexpr (sizeof(T) == 8) {
+      int2 q = *reinterpret_cast<int2*>(&v);
+      q.x = __shfl_up(q.x, d);
+      q.y = __shfl_up(q.y, d);
+      o = *reinterpret_cast<T*>(&q);
+    } else {
+      o = __shfl_up(v, d);
+    }
+    if (lane >= d) v = v + o;
+  }
+  if (lane == kWave - 1) lds[wave] = v;
+  __syncthreads();
+  T base = T(0);
+  for (int w = 0; w < wave; ++w) base = base + lds[w];
+  const T out = (wave == 0) ? v : base + v;
+  T tot = lds[0];
+  for (int w = 1; w < kDrawThreads / kWave; ++w) tot = tot + lds[w];
+  __syncthreads();
+  *total = tot;
+  return out;
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_up1(T v) {
+  if constexpr (sizeof(T) == 8) {
+    int2 q = *reinterpret_cast<int2*>(&v);
+    q.x = __shfl_up(q.x, 1);
+    q.y = __shfl_up(q.y, 1);
+    return *reinterpret_cast<T*>(&q);
+  } else {
+    return __shfl_up(v, 1);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T block_sum256(T v, T* lds) {
+  for (int m = 1; m < kWave; m <<= 1) {
+    if constexpr (sizeof(T) == 8) v += shfl_xor_d(v, m);
+    else v += __shfl_xor(v, m);
+  }
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  T t = T(0);
+  for (int w = 0; w < kDrawThreads / kWave; ++w) t = t + lds[w];
+  __syncthreads();
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Weights.
+template <typename E>
+struct Weights32 {
+  const typename E::Storage* prow;
+  const typename E::Storage* qrow;  // null: bonus draw (w = p)
+  float sl, mp, lzp, mq, lzq;
+  __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, float (&w)[kPer]) const {
+    float a[kPer];
+    load8<E>(prow, i0, hi, a);
+    if (!qrow) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) w[j] = exp2_fast(__builtin_fmaf(a[j] - mp, sl, -lzp));
+      return;
+    }
+    float b[kPer];
+    load8<E>(qrow, i0, hi, b);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float pv = exp2_fast(__builtin_fmaf(a[j] - mp, sl, -lzp));
+      const float qv = exp2_fast(__builtin_fmaf(b[j] - mq, sl, -lzq));
+      w[j] = fmaxf(pv - qv, 0.0f);
+    }
+  }
+};
+
+template <typename E>
+__device__ __forceinline__ Weights32<E> weights32(const VerifyParams& p, const DrawState& st) {
+  Weights32<E> w;
+  w.prow = static_cast<const typename E::Storage*>(p.target) + st.prow * p.stride;
+  w.qrow = (st.mode == kDrawResidual)
+               ? static_cast<const typename E::Storage*>(p.draft) + st.qrow * p.stride
+               : nullptr;
+  w.sl = st.sl;
+  w.mp = st.mp;
+  w.lzp = st.lzp;
+  w.mq = st.mq;
+  w.lzq = st.lzq;
+  return w;
+}
+
+// Float64 weights: the temperature is applied by division, the normalisers
+// are float64 sums of exp((x - max) / T).
+template <typename E>
+struct Weights64 {
+  const typename E::Storage* prow;
+  const typename E::Storage* qrow;
+  double T, mp, mq, lnzp, lnzq;
+  bool unnormalised;  // w = exp((x - mp) / T): residual mass was zero
+  __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, double (&w)[kPer]) const {
+    float a[kPer];
+    load8<E>(prow, i0, hi, a);
+    if (unnormalised || !qrow) {
+      const double off = unnormalised ? 0.0 : lnzp;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) w[j] = exp(((double)a[j] - mp) / T - off);
+      return;
+    }
+    float b[kPer];
+    load8<E>(qrow, i0, hi, b);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const double pv = exp(((double)a[j] - mp) / T - lnzp);
+      const double qv = exp(((double)b[j] - mq) / T - lnzq);
+      w[j] = pv > qv ? pv - qv : 0.0;
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ T sum8(const T (&w)[kPer]) {
+  T s = w[0];
+#pragma unroll
+  for (int j = 1; j < kPer; ++j) s = s + w[j];
+  return s;
+}
+
+// Mass of tile `tile` of a row: the block-scan total of the thread sums.
+template <typename T, typename W>
+__device__ __forceinline__ T tile_mass(const W& weights, int64_t tile, int64_t V, T* lds) {
+  const int64_t lo = tile * kDrawTile;
+  const int64_t hi = min(V, lo + (int64_t)kDrawTile);
+  T w[kPer];
+  weights(lo + (int64_t)threadIdx.x * kPer, hi, w);
+  T tot;
+  scan256<T>(sum8(w), lds, &tot);
+  return tot;
+}
+
+struct PickResult {
+  int64_t y;
+  double margin;
+  int found;
+};
+
+template <typename T>
+struct PickLds {
+  T scan[kDrawThreads / kWave];
+  T last[kDrawThreads / kWave];
+  int wave_first[kDrawThreads / kWave];
+  int64_t y;
+  double margin;
+  int found;
+  int tile;
+  T c0, t;
+};
+
+// The draw given per-tile masses: scan the masses (rounds of 256 tiles, carry
+// in order) for the total R and the crossing tile, then scan inside it.  The
+// first y with C(y) > t = u * R wins; margin = min(t - C(y-1), C(y) - t).
+template <typename T, typename W>
+__device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W& weights,
+                           PickLds<T>& L) {
+  const int tid = threadIdx.x;
+  // total
+  T carry = T(0);
+  for (int64_t base = 0; base < S2; base += kDrawThreads) {
+    const T m = (base + tid < S2) ? masses[base + tid] : T(0);
+    T tot;
+    scan256<T>(m, L.scan, &tot);
+    carry = carry + tot;
+  }
+  const T R = carry;
+  const T t = u * R;
+  if (tid == 0) {
+    L.found = 0;
+    L.tile = -1;
+  }
+  __syncthreads();
+  // crossing tile: the first tile whose inclusive cumulative mass exceeds t
+  carry = T(0);
+  for (int64_t base = 0; base < S2; base += kDrawThreads) {
+    const T m = (base + tid < S2) ? masses[base + tid] : T(0);
+    T tot;
+    const T incl = carry + scan256<T>(m, L.scan, &tot);
+    T excl = shfl_up1(incl);
+    const int lane = tid & (kWave - 1);
+    // exclusive value across wave boundaries: previous thread's inclusive
+    if (lane == kWave - 1) L.last[tid / kWave] = incl;
+    __syncthreads();
+    if (lane == 0) excl = (tid == 0) ? carry : L.last[tid / kWave - 1];
+    const bool cross = (base + tid < S2) && m > T(0) && incl > t;
+    const uint64_t mask = __ballot(cross);
+    if (lane == 0) L.wave_first[tid / kWave] = mask ? (int)__builtin_ctzll(mask) : -1;
+    __syncthreads();
+    int winner = -1;
+    for (int w = 0; w < kDrawThreads / kWave; ++w)
+      if (L.wave_first[w] >= 0) {
+        winner = w * kWave + L.wave_first[w];
+        break;
+      }
+    if (winner >= 0) {
+      if (tid == winner) {
+        L.tile = (int)(base + tid);
+        L.c0 = excl;
+      }
+      __syncthreads();
+      break;
+    }
+    carry = carry + tot;
+    __syncthreads();
+  }
+  PickResult res{-1, 0.0, 0};
+  const int tile = L.tile;
+  if (tile < 0) return res;  // t at or past the total: undecided
+  const T c0 = L.c0;
+  const int64_t lo = (int64_t)tile * kDrawTile;
+  const int64_t hi = min(V, lo + (int64_t)kDrawTile);
+  T w[kPer];
+  const int64_t i0 = lo + (int64_t)tid * kPer;
+  weights(i0, hi, w);
+  T tot;
+  const T incl = scan256<T>(sum8(w), L.scan, &tot);
+  T excl = shfl_up1(incl);
+  const int lane = tid & (kWave - 1);
+  if (lane == kWave - 1) L.last[tid / kWave] = incl;
+  __syncthreads();
+  if (lane == 0) excl = (tid == 0) ? T(0) : L.last[tid / kWave - 1];
+  T run = excl;
+  int first = -1;
+  T before = T(0), at = T(0);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const T prev = c0 + run;
+    run = run + w[j];
+    const T cur = c0 + run;
+    if (first < 0 && w[j] > T(0) && cur > t) {
+      first = j;
+      before = prev;
+      at = cur;
+    }
+  }
+  const uint64_t mask = __ballot(first >= 0);
+  if (lane == 0) L.wave_first[tid / kWave] = mask ? (int)__builtin_ctzll(mask) : -1;
+  __syncthreads();
+  int winner = -1;
+  for (int wv = 0; wv < kDrawThreads / kWave; ++wv)
+    if (L.wave_first[wv] >= 0) {
+      winner = wv * kWave + L.wave_first[wv];
+      break;
+    }
+  if (winner >= 0 && tid == winner) {
+    L.found = 1;
+    L.y = i0 + first;
+    const T a = t - before, b = at - t;
+    L.margin = (double)(a < b ? a : b);
+  }
+  __syncthreads();
+  res.found = L.found;
+  res.y = L.y;
+  res.margin = L.margin;
+  return res;
+}
+
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_mass32(VerifyParams p) {
+  __shared__ float lds[kDrawThreads / kWave];
+  const int r = blockIdx.y;
+  const DrawState st = p.req[r];
+  if (st.mode == kDrawNone) return;
+  const Weights32<E> w = weights32<E>(p, st);
+  for (int64_t tile = blockIdx.x; tile < p.S2; tile += gridDim.x) {
+    const float m = tile_mass<float>(w, tile, p.V, lds);
+    if (threadIdx.x == 0) p.seg_w32[(int64_t)r * p.S2 + tile] = m;
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_pick32(VerifyParams p) {
+  __shared__ PickLds<float> L;
+  const int r = blockIdx.x;
+  const DrawState st = p.req[r];
+  if (st.mode == kDrawNone) return;
+  const Weights32<E> w = weights32<E>(p, st);
+  PickResult res{-1, 0.0, 0};
+  const bool force64 = (p.flags & SV_FLAG_FORCE_FP64_DRAW) != 0u;
+  if (!force64) res = pick<float>(p.seg_w32 + (int64_t)r * p.S2, p.S2, p.V, st.u, w, L);
+  if (threadIdx.x == 0) {
+    if (force64 || !res.found || !(res.margin >= (double)kDrawMargin32)) {
+      p.req[r].need64 = 1;
+      const int slot = atomicAdd(p.fb_count, 1);
+      p.fb_list[slot] = r;
+    } else {
+      p.out_tokens[(int64_t)r * (p.D + 1) + st.tau] = (int32_t)res.y;
+      if (p.diag) p.diag[r].draw_margin = (float)res.margin;
+    }
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ Weights64<E> weights64(const VerifyParams& p, const DrawState& st,
+                                                  bool unnormalised) {
+  Weights64<E> w;
+  w.prow = static_cast<const typename E::Storage*>(p.target) + st.prow * p.stride;
+  w.qrow = (st.mode == kDrawResidual && !unnormalised)
+               ? static_cast<const typename E::Storage*>(p.draft) + st.qrow * p.stride
+               : nullptr;
+  w.T = st.T;
+  w.mp = st.mp;
+  w.mq = st.mq;
+  w.lnzp = 0.0;
+  w.lnzq = 0.0;
+  w.unnormalised = unnormalised;
+  return w;
+}
+
+// Float64 normaliser partials of one tile: sum exp((x - max) / T).
+template <typename E>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_z64(VerifyParams p) {
+  __shared__ double lds[kDrawThreads / kWave];
+  const int64_t items = (int64_t)(*p.fb_count) * p.S2;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int r = p.fb_list[it / p.S2];
+    const int64_t tile = it % p.S2;
+    const DrawState st = p.req[r];
+    const Weights64<E> w = weights64<E>(p, st, true);
+    const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
+    const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
+    double e[kPer];
+    w(i0, hi, e);
+    const double zp = block_sum256<double>(sum8(e), lds);
+    double zq = 0.0;
+    if (st.mode == kDrawResidual) {
+      float b[kPer];
+      load8<E>(static_cast<const typename E::Storage*>(p.draft) + st.qrow * p.stride, i0, hi, b);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) e[j] = exp(((double)b[j] - (double)st.mq) / (double)st.T);
+      zq = block_sum256<double>(sum8(e), lds);
+    }
+    if (threadIdx.x == 0) {
+      p.seg_zp64[(int64_t)r * p.S2 + tile] = zp;
+      p.seg_zq64[(int64_t)r * p.S2 + tile] = zq;
+    }
+  }
+}
+
+// Full-row float64 normaliser from the tile partials (fixed-order tree).
+__device__ __forceinline__ double merge_z64(const double* parts, int64_t S2, double* lds) {
+  double z = 0.0;
+  for (int64_t j = threadIdx.x; j < S2; j += kDrawThreads) z += parts[j];
+  return block_sum256<double>(z, lds);
+}
+
+template <typename E>
+__device__ __forceinline__ Weights64<E> full_weights64(const VerifyParams& p, const DrawState& st,
+                                                       int r, bool unnormalised, double* lds) {
+  Weights64<E> w = weights64<E>(p, st, unnormalised);
+  const double zp = merge_z64(p.seg_zp64 + (int64_t)r * p.S2, p.S2, lds);
+  w.lnzp = log(zp);
+  if (st.mode == kDrawResidual) {
+    const double zq = merge_z64(p.seg_zq64 + (int64_t)r * p.S2, p.S2, lds);
+    w.lnzq = log(zq);
+  }
+  return w;
+}
+
+template <typename E>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_mass64(VerifyParams p) {
+  __shared__ double lds[kDrawThreads / kWave];
+  const int64_t items = (int64_t)(*p.fb_count) * p.S2;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int r = p.fb_list[it / p.S2];
+    const int64_t tile = it % p.S2;
+    const DrawState st = p.req[r];
+    const Weights64<E> w = full_weights64<E>(p, st, r, false, lds);
+    const double m = tile_mass<double>(w, tile, p.V, lds);
+    if (threadIdx.x == 0) p.seg_w64[(int64_t)r * p.S2 + tile] = m;
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
+  __shared__ PickLds<double> L;
+  __shared__ double lds[kDrawThreads / kWave];
+  const int r = blockIdx.x;
+  const DrawState st = p.req[r];
+  if (st.mode == kDrawNone || !st.need64) return;
+  // Residual mass (float64): the sum of the tile masses, same order as pick.
+  double R = 0.0;
+  {
+    double carry = 0.0;
+    for (int64_t base = 0; base < p.S2; base += kDrawThreads) {
+      const double m = (base + threadIdx.x < p.S2) ? p.seg_w64[(int64_t)r * p.S2 + base + threadIdx.x] : 0.0;
+      double tot;
+      scan256<double>(m, lds, &tot);
+      carry = carry + tot;
+    }
+    R = carry;
+  }
+  const bool unnorm = !(R > 0.0);
+  PickResult res;
+  if (!unnorm) {
+    const Weights64<E> w = full_weights64<E>(p, st, r, false, lds);
+    res = pick<double>(p.seg_w64 + (int64_t)r * p.S2, p.S2, p.V, (double)st.u, w, L);
+  } else {
+    // p = q to float64 precision: draw from p (unnormalised tile partials).
+    const Weights64<E> w = weights64<E>(p, st, true);
+    res = pick<double>(p.seg_zp64 + (int64_t)r * p.S2, p.S2, p.V, (double)st.u, w, L);
+  }
+  if (!res.found) {
+    // t rounded to or past the total: the last token of non-zero weight.
+    __shared__ unsigned long long s_last1;
+    if (threadIdx.x == 0) s_last1 = 0ull;
+    __syncthreads();
+    const Weights64<E> w = unnorm ? weights64<E>(p, st, true) : full_weights64<E>(p, st, r, false, lds);
+    for (int64_t tile = 0; tile < p.S2; ++tile) {
+      const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
+      const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
+      double e[kPer];
+      w(i0, hi, e);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (e[j] > 0.0) atomicMax(&s_last1, (unsigned long long)(i0 + j + 1));
+    }
+    __syncthreads();
+    res.y = (int64_t)s_last1 - 1;
+    res.margin = 0.0;
+  }
+  if (threadIdx.x == 0) {
+    p.out_tokens[(int64_t)r * (p.D + 1) + st.tau] = (int32_t)res.y;
+    if (p.diag) {
+      p.diag[r].draw_margin = (float)res.margin;
+      p.diag[r].bits |= SV_BIT_FP64_DRAW | (unnorm ? SV_BIT_RESIDUAL_ZERO : 0u);
+    }
+  }
+}
+
+template <typename E>
+static void launch_draw_t(const VerifyParams& p, hipStream_t stream) {
+  const unsigned gx = (unsigned)(p.S2 < 1024 ? p.S2 : 1024);
+  hipLaunchKernelGGL(k_draw_mass32<E>, dim3(gx, (unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL(k_draw_pick32<E>, dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL(k_draw_z64<E>, dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL(k_draw_mass64<E>, dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL(k_draw_pick64<E>, dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
+}
+
+void launch_draw(const VerifyParams& p, hipStream_t stream) {
+  if (p.dtype == SV_DTYPE_BF16) launch_draw_t<Bf16>(p, stream);
+  else launch_draw_t<F32>(p, stream);
+}
+
+}  // namespace sv

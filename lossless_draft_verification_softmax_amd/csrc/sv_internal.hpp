@@ -12,6 +12,9 @@ namespace sv {
 
 enum DrawMode : int32_t { kDrawNone = 0, kDrawResidual = 1, kDrawBonus = 2 };
 
+// Elements per draw tile (256 threads x 8).
+constexpr int kDrawTile = 2048;
+
 // What k_accept leaves for the draw kernels of one request.
 struct DrawState {
   int32_t mode;     // DrawMode
@@ -35,7 +38,7 @@ struct VerifyParams {
   int32_t B, D;            // batch, D_max
   int64_t V, stride;       // vocabulary, row stride (elements)
   int32_t S1, seg1;        // statistics pass: segments per row, segment length
-  int32_t S2, seg2;        // draw: segments per row, segment length
+  int32_t S2, seg2;        // draw: tiles per row, tile length
   uint32_t seed_lo, seed_hi, step, flags;
   const void* target;
   const void* draft;
@@ -60,12 +63,18 @@ struct VerifyParams {
   double* seg_zp64;  // [B][S2]
   double* seg_zq64;  // [B][S2]
   double* seg_w64;   // [B][S2]
+  int32_t* fb_count; // requests queued for the float64 draw
+  int32_t* fb_list;  // [B]
+  uint32_t* plan_pairs;    // [B * D]        (r << 7 | k) row pairs at T > 0
+  uint32_t* plan_singles;  // [B * (D + 1)]  (r << 7 | k) single rows
+  int32_t* plan_counts;    // [2]
 };
 
 // ---- launch geometry (host) -------------------------------------------------
 
-// Statistics pass: enough (row, segment) workgroups to fill 256 CUs several
-// times over, but segments of at least 2048 elements.
+// Single rows (bonus rows, T = 0 rows) are cut into S1 segments so that the
+// row pass has several times more items than CUs; segments hold at least
+// 2048 elements.
 inline void stats_geometry(int32_t B, int32_t D, int64_t V, int32_t* S1, int32_t* seg1) {
   const int64_t units = (int64_t)B * (D + 1);
   int64_t s = units > 0 ? (4096 + units - 1) / units : 1;
@@ -80,21 +89,17 @@ inline void stats_geometry(int32_t B, int32_t D, int64_t V, int32_t* S1, int32_t
   *seg1 = (int32_t)len;
 }
 
-// Draw: segments of about one to two 2048-element tiles, at most 64.
+// Draw: tiles of kDrawTile elements.
 inline void draw_geometry(int64_t V, int32_t* S2, int32_t* seg2) {
-  int64_t s = (V + 2047) / 2048;
-  if (s > 64) s = 64;
-  if (s < 1) s = 1;
-  int64_t len = (V + s - 1) / s;
-  len = (len + 7) / 8 * 8;
-  *S2 = (int32_t)s;
-  *seg2 = (int32_t)len;
+  *S2 = (int32_t)((V + kDrawTile - 1) / kDrawTile);
+  *seg2 = kDrawTile;
 }
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WorkspaceLayout {
-  size_t part_p, part_q, part_a, req, seg_w32, seg_zp64, seg_zq64, seg_w64, total;
+  size_t part_p, part_q, part_a, req, seg_w32, seg_zp64, seg_zq64, seg_w64, fb_count, fb_list,
+      plan_pairs, plan_singles, plan_counts, total;
 };
 
 inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
@@ -112,11 +117,19 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
   L.seg_zp64 = off; off += align256((size_t)B * S2 * sizeof(double));
   L.seg_zq64 = off; off += align256((size_t)B * S2 * sizeof(double));
   L.seg_w64 = off; off += align256((size_t)B * S2 * sizeof(double));
+  L.fb_count = off; off += align256(sizeof(int32_t));
+  L.fb_list = off; off += align256((size_t)B * sizeof(int32_t));
+  L.plan_pairs = off; off += align256((size_t)B * (size_t)D * sizeof(uint32_t));
+  L.plan_singles = off; off += align256(U * sizeof(uint32_t));
+  L.plan_counts = off; off += align256(2 * sizeof(int32_t));
   L.total = off;
   return L;
 }
 
-hipError_t launch_verify(const VerifyParams& p, hipStream_t stream);
+hipError_t launch_verify(const VerifyParams& p, int grid, hipStream_t stream);
+void launch_plan(const VerifyParams& p, hipStream_t stream);
+void launch_rowpass(const VerifyParams& p, int grid, hipStream_t stream);
+void launch_draw(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_budget(const float* conf, int32_t B, int32_t D, const int32_t* max_depth,
                          int64_t K, int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
                          float* utility, hipStream_t stream);

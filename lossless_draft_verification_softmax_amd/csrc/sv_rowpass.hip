@@ -1,0 +1,336 @@
+// sv_rowpass.hip -- the HBM-streaming statistics pass of verification.
+//
+// For every verified position the target scores the drafted token in one
+// pass over the vocabulary ("Tencent open-sources AngelSpec", section "Why one
+// universal drafter underperforms"); per row this needs the softmax
+// normaliser (max and sum of 2^((x - max) log2(e) / T)) and, for the
+// acceptance rate of equation L_e2e ("AngelSpec: specialize the drafter...",
+// section "MTP"), sum_y min(p(y), q(y)) over the target / draft row pair.
+//
+//   k_plan     one workgroup: scans depth / temperature and writes the work
+//              list: every (request, position) row pair at T > 0, then every
+//              single row (bonus rows at T > 0, all target rows at T = 0).
+//   k_rowpass  persistent, one 1024-thread workgroup per CU, items taken
+//              round-robin.  A row pair is one item: pass 1 streams both rows
+//              from HBM with 16-byte loads (online max / sum), then pass 2
+//              streams them again for sum min(p, q).  At most one row pair
+//              per CU is in flight (about 155 MB on 256 CUs), so pass 2 reads
+//              what pass 1 just pulled into the 256 MB Infinity Cache.  Single
+//              rows are cut into segments (one pass each) and fill the tail.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "specverify.h"
+#include "sv_block.hpp"
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+
+namespace sv {
+
+constexpr int kPassThreads = 1024;
+constexpr int kPassUnroll = 4;
+constexpr int kPlanThreads = 1024;
+
+// ---------------------------------------------------------------------------
+// Exclusive prefix sum of an int over the block (fixed order); *total gets
+// the block total.
+__device__ __forceinline__ int32_t block_excl_scan_i(int32_t v, int32_t* lds, int32_t* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int32_t x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t o = __shfl_up(x, d);
+    if (lane >= d) x += o;
+  }
+  if (lane == kWave - 1) lds[wave] = x;
+  __syncthreads();
+  int32_t base = 0, tot = 0;
+  for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+    if (w < wave) base += lds[w];
+    tot += lds[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
+  __shared__ int32_t lds[kPlanThreads / kWave];
+  int32_t carry_pairs = 0, carry_singles = 0;
+  for (int base = 0; base < p.B; base += kPlanThreads) {
+    const int r = base + (int)threadIdx.x;
+    int32_t np = 0, ns = 0, n = 0;
+    float T = 0.0f;
+    if (r < p.B) {
+      n = p.depth[r];
+      T = p.temperature[r];
+      const bool valid = n >= 0 && n <= p.D && temperature_ok(T) &&
+                         !(T > 0.0f && n > 0 && p.draft == nullptr);
+      if (valid) {
+        np = (T > 0.0f) ? n : 0;
+        ns = (T > 0.0f) ? 1 : n + 1;
+      }
+    }
+    int32_t tp, ts;
+    const int32_t op = carry_pairs + block_excl_scan_i(np, lds, &tp);
+    const int32_t os = carry_singles + block_excl_scan_i(ns, lds, &ts);
+    for (int k = 0; k < np; ++k) p.plan_pairs[op + k] = ((uint32_t)r << 7) | (uint32_t)k;
+    for (int j = 0; j < ns; ++j)
+      p.plan_singles[os + j] = ((uint32_t)r << 7) | (uint32_t)((T > 0.0f) ? n : j);
+    carry_pairs += tp;
+    carry_singles += ts;
+  }
+  if (threadIdx.x == 0) {
+    p.plan_counts[0] = carry_pairs;
+    p.plan_counts[1] = carry_singles;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming loops.  A thread's share of [lo, hi) is the vectors
+// lo + VEC * (tid + j * blockDim); they are taken in batches of kPassUnroll
+// vectors per row, and the loads of the next batch are issued before the
+// current batch is processed (two register buffers), so every wave keeps
+// loads in flight while it computes.
+
+template <typename E, bool kPair>
+struct Batch {
+  uint4 p[kPassUnroll];
+  uint4 q[kPair ? kPassUnroll : 1];
+};
+
+template <typename E, bool kPair>
+__device__ __forceinline__ void load_batch(Batch<E, kPair>& b, const typename E::Storage* prow,
+                                           const typename E::Storage* qrow, int64_t base,
+                                           int64_t step, int64_t vhi) {
+  const uint4 pad = make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+#pragma unroll
+  for (int u = 0; u < kPassUnroll; ++u) {
+    const int64_t i = base + u * step;
+    b.p[u] = (i < vhi) ? load16(prow + i) : pad;
+    if constexpr (kPair) b.q[u] = (i < vhi) ? load16(qrow + i) : pad;
+  }
+}
+
+template <typename E, bool kPair>
+__device__ __forceinline__ void softmax_batch(const Batch<E, kPair>& b, float sl, SoftmaxPart& sp,
+                                              SoftmaxPart& sq) {
+  constexpr int VEC = E::kPerVec;
+  constexpr int G = VEC * kPassUnroll;
+  float x[G];
+#pragma unroll
+  for (int u = 0; u < kPassUnroll; ++u)
+    E::unpack(b.p[u], *reinterpret_cast<float(*)[VEC]>(&x[u * VEC]));
+  softmax_group<G>(sp, x, sl);
+  if constexpr (kPair) {
+#pragma unroll
+    for (int u = 0; u < kPassUnroll; ++u)
+      E::unpack(b.q[u], *reinterpret_cast<float(*)[VEC]>(&x[u * VEC]));
+    softmax_group<G>(sq, x, sl);
+  }
+}
+
+// Pass 1 over [lo, hi) of one row (and its partner row when kPair).
+template <typename E, bool kPair>
+__device__ __forceinline__ void stream_softmax(const typename E::Storage* prow,
+                                               const typename E::Storage* qrow, int64_t lo,
+                                               int64_t hi, float sl, SoftmaxPart& sp,
+                                               SoftmaxPart& sq) {
+  constexpr int VEC = E::kPerVec;
+  const int64_t vhi = lo + ((hi - lo) / VEC) * VEC;
+  const int64_t step = (int64_t)blockDim.x * VEC;
+  const int64_t batch = step * kPassUnroll;
+  int64_t base = lo + (int64_t)threadIdx.x * VEC;
+  Batch<E, kPair> b0, b1;
+  if (base < vhi) load_batch<E, kPair>(b0, prow, qrow, base, step, vhi);
+  for (; base < vhi; base += 2 * batch) {
+    if (base + batch < vhi) load_batch<E, kPair>(b1, prow, qrow, base + batch, step, vhi);
+    softmax_batch<E, kPair>(b0, sl, sp, sq);
+    if (base + batch >= vhi) break;
+    if (base + 2 * batch < vhi) load_batch<E, kPair>(b0, prow, qrow, base + 2 * batch, step, vhi);
+    softmax_batch<E, kPair>(b1, sl, sp, sq);
+  }
+  for (int64_t i = vhi + threadIdx.x; i < hi; i += blockDim.x) {
+    float x1[1] = {E::load1(prow, i)};
+    softmax_group<1>(sp, x1, sl);
+    if constexpr (kPair) {
+      x1[0] = E::load1(qrow, i);
+      softmax_group<1>(sq, x1, sl);
+    }
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ float overlap_batch(const Batch<E, true>& b, float sl, float cp,
+                                               float cq) {
+  constexpr int VEC = E::kPerVec;
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kPassUnroll; ++u) {
+    float a[VEC], c[VEC], e[VEC];
+    E::unpack(b.p[u], a);
+    E::unpack(b.q[u], c);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      e[j] = exp2_fast(fminf(__builtin_fmaf(a[j], sl, -cp), __builtin_fmaf(c[j], sl, -cq)));
+#pragma unroll
+    for (int w = 1; w < VEC; w <<= 1) {
+#pragma unroll
+      for (int j = 0; j + w < VEC; j += 2 * w) e[j] += e[j + w];
+    }
+    acc += e[0];
+  }
+  return acc;
+}
+
+// Pass 2: this thread's share of sum_y 2^min(x_p(y) sl - cp, x_q(y) sl - cq)
+// (padding vectors are -inf and add 0).
+template <typename E>
+__device__ __forceinline__ float stream_overlap(const typename E::Storage* prow,
+                                                const typename E::Storage* qrow, int64_t V,
+                                                float sl, float cp, float cq) {
+  constexpr int VEC = E::kPerVec;
+  const int64_t vhi = (V / VEC) * VEC;
+  const int64_t step = (int64_t)blockDim.x * VEC;
+  const int64_t batch = step * kPassUnroll;
+  int64_t base = (int64_t)threadIdx.x * VEC;
+  float acc = 0.0f;
+  Batch<E, true> b0, b1;
+  if (base < vhi) load_batch<E, true>(b0, prow, qrow, base, step, vhi);
+  for (; base < vhi; base += 2 * batch) {
+    if (base + batch < vhi) load_batch<E, true>(b1, prow, qrow, base + batch, step, vhi);
+    acc += overlap_batch<E>(b0, sl, cp, cq);
+    if (base + batch >= vhi) break;
+    if (base + 2 * batch < vhi) load_batch<E, true>(b0, prow, qrow, base + 2 * batch, step, vhi);
+    acc += overlap_batch<E>(b1, sl, cp, cq);
+  }
+  for (int64_t i = vhi + threadIdx.x; i < V; i += blockDim.x) {
+    const float a = E::load1(prow, i), c = E::load1(qrow, i);
+    acc += exp2_fast(fminf(__builtin_fmaf(a, sl, -cp), __builtin_fmaf(c, sl, -cq)));
+  }
+  return acc;
+}
+
+template <typename E>
+__device__ void pair_item(const VerifyParams& p, uint32_t item, SoftmaxPart* lds_sm,
+                          float* lds_f) {
+  const int r = (int)(item >> 7), k = (int)(item & 127u);
+  const float sl = kLog2e / p.temperature[r];
+  const auto* prow = row_ptr<E>(p.target, p.target_row0[r] + k, p.stride);
+  const auto* qrow = row_ptr<E>(p.draft, p.draft_row0[r] + k, p.stride);
+  SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
+  stream_softmax<E, true>(prow, qrow, 0, p.V, sl, sp, sq);
+  sp = block_merge(sp, sl, lds_sm);
+  sq = block_merge(sq, sl, lds_sm);
+  const int64_t slot = ((int64_t)r * (p.D + 1) + k) * p.S1;
+  if (threadIdx.x == 0) {
+    p.part_p[slot] = make_float2(sp.m, sp.z);
+    p.part_q[slot] = make_float2(sq.m, sq.z);
+  }
+  if (!p.alpha) return;
+  float a = 0.0f;
+  const bool finite = sp.m == sp.m && sq.m == sq.m && fabsf(sp.m) < INFINITY &&
+                      fabsf(sq.m) < INFINITY;
+  if (finite) {  // block-uniform
+    const float cp = __builtin_fmaf(sp.m, sl, __log2f(sp.z));
+    const float cq = __builtin_fmaf(sq.m, sl, __log2f(sq.z));
+    a = block_sum_f(stream_overlap<E>(prow, qrow, p.V, sl, cp, cq), lds_f);
+  }
+  if (threadIdx.x == 0) p.part_a[slot] = a;
+}
+
+template <typename E>
+__device__ void single_item(const VerifyParams& p, uint32_t item, int seg, SoftmaxPart* lds_sm,
+                            ArgMax* lds_am) {
+  using S = typename E::Storage;
+  constexpr int VEC = E::kPerVec;
+  const int r = (int)(item >> 7), k = (int)(item & 127u);
+  const float T = p.temperature[r];
+  const S* prow = row_ptr<E>(p.target, p.target_row0[r] + k, p.stride);
+  const int64_t lo = (int64_t)seg * p.seg1;
+  const int64_t hi = min(p.V, lo + (int64_t)p.seg1);
+  const int64_t slot = ((int64_t)r * (p.D + 1) + k) * p.S1 + seg;
+  if (T > 0.0f) {
+    const float sl = kLog2e / T;
+    SoftmaxPart sp{-INFINITY, 0.0f}, unused{-INFINITY, 0.0f};
+    if (hi > lo) stream_softmax<E, false>(prow, nullptr, lo, hi, sl, sp, unused);
+    sp = block_merge(sp, sl, lds_sm);
+    if (threadIdx.x == 0) p.part_p[slot] = make_float2(sp.m, sp.z);
+    return;
+  }
+  // T = 0: arg max over the segment.  Per thread the best vector (strictly
+  // greater keeps the earliest; NaN propagates through the maximum), then the
+  // first maximal element inside it.
+  const int64_t vhi = (hi > lo) ? lo + ((hi - lo) / VEC) * VEC : lo;
+  const int64_t step = (int64_t)blockDim.x * VEC;
+  float best = -INFINITY;
+  int64_t bvec = -1;
+  const int64_t batch = step * kPassUnroll;
+  auto argmax_batch = [&](const Batch<E, false>& bt, int64_t b0) {
+#pragma unroll
+    for (int u = 0; u < kPassUnroll; ++u) {
+      float x[VEC];
+      E::unpack(bt.p[u], x);
+      float cm = x[0];
+#pragma unroll
+      for (int j = 1; j < VEC; ++j) cm = vmax(cm, x[j]);
+      const bool up = cm > best;
+      best = vmax(best, cm);
+      bvec = up ? b0 + u * step : bvec;
+    }
+  };
+  int64_t base = lo + (int64_t)threadIdx.x * VEC;
+  Batch<E, false> b0, b1;
+  if (base < vhi) load_batch<E, false>(b0, prow, nullptr, base, step, vhi);
+  for (; base < vhi; base += 2 * batch) {
+    if (base + batch < vhi) load_batch<E, false>(b1, prow, nullptr, base + batch, step, vhi);
+    argmax_batch(b0, base);
+    if (base + batch >= vhi) break;
+    if (base + 2 * batch < vhi) load_batch<E, false>(b0, prow, nullptr, base + 2 * batch, step, vhi);
+    argmax_batch(b1, base + batch);
+  }
+  ArgMax a{best, INT32_MAX};
+  if (best == best && bvec >= 0) {
+    float x[VEC];
+    E::unpack(load16(prow + bvec), x);
+#pragma unroll
+    for (int j = VEC - 1; j >= 0; --j)
+      if (x[j] == best) a.i = (int32_t)(bvec + j);
+  }
+  for (int64_t i = vhi + threadIdx.x; i < hi; i += blockDim.x)
+    a = argmax_merge(a, ArgMax{E::load1(prow, i), (int32_t)i});
+  a = block_argmax(a, lds_am);
+  if (threadIdx.x == 0) p.part_p[slot] = make_float2(a.v, __int_as_float(a.i));
+}
+
+template <typename E>
+__global__ __launch_bounds__(kPassThreads) void k_rowpass(VerifyParams p) {
+  __shared__ SoftmaxPart lds_sm[kPassThreads / kWave];
+  __shared__ ArgMax lds_am[kPassThreads / kWave];
+  __shared__ float lds_f[kPassThreads / kWave];
+  const int64_t n_pairs = p.plan_counts[0];
+  const int64_t n_singles = p.plan_counts[1];
+  const int64_t total = n_pairs + n_singles * p.S1;
+  for (int64_t it = blockIdx.x; it < total; it += gridDim.x) {
+    if (it < n_pairs) {
+      pair_item<E>(p, p.plan_pairs[it], lds_sm, lds_f);
+    } else {
+      const int64_t j = it - n_pairs;
+      single_item<E>(p, p.plan_singles[j / p.S1], (int)(j % p.S1), lds_sm, lds_am);
+    }
+  }
+}
+
+void launch_plan(const VerifyParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, p);
+}
+
+void launch_rowpass(const VerifyParams& p, int grid, hipStream_t stream) {
+  if (p.dtype == SV_DTYPE_BF16)
+    hipLaunchKernelGGL(k_rowpass<Bf16>, dim3((unsigned)grid), dim3(kPassThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(k_rowpass<F32>, dim3((unsigned)grid), dim3(kPassThreads), 0, stream, p);
+}
+
+}  // namespace sv
