@@ -61,6 +61,8 @@ typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
 
 /* sv_verify_args.flags */
 #define SV_FLAG_FORCE_FP64_DRAW 1u /* take every T > 0 draw on the float64 path */
+#define SV_FLAG_STREAMING_ROW_PASS 2u /* use the streaming row pass (two reads of each row
+                                         pair) instead of the register-resident team pass */
 
 /* sv_diag.bits */
 #define SV_BIT_BAD_DEPTH 1u        /* depth[r] outside [0, D_max]                      */
@@ -69,6 +71,7 @@ typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
 #define SV_BIT_RESIDUAL_ZERO 8u    /* residual mass was zero: the draw used p          */
 #define SV_BIT_BAD_TEMPERATURE 16u /* temperature[r] negative, NaN or infinite         */
 #define SV_BIT_FP64_DRAW 32u       /* the draw was recomputed in float64               */
+#define SV_BIT_SYNC_TIMEOUT 64u    /* the row pass's team wait expired: results invalid */
 
 /* Per-request diagnostics (written when sv_verify_args.diag != NULL). */
 typedef struct sv_diag {
@@ -186,7 +189,7 @@ typedef struct sv_verify_args {
    * that are recorded on `stream` at the stage boundaries: [0] before the
    * work-list planner, [1] after it, [2] after the row pass (row statistics
    * and acceptance rates), [3] after the accept scan, [4] after the draw.
-   * For timing only. */
+   * An entry may be NULL (not recorded).  For timing only. */
   void* const* stage_events;
 } sv_verify_args;
 

@@ -37,7 +37,7 @@ sv_status validate_verify(const sv_verify_args* a, size_t* need) {
   if (a->B < 0 || a->D_max < 0 || a->D_max > SV_MAX_DEPTH) return SV_ERR_INVALID_ARGUMENT;
   if (a->V < 1 || a->V > INT32_MAX || a->row_stride < a->V) return SV_ERR_INVALID_ARGUMENT;
   if (a->dtype != SV_DTYPE_BF16 && a->dtype != SV_DTYPE_FP32) return SV_ERR_UNSUPPORTED;
-  if (a->flags & ~SV_FLAG_FORCE_FP64_DRAW) return SV_ERR_UNSUPPORTED;
+  if (a->flags & ~(SV_FLAG_FORCE_FP64_DRAW | SV_FLAG_STREAMING_ROW_PASS)) return SV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * (a->D_max + 1) > (int64_t)INT32_MAX / 64) return SV_ERR_INVALID_ARGUMENT;
   if (a->B == 0) {
     *need = 0;
@@ -131,9 +131,11 @@ sv_status sv_verify_batch(const sv_verify_args* a, void* stream) {
   p.seg_w64 = reinterpret_cast<double*>(ws + L.seg_w64);
   p.fb_count = reinterpret_cast<int32_t*>(ws + L.fb_count);
   p.fb_list = reinterpret_cast<int32_t*>(ws + L.fb_list);
-  p.plan_pairs = reinterpret_cast<uint32_t*>(ws + L.plan_pairs);
-  p.plan_singles = reinterpret_cast<uint32_t*>(ws + L.plan_singles);
+  p.plan_pairs = reinterpret_cast<sv::PlanItem*>(ws + L.plan_pairs);
+  p.plan_singles = reinterpret_cast<sv::PlanItem*>(ws + L.plan_singles);
   p.plan_counts = reinterpret_cast<int32_t*>(ws + L.plan_counts);
+  p.team_xch = reinterpret_cast<uint64_t*>(ws + L.team_xch);
+  p.sync_error = reinterpret_cast<int32_t*>(ws + L.sync_error);
   const int grid = device_cu_count();
   if (grid <= 0) return SV_ERR_DEVICE;
   const hipError_t e = sv::launch_verify(p, grid, static_cast<hipStream_t>(stream));

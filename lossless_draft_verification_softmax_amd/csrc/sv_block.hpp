@@ -11,14 +11,25 @@
 
 namespace sv {
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, which makes every wave wait for all of its outstanding vector loads
+// (the vmcnt counter is in order) and would drain the prefetched rows of the
+// streaming loops at every reduction.  All intra-workgroup communication here
+// goes through LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float block_sum_f(float v, float* lds) {
   v = wave_sum(v);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (lane == 0) lds[wave] = v;
-  __syncthreads();
+  lds_barrier();
   float t = 0.0f;
   for (int w = 0; w < (int)(blockDim.x / kWave); ++w) t += lds[w];
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
@@ -26,10 +37,10 @@ __device__ __forceinline__ double block_sum_d(double v, double* lds) {
   for (int m = 1; m < kWave; m <<= 1) v += shfl_xor_d(v, m);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (lane == 0) lds[wave] = v;
-  __syncthreads();
+  lds_barrier();
   double t = 0.0;
   for (int w = 0; w < (int)(blockDim.x / kWave); ++w) t += lds[w];
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
@@ -37,10 +48,10 @@ __device__ __forceinline__ SoftmaxPart block_merge(SoftmaxPart p, float sl, Soft
   p = wave_merge(p, sl);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (lane == 0) lds[wave] = p;
-  __syncthreads();
+  lds_barrier();
   SoftmaxPart t = lds[0];
   for (int w = 1; w < (int)(blockDim.x / kWave); ++w) t = merge_parts(t, lds[w], sl);
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
@@ -63,10 +74,10 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax a, ArgMax* lds) {
   }
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (lane == 0) lds[wave] = a;
-  __syncthreads();
+  lds_barrier();
   ArgMax t = lds[0];
   for (int w = 1; w < (int)(blockDim.x / kWave); ++w) t = argmax_merge(t, lds[w]);
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
@@ -93,17 +104,25 @@ __device__ __forceinline__ void softmax_group(SoftmaxPart& s, const float (&x)[N
   const float mn = vmax(s.m, cm);
   const float ms = (mn == -INFINITY) ? 0.0f : mn;
   const float msl = ms * sl;
-  float e[N];
+  // exponentials in chunks of at most 8 (pairwise inside a chunk, chunks in
+  // order), so that only 8 of them are live at a time
+  constexpr int C = N < 8 ? N : 8;
+  static_assert(N % C == 0, "group size must be a multiple of the chunk");
+  float acc = 0.0f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) e[i] = exp2_fast(__builtin_fmaf(x[i], sl, -msl));
-  // pairwise sum of the group
+  for (int c = 0; c < N; c += C) {
+    float e[C];
 #pragma unroll
-  for (int w = 1; w < N; w <<= 1) {
+    for (int i = 0; i < C; ++i) e[i] = exp2_fast(__builtin_fmaf(x[c + i], sl, -msl));
 #pragma unroll
-    for (int i = 0; i + w < N; i += 2 * w) e[i] += e[i + w];
+    for (int w = 1; w < C; w <<= 1) {
+#pragma unroll
+      for (int i = 0; i + w < C; i += 2 * w) e[i] += e[i + w];
+    }
+    acc = (c == 0) ? e[0] : acc + e[0];
   }
   const float scale = exp2_fast(__builtin_fmaf(s.m, sl, -msl));
-  s.z = __builtin_fmaf(s.z, scale, e[0]);
+  s.z = __builtin_fmaf(s.z, scale, acc);
   s.m = mn;
 }
 

@@ -6,9 +6,9 @@
 //
 // One workgroup of 1024 threads: float32 prefix products, 64-bit keys
 // (score bits above the complemented flat index, so equal scores order by
-// lower request, then lower position), a bitonic sort in LDS, then per-request
-// counts and the packed row offsets.  The whole batch (B * D_max <= 4096
-// keys, 32 KB) stays in LDS; B <= 4096.
+// lower request, then lower position), a radix select of the K-th largest
+// key, per-request counts and the packed row offsets.  The whole batch
+// (B * D_max <= 4096 keys, 32 KB) stays in LDS; B <= 4096.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,6 +19,8 @@
 namespace sv {
 
 constexpr int kBudgetThreads = 1024;
+constexpr int kBudgetWaves = kBudgetThreads / kWave;
+constexpr int kKeySlots = SV_MAX_BUDGET_POSITIONS / kBudgetThreads;  // keys per thread
 
 __device__ __forceinline__ float block_sum_budget(float v, float* lds) {
   v = wave_sum(v);
@@ -26,40 +28,58 @@ __device__ __forceinline__ float block_sum_budget(float v, float* lds) {
   if (lane == 0) lds[wave] = v;
   __syncthreads();
   float t = 0.0f;
-  for (int w = 0; w < kBudgetThreads / kWave; ++w) t += lds[w];
+  for (int w = 0; w < kBudgetWaves; ++w) t += lds[w];
   __syncthreads();
   return t;
 }
 
+// Inclusive prefix sum over the lanes of a wavefront.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Keys: (score bits << 32) | ~flat_index, unique and nonzero for every
+// position within its request's limit, 0 elsewhere.  Within a request the
+// scores do not increase with the position (confidences are clamped to
+// [0, 1]) and ~index decreases, so a request's keys strictly decrease and the
+// global top K keeps a prefix of every request.  The kernel therefore needs
+// only the K-th largest key t (a radix select, eight 8-bit digits from the
+// top) and counts per request the keys >= t; no sort.
 __global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, int32_t B, int32_t D,
                                                            const int32_t* max_depth, int64_t K,
-                                                           int32_t N2, int32_t* depth,
-                                                           int64_t* draft_row0, int64_t* target_row0,
-                                                           float* utility) {
+                                                           int32_t* depth, int64_t* draft_row0,
+                                                           int64_t* target_row0, float* utility) {
   __shared__ uint64_t keys[SV_MAX_BUDGET_POSITIONS];
   __shared__ int32_t counts[SV_MAX_BUDGET_POSITIONS];
-  __shared__ float red[kBudgetThreads / kWave];
-  __shared__ int32_t s_valid;
+  __shared__ int32_t hist[256];
+  __shared__ float red[kBudgetWaves];
+  __shared__ int32_t wtot[kBudgetWaves];
+  __shared__ int32_t s_valid, s_need;
+  __shared__ uint64_t s_prefix;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int N = B * D;
-  for (int i = tid; i < N2; i += kBudgetThreads) keys[i] = 0ull;
   for (int r = tid; r < B; r += kBudgetThreads) counts[r] = 0;
   if (tid == 0) s_valid = 0;
-  __syncthreads();
   // One coalesced pass stages the confidences in the key slots (as float
-  // bits); the product loop below then reads LDS instead of waiting on one
-  // global load per position.  Each slot is read and then overwritten by
-  // the same thread.
+  // bits); the product loop then reads LDS.
   for (int i = tid; i < N; i += kBudgetThreads) keys[i] = (uint64_t)__float_as_uint(conf[i]);
   __syncthreads();
 
-  // Prefix-confidence products, left to right in float32.
+  // Prefix-confidence products, left to right in float32, one request per
+  // thread; each slot is read and then overwritten by the same thread.
   int valid = 0;
   float total = 0.0f;
   for (int r = tid; r < B; r += kBudgetThreads) {
     int lim = max_depth ? max_depth[r] : D;
     lim = lim < 0 ? 0 : (lim > D ? D : lim);
-    float s = 1.0f;
+    float sc = 1.0f;
     for (int k = 0; k < D; ++k) {
       const int idx = r * D + k;
       if (k >= lim) {  // past this request's limit: key 0, never kept
@@ -69,125 +89,124 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, in
       float c = __uint_as_float((uint32_t)keys[idx]);
       if (!(c >= 0.0f)) c = 0.0f;  // NaN and negatives read as 0
       if (c > 1.0f) c = 1.0f;
-      s = s * c;
-      total += s;
-      keys[idx] = ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(~(uint32_t)idx);
+      sc = sc * c;
+      total += sc;
+      keys[idx] = ((uint64_t)__float_as_uint(sc) << 32) | (uint64_t)(~(uint32_t)idx);
     }
     valid += lim;
   }
   atomicAdd(&s_valid, valid);
   __syncthreads();
 
-  // Bitonic sort, descending, over N2 (a power of two, >= 64) keys.  Key i
-  // lives in register slot i / 1024 of thread i % 1024.  Partners at stride
-  // >= 1024 are in the same thread, strides 64..512 go through LDS, strides
-  // below 64 stay inside the wavefront (shuffles, no barrier).  Padding and
-  // cut-off positions hold key 0, below every real key (a real key's low
-  // word ~idx is never 0).
-  constexpr int kSlots = SV_MAX_BUDGET_POSITIONS / kBudgetThreads;
-  const int nslots = (N2 + kBudgetThreads - 1) / kBudgetThreads;
-  uint64_t key[kSlots];
+  uint64_t key[kKeySlots];
 #pragma unroll
-  for (int sl = 0; sl < kSlots; ++sl) {
-    const int i = sl * kBudgetThreads + tid;
-    key[sl] = (sl < nslots && i < N2) ? keys[i] : 0ull;
+  for (int j = 0; j < kKeySlots; ++j) {
+    const int i = j * kBudgetThreads + tid;
+    key[j] = i < N ? keys[i] : 0ull;
   }
-  for (int size = 2; size <= N2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= kBudgetThreads) {
-        const int sx = stride / kBudgetThreads;
-#pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) {
-          if (sl >= nslots || (sl & sx)) continue;
-          const int i = sl * kBudgetThreads + tid;
-          const bool desc = (i & size) == 0;
-#pragma unroll
-          for (int sh = 0; sh < kSlots; ++sh) {
-            if (sh != (sl ^ sx)) continue;
-            const uint64_t a = key[sl], b = key[sh];
-            const bool swap = desc ? (a < b) : (a > b);
-            key[sl] = swap ? b : a;
-            key[sh] = swap ? a : b;
-          }
-        }
-      } else if (stride >= kWave) {
-#pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl)
-          if (sl < nslots) keys[sl * kBudgetThreads + tid] = key[sl];
-        __syncthreads();
-#pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) {
-          if (sl >= nslots) continue;
-          const int i = sl * kBudgetThreads + tid;
-          if (i >= N2) continue;
-          const int pi = i ^ stride;
-          const uint64_t other = keys[pi];
-          const bool desc = (i & size) == 0;
-          const bool lower = i < pi;
-          const uint64_t hi = key[sl] > other ? key[sl] : other;
-          const uint64_t lo = key[sl] > other ? other : key[sl];
-          key[sl] = (lower == desc) ? hi : lo;
-        }
-        __syncthreads();
-      } else {
-#pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) {
-          if (sl >= nslots) continue;
-          const int i = sl * kBudgetThreads + tid;
-          const uint32_t lo32 = __shfl_xor((uint32_t)(key[sl] & 0xffffffffull), stride);
-          const uint32_t hi32 = __shfl_xor((uint32_t)(key[sl] >> 32), stride);
-          const uint64_t other = ((uint64_t)hi32 << 32) | lo32;
-          const bool desc = (i & size) == 0;
-          const bool lower = (i & stride) == 0;
-          const uint64_t hi = key[sl] > other ? key[sl] : other;
-          const uint64_t lo = key[sl] > other ? other : key[sl];
-          key[sl] = (lower == desc) ? hi : lo;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int sl = 0; sl < kSlots; ++sl)
-    if (sl < nslots && sl * kBudgetThreads + tid < N2) keys[sl * kBudgetThreads + tid] = key[sl];
-  __syncthreads();
-
   int64_t kk = K < 0 ? 0 : K;
   if (kk > s_valid) kk = s_valid;
-  const int Keff = (int)kk;
+  const int32_t Keff = (int32_t)kk;
+
+  // Radix select of the Keff-th largest key.  After digit round d, s_prefix
+  // holds its top 8 (d + 1) bits and s_need its rank among the keys that
+  // share them.
+  if (tid == 0) {
+    s_prefix = 0ull;
+    s_need = Keff;
+  }
+  uint64_t thr = ~0ull;  // nothing kept when Keff == 0
+  if (Keff > 0) {
+    for (int d = 0; d < 8; ++d) {
+      const int shift = 56 - 8 * d;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      const uint64_t prefix = s_prefix;
+      const int32_t need = s_need;
+#pragma unroll
+      for (int j = 0; j < kKeySlots; ++j) {
+        // keys sharing the selected top bits (all keys in round 0)
+        const bool match = d == 0 || (key[j] >> (shift + 8)) == (prefix >> (shift + 8));
+        if (match && j * kBudgetThreads + tid < N)
+          atomicAdd(&hist[(int)((key[j] >> shift) & 255u)], 1);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l holds digits 255 - 4 l .. 252 - 4 l (descending)
+        int32_t h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = hist[255 - 4 * lane - j];
+        const int32_t sum = h[0] + h[1] + h[2] + h[3];
+        const int32_t incl = wave_incl_scan(sum);
+        int32_t run = incl - sum;
+        if (run < need && need <= incl) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (run < need && need <= run + h[j]) {
+              s_prefix = prefix | ((uint64_t)(255 - 4 * lane - j) << shift);
+              s_need = need - run;
+            }
+            run += h[j];
+          }
+        }
+      }
+      __syncthreads();
+    }
+    thr = s_prefix;
+  }
+
+  // Kept positions per request and the kept utility.
   float kept = 0.0f;
-  for (int i = tid; i < Keff; i += kBudgetThreads) {
-    const uint32_t idx = ~(uint32_t)(keys[i] & 0xffffffffull);
-    atomicAdd(&counts[idx / D], 1);
-    kept += __uint_as_float((uint32_t)(keys[i] >> 32));
+#pragma unroll
+  for (int j = 0; j < kKeySlots; ++j) {
+    const int i = j * kBudgetThreads + tid;
+    if (i < N && key[j] != 0ull && key[j] >= thr) {
+      atomicAdd(&counts[i / D], 1);
+      kept += __uint_as_float((uint32_t)(key[j] >> 32));
+    }
   }
   __syncthreads();
   kept = block_sum_budget(kept, red);
   total = block_sum_budget(total, red);
 
-  if (tid == 0) {
-    int64_t dr = 0, tr = 0;
-    for (int r = 0; r < B; ++r) {
-      const int32_t c = counts[r];
-      depth[r] = c;
+  // Packed row offsets: exclusive scans of c_r (draft rows) and c_r + 1
+  // (target rows) over the requests; thread t takes kKeySlots consecutive
+  // requests.
+  int32_t c[kKeySlots];
+  int32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kKeySlots; ++j) {
+    const int r = tid * kKeySlots + j;
+    c[j] = r < B ? counts[r] : 0;
+    mine += c[j];
+  }
+  const int32_t wincl = wave_incl_scan(mine);
+  if (lane == kWave - 1) wtot[wave] = wincl;
+  __syncthreads();
+  int32_t before = wincl - mine;
+  for (int w = 0; w < wave; ++w) before += wtot[w];
+  int64_t dr = before;
+#pragma unroll
+  for (int j = 0; j < kKeySlots; ++j) {
+    const int r = tid * kKeySlots + j;
+    if (r < B) {
+      depth[r] = c[j];
       if (draft_row0) draft_row0[r] = dr;
-      if (target_row0) target_row0[r] = tr;
-      dr += c;
-      tr += c + 1;
+      if (target_row0) target_row0[r] = dr + r;
     }
-    if (utility) {
-      utility[0] = kept;
-      utility[1] = total;
-    }
+    dr += c[j];
+  }
+  if (utility && tid == 0) {
+    utility[0] = kept;
+    utility[1] = total;
   }
 }
 
 hipError_t launch_budget(const float* conf, int32_t B, int32_t D, const int32_t* max_depth,
                          int64_t K, int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
                          float* utility, hipStream_t stream) {
-  int32_t N = B * D, N2 = kWave;  // at least one full wavefront of keys
-  while (N2 < N) N2 <<= 1;
   hipLaunchKernelGGL(k_budget, dim3(1), dim3(kBudgetThreads), 0, stream, conf, B, D, max_depth, K,
-                     N2, depth, draft_row0, target_row0, utility);
+                     depth, draft_row0, target_row0, utility);
   return hipGetLastError();
 }
 

@@ -14,6 +14,12 @@ enum DrawMode : int32_t { kDrawNone = 0, kDrawResidual = 1, kDrawBonus = 2 };
 
 // Elements per draw tile (256 threads x 8).
 constexpr int kDrawTile = 2048;
+// Largest grid of the team row pass, and most members per row.
+constexpr int kMaxTeamGrid = 1024;
+constexpr int kMaxTeam = 64;
+// Team exchange: per workgroup of the team grid, four ring slots of one
+// four-word record.
+constexpr int kTeamXchWords = kMaxTeamGrid * 4 * 4;
 
 // What k_accept leaves for the draw kernels of one request.
 struct DrawState {
@@ -33,11 +39,25 @@ struct DrawState {
   int32_t pad;
 };
 
+// One row-pass work item, written by the planner so that a workgroup can
+// issue a unit's loads from a single 32-byte read.
+struct PlanItem {
+  int64_t trow;   // target row index
+  int64_t drow;   // draft row index (row pairs)
+  uint32_t code;  // request << 7 | position
+  float T;        // temperature
+  uint32_t pad0, pad1;
+};
+
 struct VerifyParams {
   sv_dtype dtype;
   int32_t B, D;            // batch, D_max
   int64_t V, stride;       // vocabulary, row stride (elements)
-  int32_t S1, seg1;        // statistics pass: segments per row, segment length
+  int32_t S1, seg1;        // row pass: partial-state slots per row, segment length
+  int32_t pair_slots;      // partial-state slots of a T > 0 row pair (1 or S1)
+  int32_t alpha_slots;     // partial sums of min(p, q) per row pair (1 or S1)
+  int32_t team, nteams;    // team row pass: members per row, teams
+  int64_t team_len;        // team row pass: slice length (elements)
   int32_t S2, seg2;        // draw: tiles per row, tile length
   uint32_t seed_lo, seed_hi, step, flags;
   const void* target;
@@ -65,9 +85,11 @@ struct VerifyParams {
   double* seg_w64;   // [B][S2]
   int32_t* fb_count; // requests queued for the float64 draw
   int32_t* fb_list;  // [B]
-  uint32_t* plan_pairs;    // [B * D]        (r << 7 | k) row pairs at T > 0
-  uint32_t* plan_singles;  // [B * (D + 1)]  (r << 7 | k) single rows
+  PlanItem* plan_pairs;    // [B * D]        row pairs at T > 0
+  PlanItem* plan_singles;  // [B * (D + 1)]  single rows
   int32_t* plan_counts;    // [2]
+  uint64_t* team_xch;      // [kMaxTeamGrid * 4][4] tagged slice states exchanged in a team
+  int32_t* sync_error;     // set if a team wait expired
 };
 
 // ---- launch geometry (host) -------------------------------------------------
@@ -99,7 +121,8 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WorkspaceLayout {
   size_t part_p, part_q, part_a, req, seg_w32, seg_zp64, seg_zq64, seg_w64, fb_count, fb_list,
-      plan_pairs, plan_singles, plan_counts, total;
+      plan_pairs, plan_singles, plan_counts, team_xch, sync_error, total;
+  int32_t slots;
 };
 
 inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
@@ -107,11 +130,13 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
   stats_geometry(B, D, V, &S1, &seg1);
   draw_geometry(V, &S2, &seg2);
   const size_t U = (size_t)B * (size_t)(D + 1);
+  const size_t slots = (size_t)(S1 > kMaxTeam ? S1 : kMaxTeam);
   WorkspaceLayout L;
+  L.slots = (int32_t)slots;
   size_t off = 0;
-  L.part_p = off; off += align256(U * S1 * sizeof(float2));
-  L.part_q = off; off += align256(U * S1 * sizeof(float2));
-  L.part_a = off; off += align256(U * S1 * sizeof(float));
+  L.part_p = off; off += align256(U * slots * sizeof(float2));
+  L.part_q = off; off += align256(U * slots * sizeof(float2));
+  L.part_a = off; off += align256(U * slots * sizeof(float));
   L.req = off; off += align256((size_t)B * sizeof(DrawState));
   L.seg_w32 = off; off += align256((size_t)B * S2 * sizeof(float));
   L.seg_zp64 = off; off += align256((size_t)B * S2 * sizeof(double));
@@ -119,14 +144,19 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
   L.seg_w64 = off; off += align256((size_t)B * S2 * sizeof(double));
   L.fb_count = off; off += align256(sizeof(int32_t));
   L.fb_list = off; off += align256((size_t)B * sizeof(int32_t));
-  L.plan_pairs = off; off += align256((size_t)B * (size_t)D * sizeof(uint32_t));
-  L.plan_singles = off; off += align256(U * sizeof(uint32_t));
+  L.plan_pairs = off; off += align256((size_t)B * (size_t)D * sizeof(PlanItem));
+  L.plan_singles = off; off += align256(U * sizeof(PlanItem));
   L.plan_counts = off; off += align256(2 * sizeof(int32_t));
+  L.team_xch = off; off += align256((size_t)kTeamXchWords * sizeof(uint64_t));
+  L.sync_error = off; off += align256(sizeof(int32_t));
   L.total = off;
   return L;
 }
 
-hipError_t launch_verify(const VerifyParams& p, int grid, hipStream_t stream);
+hipError_t launch_verify(VerifyParams& p, int grid, hipStream_t stream);
+bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
+                   int32_t* slice_len);
+hipError_t launch_rowteam(VerifyParams& p, int grid, int nv, hipStream_t stream);
 void launch_plan(const VerifyParams& p, hipStream_t stream);
 void launch_rowpass(const VerifyParams& p, int grid, hipStream_t stream);
 void launch_draw(const VerifyParams& p, hipStream_t stream);

@@ -44,13 +44,13 @@ __device__ __forceinline__ int32_t block_excl_scan_i(int32_t v, int32_t* lds, in
     if (lane >= d) x += o;
   }
   if (lane == kWave - 1) lds[wave] = x;
-  __syncthreads();
+  lds_barrier();
   int32_t base = 0, tot = 0;
   for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
     if (w < wave) base += lds[w];
     tot += lds[w];
   }
-  __syncthreads();
+  lds_barrier();
   *total = tot;
   return base + x - v;
 }
@@ -75,16 +75,28 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
     int32_t tp, ts;
     const int32_t op = carry_pairs + block_excl_scan_i(np, lds, &tp);
     const int32_t os = carry_singles + block_excl_scan_i(ns, lds, &ts);
-    for (int k = 0; k < np; ++k) p.plan_pairs[op + k] = ((uint32_t)r << 7) | (uint32_t)k;
-    for (int j = 0; j < ns; ++j)
-      p.plan_singles[os + j] = ((uint32_t)r << 7) | (uint32_t)((T > 0.0f) ? n : j);
+    if (np > 0 || ns > 0) {
+      const int64_t t0 = p.target_row0[r];
+      const int64_t d0 = (np > 0) ? p.draft_row0[r] : 0;
+      for (int k = 0; k < np; ++k)
+        p.plan_pairs[op + k] = PlanItem{t0 + k, d0 + k, ((uint32_t)r << 7) | (uint32_t)k, T, 0u, 0u};
+      for (int j = 0; j < ns; ++j) {
+        const int k = (T > 0.0f) ? n : j;
+        p.plan_singles[os + j] = PlanItem{t0 + k, 0, ((uint32_t)r << 7) | (uint32_t)k, T, 0u, 0u};
+      }
+    }
     carry_pairs += tp;
     carry_singles += ts;
   }
   if (threadIdx.x == 0) {
     p.plan_counts[0] = carry_pairs;
     p.plan_counts[1] = carry_singles;
+    *p.sync_error = 0;
   }
+  // The team row pass tells fresh exchange words from stale ones by their tag
+  // (never 0 once written): clear them before every launch.
+  uint4* xch = reinterpret_cast<uint4*>(p.team_xch);
+  for (int i = threadIdx.x; i < kTeamXchWords / 2; i += kPlanThreads) xch[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -213,12 +225,12 @@ __device__ __forceinline__ float stream_overlap(const typename E::Storage* prow,
 }
 
 template <typename E>
-__device__ void pair_item(const VerifyParams& p, uint32_t item, SoftmaxPart* lds_sm,
+__device__ void pair_item(const VerifyParams& p, const PlanItem& it, SoftmaxPart* lds_sm,
                           float* lds_f) {
-  const int r = (int)(item >> 7), k = (int)(item & 127u);
-  const float sl = kLog2e / p.temperature[r];
-  const auto* prow = row_ptr<E>(p.target, p.target_row0[r] + k, p.stride);
-  const auto* qrow = row_ptr<E>(p.draft, p.draft_row0[r] + k, p.stride);
+  const int r = (int)(it.code >> 7), k = (int)(it.code & 127u);
+  const float sl = kLog2e / it.T;
+  const auto* prow = row_ptr<E>(p.target, it.trow, p.stride);
+  const auto* qrow = row_ptr<E>(p.draft, it.drow, p.stride);
   SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
   stream_softmax<E, true>(prow, qrow, 0, p.V, sl, sp, sq);
   sp = block_merge(sp, sl, lds_sm);
@@ -241,13 +253,13 @@ __device__ void pair_item(const VerifyParams& p, uint32_t item, SoftmaxPart* lds
 }
 
 template <typename E>
-__device__ void single_item(const VerifyParams& p, uint32_t item, int seg, SoftmaxPart* lds_sm,
-                            ArgMax* lds_am) {
+__device__ void single_item(const VerifyParams& p, const PlanItem& it, int seg,
+                            SoftmaxPart* lds_sm, ArgMax* lds_am) {
   using S = typename E::Storage;
   constexpr int VEC = E::kPerVec;
-  const int r = (int)(item >> 7), k = (int)(item & 127u);
-  const float T = p.temperature[r];
-  const S* prow = row_ptr<E>(p.target, p.target_row0[r] + k, p.stride);
+  const int r = (int)(it.code >> 7), k = (int)(it.code & 127u);
+  const float T = it.T;
+  const S* prow = row_ptr<E>(p.target, it.trow, p.stride);
   const int64_t lo = (int64_t)seg * p.seg1;
   const int64_t hi = min(p.V, lo + (int64_t)p.seg1);
   const int64_t slot = ((int64_t)r * (p.D + 1) + k) * p.S1 + seg;

@@ -1,0 +1,544 @@
+// sv_rowteam.hip -- the row pass with each row pair read from HBM once.
+//
+// Per T > 0 draft position the statistics pass needs both rows' softmax
+// normalisers and then, with the full-row normalisers, sum_y min(p, q)
+// (equation L_e2e of "AngelSpec: specialize the drafter...", section "MTP";
+// one target pass over all drafts, "Tencent open-sources AngelSpec", section
+// "Why one universal drafter underperforms").  The second sum needs the first
+// pass finished over the whole row, so a row pair is split across a team of
+// T workgroups (one per CU, all resident at once): each member keeps its
+// slice of the pair in registers, computes
+// the slice's (max, sum) for both rows, publishes them, and once the whole
+// team has published computes its slice of sum min(p, q) from the same
+// registers.  Nothing is read twice from memory.
+//
+// Each member walks a sequence of units (its team's row pairs, then a share
+// of the single rows: bonus rows at T > 0 and all target rows at T = 0).
+//
+// Workgroup layout: waves 0..14 are data waves, wave 15 is the communication
+// wave.  The data waves only load rows and reduce them to per-wave states
+// in LDS; the communication wave combines those states, writes the partial
+// slots, publishes to the team, waits for the team and hands the row
+// normalisers back through LDS.  Loads complete in order per wave, so any
+// wave that waited on a fresh global load (a poll) would also wait for all
+// of its earlier row loads; keeping polls out of the data waves keeps their
+// prefetches in flight.  For the same reason every data wave issues exactly
+// the same loads on every path (lanes and units without data read a fixed
+// dummy line), which lets the compiler wait on the oldest unit only.
+//
+// Software pipeline, step s: the data waves issue the loads of unit s + 2,
+// take the first pass of unit s and then the second pass of unit s - 1,
+// whose team normalisers the communication wave has gathered while the data
+// waves were in the first pass of unit s.  Four register buffers rotate
+// (s - 1, s, and two units in flight).
+//
+// Team exchange: member m publishes its slice states of its n-th row pair as
+// four 64-bit words (value bits | (n + 1) << 32) in ring slot n mod 4; a
+// reader accepts a word only if its tag is n + 1, so no fences are needed.
+// A member publishes n only after it has read every member's n - 1, and a
+// member publishes n - 1 only after it has read every member's n - 2, so a
+// ring slot is never overwritten before all its readers are done.  The words
+// are cleared before each launch.  The wait is bounded; on expiry the kernel
+// sets an error word that the accept kernel turns into SV_BIT_SYNC_TIMEOUT
+// on every request, and the member stops waiting.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "specverify.h"
+#include "sv_block.hpp"
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+
+namespace sv {
+
+constexpr int kTeamThreads = 1024;
+constexpr int kDataWaves = kTeamThreads / kWave - 1;
+constexpr int kDataThreads = kDataWaves * kWave;
+constexpr uint32_t kSpinLimit = 1u << 20;  // polls; a normal wait takes a few
+
+template <int NV>
+struct Regs {
+  uint4 p[NV];
+  uint4 q[NV];
+};
+
+struct UnitDesc {
+  int32_t kind;   // 0 none, 1 row pair, 2 single row
+  int32_t slice;  // slice index (team member for pairs)
+  int64_t pair_ordinal;
+  PlanItem item;  // rows, request / position, temperature
+};
+
+// Shared state, double-buffered by unit parity (see the step order above).
+struct TeamLds {
+  SoftmaxPart sm[2][kDataWaves][2];  // per-wave (max, sum) of p and q
+  ArgMax am[2][kDataWaves];          // per-wave arg max at T = 0
+  float acc[2][kDataWaves];          // per-wave sum of min(p, q)
+  float c[2][2];                     // team log2 normalisers of p and q
+  int ok[2];
+};
+
+// Work items are read-only here and uniform across the workgroup: read them
+// through the constant address space, so that they become scalar loads that
+// count against the scalar-memory counter rather than the in-order vector-load
+// counter that tracks the rows in flight.
+__device__ __forceinline__ PlanItem load_item(const PlanItem* items, int64_t n) {
+  const __attribute__((address_space(4))) PlanItem* c =
+      (const __attribute__((address_space(4))) PlanItem*)items;
+  PlanItem it;
+  it.trow = c[n].trow;
+  it.drow = c[n].drow;
+  it.code = c[n].code;
+  it.T = c[n].T;
+  it.pad0 = 0u;
+  it.pad1 = 0u;
+  return it;
+}
+
+__device__ __forceinline__ UnitDesc no_unit() {
+  UnitDesc u;
+  u.kind = 0;
+  u.slice = 0;
+  u.pair_ordinal = 0;
+  u.item = PlanItem{0, 0, 0u, 0.0f, 0u, 0u};
+  return u;
+}
+
+// Unit j of this workgroup: its team's row pairs first, then single-row
+// slices dealt round-robin over the whole grid.
+__device__ __forceinline__ UnitDesc unit_at(const VerifyParams& p, int64_t j, int64_t n,
+                                            int team, int member, int64_t my_pairs) {
+  if (j >= n) return no_unit();
+  UnitDesc u;
+  if (j < my_pairs) {
+    u.kind = 1;
+    u.item = load_item(p.plan_pairs, (int64_t)team + (int64_t)p.nteams * j);
+    u.slice = member;
+    u.pair_ordinal = j;
+  } else {
+    const int64_t su = (int64_t)blockIdx.x + (int64_t)gridDim.x * (j - my_pairs);
+    u.kind = 2;
+    u.item = load_item(p.plan_singles, su / p.team);
+    u.slice = (int)(su % p.team);
+    u.pair_ordinal = 0;
+  }
+  return u;
+}
+
+__device__ __forceinline__ bool wants_alpha(const VerifyParams& p, const UnitDesc& u) {
+  return u.kind == 1 && p.alpha != nullptr;
+}
+
+__device__ __forceinline__ int64_t unit_slot(const VerifyParams& p, const UnitDesc& u) {
+  const int64_t unit = (int64_t)(u.item.code >> 7) * (p.D + 1) + (u.item.code & 127u);
+  return unit * p.S1 + u.slice;
+}
+
+template <typename E>
+__device__ __forceinline__ void slice_bounds(const VerifyParams& p, int slice, int64_t* lo,
+                                             int64_t* vhi, int64_t* hi) {
+  constexpr int VEC = E::kPerVec;
+  *lo = (int64_t)slice * p.team_len;
+  *hi = min(p.V, *lo + (int64_t)p.team_len);
+  if (*hi < *lo) *hi = *lo;
+  *vhi = *lo + ((*hi - *lo) / VEC) * VEC;
+}
+
+template <typename E>
+__device__ __forceinline__ int64_t slice_vectors(const VerifyParams& p, const UnitDesc& u) {
+  int64_t lo, vhi, hi;
+  slice_bounds<E>(p, u.slice, &lo, &vhi, &hi);
+  return u.kind == 0 ? 0 : (vhi - lo) / E::kPerVec;
+}
+
+// Issues the 2 * NV loads of a unit.  Vectors outside the slice, the draft
+// row of a single row and every vector of an empty unit read the dummy line
+// instead; the passes mask them out.
+template <typename E, int NV>
+__device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc& u, Regs<NV>& R,
+                                          const uint4* dummy) {
+  using S = typename E::Storage;
+  constexpr int VEC = E::kPerVec;
+  const int64_t lo = (int64_t)u.slice * p.team_len;
+  const int64_t nvec = slice_vectors<E>(p, u);
+  const S* prow = row_ptr<E>(p.target, u.item.trow, p.stride) + lo;
+  const S* qrow = row_ptr<E>(p.draft, u.item.drow, p.stride) + lo;
+  const bool pair = u.kind == 1;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+    const bool in = v < nvec;
+    const void* pa = in ? (const void*)(prow + v * VEC) : (const void*)dummy;
+    const void* qa = (in && pair) ? (const void*)(qrow + v * VEC) : (const void*)dummy;
+    R.p[i] = load16(pa);
+    R.q[i] = load16(qa);
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ uint4 masked(const uint4& v, bool in) {
+  const uint32_t w = E::kNegInfWord;
+  return in ? v : make_uint4(w, w, w, w);
+}
+
+// ---------------------------------------------------------------------------
+// Data waves.
+
+// First pass of a unit over this thread's vectors: (max, sum) of the slice
+// for p (and q for a pair), or the slice arg max at T = 0; one state per
+// wave into LDS.
+template <typename E, int NV>
+__device__ __forceinline__ void first_pass_data(const VerifyParams& p, const UnitDesc& u,
+                                                const Regs<NV>& R, TeamLds& L, int b) {
+  constexpr int VEC = E::kPerVec;
+  if (u.kind == 0) return;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const float T = u.item.T;
+  const int64_t nvec = slice_vectors<E>(p, u);
+  int64_t lo, vhi, hi;
+  slice_bounds<E>(p, u.slice, &lo, &vhi, &hi);
+  const auto* prow = row_ptr<E>(p.target, u.item.trow, p.stride);
+  if (u.kind == 2 && T == 0.0f) {
+    // arg max of this thread's vectors: best vector in order, then its first
+    // maximal element (NaN propagates through the maximum)
+    float best = -INFINITY;
+    int bi = -1;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+      float x[VEC];
+      E::unpack(masked<E>(R.p[i], v < nvec), x);
+      float cm = x[0];
+#pragma unroll
+      for (int j = 1; j < VEC; ++j) cm = vmax(cm, x[j]);
+      const bool up = cm > best;
+      best = vmax(best, cm);
+      bi = up ? i : bi;
+    }
+    ArgMax a{best, INT32_MAX};
+    if (best == best && bi >= 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (i != bi) continue;
+        float x[VEC];
+        E::unpack(R.p[i], x);
+        const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+#pragma unroll
+        for (int j = VEC - 1; j >= 0; --j)
+          if (x[j] == best) a.i = (int32_t)(lo + v * VEC + j);
+      }
+    }
+    for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads)
+      a = argmax_merge(a, ArgMax{E::load1(prow, i), (int32_t)i});
+    for (int m = 1; m < kWave; m <<= 1) {
+      ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
+      a = argmax_merge(a, o);
+    }
+    if (lane == 0) L.am[b][wave] = a;
+    return;
+  }
+  const float sl = kLog2e / T;
+  float x[VEC * NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+    E::unpack(masked<E>(R.p[i], v < nvec), *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
+  }
+  SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
+  softmax_group<VEC * NV>(sp, x, sl);
+  for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
+    float x1[1] = {E::load1(prow, i)};
+    softmax_group<1>(sp, x1, sl);
+  }
+  if (u.kind == 1) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+      E::unpack(masked<E>(R.q[i], v < nvec), *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
+    }
+    softmax_group<VEC * NV>(sq, x, sl);
+    const auto* qrow = row_ptr<E>(p.draft, u.item.drow, p.stride);
+    for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
+      float x1[1] = {E::load1(qrow, i)};
+      softmax_group<1>(sq, x1, sl);
+    }
+  }
+  sp = wave_merge(sp, sl);
+  sq = wave_merge(sq, sl);
+  if (lane == 0) {
+    L.sm[b][wave][0] = sp;
+    L.sm[b][wave][1] = sq;
+  }
+}
+
+// Second pass of a row pair: this thread's share of sum min(p, q) with the
+// team's normalisers; one sum per wave into LDS.
+template <typename E, int NV>
+__device__ __forceinline__ void second_pass_data(const VerifyParams& p, const UnitDesc& u,
+                                                 const Regs<NV>& R, TeamLds& L, int b) {
+  constexpr int VEC = E::kPerVec;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const float sl = kLog2e / u.item.T;
+  const float cp = L.c[b][0], cq = L.c[b][1];
+  const bool ok = L.ok[b] != 0;
+  float acc = 0.0f;
+  if (ok) {
+    const int64_t nvec = slice_vectors<E>(p, u);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+      float a[VEC], c[VEC], e[VEC];
+      E::unpack(masked<E>(R.p[i], v < nvec), a);
+      E::unpack(masked<E>(R.q[i], v < nvec), c);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        e[j] = exp2_fast(fminf(__builtin_fmaf(a[j], sl, -cp), __builtin_fmaf(c[j], sl, -cq)));
+#pragma unroll
+      for (int w = 1; w < VEC; w <<= 1) {
+#pragma unroll
+        for (int j = 0; j + w < VEC; j += 2 * w) e[j] += e[j + w];
+      }
+      acc += e[0];
+    }
+    int64_t lo, vhi, hi;
+    slice_bounds<E>(p, u.slice, &lo, &vhi, &hi);
+    const auto* prow = row_ptr<E>(p.target, u.item.trow, p.stride);
+    const auto* qrow = row_ptr<E>(p.draft, u.item.drow, p.stride);
+    for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads)
+      acc += exp2_fast(fminf(__builtin_fmaf(E::load1(prow, i), sl, -cp),
+                             __builtin_fmaf(E::load1(qrow, i), sl, -cq)));
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) L.acc[b][wave] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Communication wave.
+
+// Combines the data waves' first-pass states of a unit (a fixed reduction
+// tree over the lanes), writes the partial slots and publishes a pair.
+__device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const UnitDesc& u,
+                                                const TeamLds& L, int b, int team, int member) {
+  if (u.kind == 0) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t slot = unit_slot(p, u);
+  if (u.kind == 2 && u.item.T == 0.0f) {
+    ArgMax a = (lane < kDataWaves) ? L.am[b][lane] : ArgMax{-INFINITY, INT32_MAX};
+    for (int m = 1; m < kWave; m <<= 1) {
+      ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
+      a = argmax_merge(a, o);
+    }
+    if (lane == 0) p.part_p[slot] = make_float2(a.v, __int_as_float(a.i));
+    return;
+  }
+  const float sl = kLog2e / u.item.T;
+  SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
+  if (lane < kDataWaves) {
+    sp = L.sm[b][lane][0];
+    sq = L.sm[b][lane][1];
+  }
+  sp = wave_merge(sp, sl);
+  sq = wave_merge(sq, sl);
+  if (lane == 0) {
+    p.part_p[slot] = make_float2(sp.m, sp.z);
+    if (u.kind == 1) p.part_q[slot] = make_float2(sq.m, sq.z);
+  }
+  if (wants_alpha(p, u) && lane < 4) {
+    const float v = lane == 0 ? sp.m : lane == 1 ? sp.z : lane == 2 ? sq.m : sq.z;
+    const uint64_t tag = (uint64_t)(uint32_t)(u.pair_ordinal + 1) << 32;
+    const int64_t rec = ((int64_t)team * 4 + (u.pair_ordinal & 3)) * p.team + member;
+    __hip_atomic_store(&p.team_xch[rec * 4 + lane], tag | (uint64_t)__float_as_uint(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Waits until every member of the team has published row pair u, then
+// combines the members' states into the row log2 normalisers (member 0 also
+// stores the row states in its slots).
+__device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const UnitDesc& u,
+                                               TeamLds& L, int b, int team, int member,
+                                               bool& failed) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nt = p.team;
+  const uint32_t need = (uint32_t)(u.pair_ordinal + 1);
+  const int64_t rec = ((int64_t)team * 4 + (u.pair_ordinal & 3)) * nt + lane;
+  uint64_t w[4] = {0, 0, 0, 0};
+  bool done = false;
+  const uint32_t limit = failed ? 1u : kSpinLimit;
+  for (uint32_t spin = 0; spin < limit; ++spin) {
+    bool mine = true;
+    if (lane < nt) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        w[k] = __hip_atomic_load(&p.team_xch[rec * 4 + k], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        mine = mine && (uint32_t)(w[k] >> 32) == need;
+      }
+    }
+    if (__all(mine)) {
+      done = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!done) {
+    if (!failed && lane == 0)
+      __hip_atomic_store(p.sync_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    failed = true;
+  }
+  const float sl = kLog2e / u.item.T;
+  SoftmaxPart a{-INFINITY, 0.0f}, c{-INFINITY, 0.0f};
+  if (lane < nt) {
+    a = SoftmaxPart{__uint_as_float((uint32_t)w[0]), __uint_as_float((uint32_t)w[1])};
+    c = SoftmaxPart{__uint_as_float((uint32_t)w[2]), __uint_as_float((uint32_t)w[3])};
+  }
+  a = wave_merge(a, sl);
+  c = wave_merge(c, sl);
+  if (lane == 0) {
+    // Member 0 replaces its slice states with the row states, so that the
+    // accept kernel reads one slot per row of a pair.
+    if (member == 0) {
+      const int64_t slot = unit_slot(p, u);
+      p.part_p[slot] = make_float2(a.m, a.z);
+      p.part_q[slot] = make_float2(c.m, c.z);
+    }
+    const bool ok = a.m == a.m && c.m == c.m && fabsf(a.m) < INFINITY && fabsf(c.m) < INFINITY;
+    L.ok[b] = ok;
+    L.c[b][0] = ok ? __builtin_fmaf(a.m, sl, __log2f(a.z)) : 0.0f;
+    L.c[b][1] = ok ? __builtin_fmaf(c.m, sl, __log2f(c.z)) : 0.0f;
+  }
+}
+
+// Sum of the data waves' second-pass sums into the partial slot.
+__device__ __forceinline__ void second_pass_comm(const VerifyParams& p, const UnitDesc& u,
+                                                 const TeamLds& L, int b) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float a = (lane < kDataWaves) ? L.acc[b][lane] : 0.0f;
+  a = wave_sum(a);
+  if (lane == 0) p.part_a[unit_slot(p, u)] = a;
+}
+
+// ---------------------------------------------------------------------------
+
+template <typename E, int NV>
+__global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
+  __shared__ TeamLds L;
+  const int nt = p.team;
+  const int team = (int)blockIdx.x / nt;
+  const int member = (int)blockIdx.x % nt;
+  const int64_t n_pairs = p.plan_counts[0];
+  const int64_t n_single_units = (int64_t)p.plan_counts[1] * nt;
+  const int64_t my_pairs =
+      (team < p.nteams && n_pairs > team) ? (n_pairs - 1 - team) / p.nteams + 1 : 0;
+  const int64_t my_singles =
+      n_single_units > blockIdx.x ? (n_single_units - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int64_t n = my_pairs + my_singles;
+
+  // Both roles run steps s = 0 .. n with one barrier each, then a last one.
+  // Data step s: loads of unit s + 2, first pass of unit s, barrier, second
+  // pass of unit s - 1.  Communication window s (between barriers s and
+  // s + 1): sum of the second pass of unit s - 2, combination and publication
+  // of the first pass of unit s, team wait for unit s.  The team wait thus
+  // overlaps the data waves' next second and first passes.
+  if (threadIdx.x < kDataThreads) {
+    const uint4* dummy = reinterpret_cast<const uint4*>(p.plan_counts);
+    Regs<NV> R0, R1, R2, R3;
+    UnitDesc U0 = unit_at(p, 0, n, team, member, my_pairs);
+    UnitDesc U1 = unit_at(p, 1, n, team, member, my_pairs);
+    UnitDesc U2 = no_unit(), U3 = no_unit();
+    UnitDesc un = unit_at(p, 2, n, team, member, my_pairs);
+    load_unit<E, NV>(p, U0, R0, dummy);
+    load_unit<E, NV>(p, U1, R1, dummy);
+    // Step s: first pass on buffer s mod 4, second pass on buffer s - 1
+    // mod 4, loads into buffer s + 2 mod 4.
+    auto step = [&](int64_t s, const Regs<NV>& Rf, const UnitDesc& Uf, const Regs<NV>& Rs,
+                    const UnitDesc& Us, Regs<NV>& Rl, UnitDesc& Ul) {
+      Ul = un;
+      load_unit<E, NV>(p, Ul, Rl, dummy);
+      un = unit_at(p, s + 3, n, team, member, my_pairs);
+      first_pass_data<E, NV>(p, Uf, Rf, L, (int)(s & 1));
+      lds_barrier();
+      if (wants_alpha(p, Us)) second_pass_data<E, NV>(p, Us, Rs, L, (int)((s - 1) & 1));
+    };
+    for (int64_t s = 0;; s += 4) {
+      step(s, R0, U0, R3, U3, R2, U2);
+      if (s + 1 > n) break;
+      step(s + 1, R1, U1, R0, U0, R3, U3);
+      if (s + 2 > n) break;
+      step(s + 2, R2, U2, R1, U1, R0, U0);
+      if (s + 3 > n) break;
+      step(s + 3, R3, U3, R2, U2, R1, U1);
+      if (s + 4 > n) break;
+    }
+    lds_barrier();
+  } else {
+    bool failed = false;
+    UnitDesc um2 = no_unit(), um1 = no_unit();
+    for (int64_t s = 0; s <= n; ++s) {
+      const UnitDesc u = unit_at(p, s, n, team, member, my_pairs);
+      lds_barrier();
+      if (wants_alpha(p, um2)) second_pass_comm(p, um2, L, (int)(s & 1));
+      first_pass_comm(p, u, L, (int)(s & 1), team, member);
+      if (wants_alpha(p, u)) team_wait_comm(p, u, L, (int)(s & 1), team, member, failed);
+      um2 = um1;
+      um1 = u;
+    }
+    lds_barrier();
+    // um2 is now the last unit, n - 1
+    if (wants_alpha(p, um2)) second_pass_comm(p, um2, L, (int)((n - 1) & 1));
+  }
+}
+
+// Team geometry for a row of V elements: NV <= 2 16-byte vectors per data
+// thread per row (four buffers of two rows stay in registers), T members per
+// row.  Returns false if a row needs more than 64 members (the caller then
+// uses the streaming row pass).
+bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
+                   int32_t* slice_len) {
+  const int64_t vec = (dtype == SV_DTYPE_BF16) ? 8 : 4;
+  const int64_t rowvec = (V + vec - 1) / vec;
+  int64_t nv = (rowvec + kDataThreads - 1) / kDataThreads;
+  if (nv > 2) nv = 2;
+  if (nv < 1) nv = 1;
+  const int64_t t = (rowvec + kDataThreads * nv - 1) / (kDataThreads * nv);
+  if (t > 64 || t > grid) return false;
+  const int64_t svec = (rowvec + t - 1) / t;
+  *T = (int32_t)t;
+  *NV = (int32_t)((svec + kDataThreads - 1) / kDataThreads);
+  *slice_len = (int32_t)(svec * vec);
+  return true;
+}
+
+// The team kernel needs every workgroup of a team resident at once.  The grid
+// is at most one workgroup per CU and the kernel must fit at least one
+// workgroup per CU (checked once per variant), so on a device that is not
+// running other work every workgroup is resident from the start.  (A plain
+// launch: the cooperative launch path costs more than ten microseconds of
+// launch latency here.)  On a shared device the team wait is still bounded.
+template <typename E, int NV>
+static hipError_t launch_team_t(VerifyParams& p, int grid, hipStream_t stream) {
+  static std::atomic<int> per_cu{-1};
+  int fit = per_cu.load(std::memory_order_relaxed);
+  if (fit < 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_rowteam<E, NV>, kTeamThreads, 0) !=
+        hipSuccess)
+      nb = 0;
+    fit = nb;
+    per_cu.store(fit, std::memory_order_relaxed);
+  }
+  if (fit < 1) return hipErrorLaunchOutOfResources;
+  hipLaunchKernelGGL((k_rowteam<E, NV>), dim3((unsigned)grid), dim3(kTeamThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowteam(VerifyParams& p, int grid, int nv, hipStream_t stream) {
+  if (p.dtype == SV_DTYPE_BF16)
+    return nv == 1 ? launch_team_t<Bf16, 1>(p, grid, stream) : launch_team_t<Bf16, 2>(p, grid, stream);
+  return nv == 1 ? launch_team_t<F32, 1>(p, grid, stream) : launch_team_t<F32, 2>(p, grid, stream);
+}
+
+}  // namespace sv

@@ -27,23 +27,37 @@
 namespace sv {
 
 
-// Merge the nseg segment states of a row (fixed order).  A row pair's rows
-// have one state each (slot 0); single rows have S1 segment states.
+// Merge the nseg segment states of a row (fixed order).  The slot loads are
+// issued kMergeChunk at a time so that a row costs one memory latency per
+// chunk rather than one per slot.
+constexpr int kMergeChunk = 16;
+
 __device__ __forceinline__ SoftmaxPart merge_row(const float2* parts, int64_t unit, int S1,
                                                  int nseg, float sl) {
   SoftmaxPart s{-INFINITY, 0.0f};
-  for (int j = 0; j < nseg; ++j) {
-    float2 v = parts[unit * S1 + j];
-    s = merge_parts(s, SoftmaxPart{v.x, v.y}, sl);
+  const float2* row = parts + unit * S1;
+  for (int j0 = 0; j0 < nseg; j0 += kMergeChunk) {
+    float2 v[kMergeChunk];
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i)
+      v[i] = (j0 + i < nseg) ? row[j0 + i] : make_float2(-INFINITY, 0.0f);
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) s = merge_parts(s, SoftmaxPart{v[i].x, v[i].y}, sl);
   }
   return s;
 }
 
 __device__ __forceinline__ ArgMax merge_row_argmax(const float2* parts, int64_t unit, int S1) {
   ArgMax a{-INFINITY, INT32_MAX};
-  for (int j = 0; j < S1; ++j) {
-    float2 v = parts[unit * S1 + j];
-    a = argmax_merge(a, ArgMax{v.x, __float_as_int(v.y)});
+  const float2* row = parts + unit * S1;
+  for (int j0 = 0; j0 < S1; j0 += kMergeChunk) {
+    float2 v[kMergeChunk];
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i)
+      v[i] = (j0 + i < S1) ? row[j0 + i] : make_float2(-INFINITY, __int_as_float(INT32_MAX));
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i)
+      a = argmax_merge(a, ArgMax{v[i].x, __float_as_int(v[i].y)});
   }
   return a;
 }
@@ -70,6 +84,7 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
   __syncthreads();
 
   uint32_t bits = 0u;
+  if (*p.sync_error) bits |= SV_BIT_SYNC_TIMEOUT;
   if (n < 0 || n > D) bits |= SV_BIT_BAD_DEPTH;
   if (!temperature_ok(T)) bits |= SV_BIT_BAD_TEMPERATURE;
   const bool live = (bits == 0u) && k <= n;
@@ -92,13 +107,13 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       if (k < n) keep = (d == am.i);
     } else {
       sl = kLog2e / T;
-      sp = merge_row(p.part_p, unit, p.S1, (k < n) ? 1 : p.S1, sl);
+      sp = merge_row(p.part_p, unit, p.S1, (k < n) ? p.pair_slots : p.S1, sl);
       if (!finite_f(sp.m)) bits |= SV_BIT_BAD_ROW;
       if (k < n) {
         if (p.draft == nullptr) {
           bits |= SV_BIT_BAD_ROW;
         } else {
-          sq = merge_row(p.part_q, unit, p.S1, 1, sl);
+          sq = merge_row(p.part_q, unit, p.S1, p.pair_slots, sl);
           if (!finite_f(sq.m)) bits |= SV_BIT_BAD_ROW;
         }
       }
@@ -154,7 +169,14 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       if (T == 0.0f) {
         a = keep ? 1.0f : 0.0f;
       } else {
-        a = p.part_a[unit * p.S1];
+        const float* pa = p.part_a + unit * p.S1;
+        for (int j0 = 0; j0 < p.alpha_slots; j0 += kMergeChunk) {
+          float v[kMergeChunk];
+#pragma unroll
+          for (int i = 0; i < kMergeChunk; ++i) v[i] = (j0 + i < p.alpha_slots) ? pa[j0 + i] : 0.0f;
+#pragma unroll
+          for (int i = 0; i < kMergeChunk; ++i) a += v[i];
+        }
       }
     }
     p.alpha[(int64_t)r * D + k] = a;
@@ -197,15 +219,44 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
 // ---------------------------------------------------------------------------
 // Host-side launch sequence.
 static void mark(const VerifyParams& p, int i, hipStream_t stream) {
-  if (p.events) (void)hipEventRecord(static_cast<hipEvent_t>(p.events[i]), stream);
+  if (p.events && p.events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(p.events[i]), stream);
 }
 
 template <typename E>
-static hipError_t launch_all(const VerifyParams& p, int grid, hipStream_t stream) {
+static hipError_t launch_all(VerifyParams& p, int grid, hipStream_t stream) {
+  // Team row pass when a row fits a team of at most 64 members and the team
+  // kernel fits one workgroup per CU; otherwise the streaming row pass.
+  int32_t T = 0, nv = 0, slice = 0;
+  const bool team = (p.flags & SV_FLAG_STREAMING_ROW_PASS) == 0u && grid <= kMaxTeamGrid &&
+                    team_geometry(p.dtype, p.V, grid, &T, &nv, &slice);
+  if (team) {
+    p.S1 = T;
+    // with acceptance rates the team pass stores a pair's row states in slot 0
+    p.pair_slots = p.alpha ? 1 : T;
+    p.alpha_slots = T;
+    p.team = T;
+    p.nteams = grid / T;
+    p.team_len = slice;
+  } else {
+    p.pair_slots = 1;
+    p.alpha_slots = 1;
+    p.team = 0;
+    p.nteams = 0;
+  }
   mark(p, 0, stream);
   launch_plan(p, stream);
   mark(p, 1, stream);
-  launch_rowpass(p, grid, stream);
+  bool done = false;
+  if (team) done = launch_rowteam(p, grid, nv, stream) == hipSuccess;
+  if (!done) {
+    (void)hipGetLastError();
+    if (team) {  // fall back: streaming pass with its own slot layout
+      stats_geometry(p.B, p.D, p.V, &p.S1, &p.seg1);
+      p.pair_slots = 1;
+      p.alpha_slots = 1;
+    }
+    launch_rowpass(p, grid, stream);
+  }
   mark(p, 2, stream);
   hipLaunchKernelGGL(k_accept<E>, dim3((unsigned)p.B), dim3(128), 0, stream, p);
   mark(p, 3, stream);
@@ -214,7 +265,7 @@ static hipError_t launch_all(const VerifyParams& p, int grid, hipStream_t stream
   return hipGetLastError();
 }
 
-hipError_t launch_verify(const VerifyParams& p, int grid, hipStream_t stream) {
+hipError_t launch_verify(VerifyParams& p, int grid, hipStream_t stream) {
   return (p.dtype == SV_DTYPE_BF16) ? launch_all<Bf16>(p, grid, stream)
                                     : launch_all<F32>(p, grid, stream);
 }

@@ -27,6 +27,7 @@ SV_DTYPE_FP32 = 1
 SV_MAX_DEPTH = 64
 SV_MAX_BUDGET_POSITIONS = 4096
 SV_FLAG_FORCE_FP64_DRAW = 1
+SV_FLAG_STREAMING_ROW_PASS = 2
 SV_NUM_STAGE_EVENTS = 5
 
 BIT_BAD_DEPTH = 1
@@ -35,6 +36,7 @@ BIT_BAD_ROW = 4
 BIT_RESIDUAL_ZERO = 8
 BIT_BAD_TEMPERATURE = 16
 BIT_FP64_DRAW = 32
+BIT_SYNC_TIMEOUT = 64
 
 EXPORTS = ["sv_status_string", "sv_version", "sv_k_rho", "sv_allocate_budget",
            "sv_verify_workspace_bytes", "sv_verify_batch", "sv_accept_stats"]
@@ -239,16 +241,18 @@ class Verifier:
 
     def set_stage_events(self, events):
         """Ask for SV_NUM_STAGE_EVENTS torch.cuda.Event objects (timing
-        enabled) to be recorded at the stage boundaries; None switches off."""
+        enabled; an entry may be None) to be recorded at the stage
+        boundaries; None switches off."""
         if events is None:
             self.args.stage_events = None
             self._events = None
             return
         assert len(events) == SV_NUM_STAGE_EVENTS
         for e in events:  # torch creates the HIP event on first record
-            if e.cuda_event == 0:
+            if e is not None and e.cuda_event == 0:
                 e.record()
-        self._events = (ctypes.c_void_p * SV_NUM_STAGE_EVENTS)(*[e.cuda_event for e in events])
+        self._events = (ctypes.c_void_p * SV_NUM_STAGE_EVENTS)(
+            *[e.cuda_event if e is not None else None for e in events])
         self.args.stage_events = ctypes.cast(self._events, ctypes.c_void_p)
 
     def run(self) -> VerifyOutputs:

@@ -67,7 +67,7 @@ def test_c3_block_t1_sampled():
     full_depth_case("c3", sample=[0, 5, 13, 31])
 
 
-def budget_case(name, sample=None, packed=True):
+def budget_case(name, sample=None, packed=True, flags=0):
     w = synth.make(name, device=DEV)
     conf = w.conf.to(DEV).contiguous()
     bud = sv.allocate_budget(conf, w.K)
@@ -90,7 +90,8 @@ def budget_case(name, sample=None, packed=True):
         tr0 = bud["target_row0"]
     else:
         target, tr0 = w.target, tr0_pad
-    g = gpu_verify(target, w.draft, tr0, dr0, w.draft_tokens, bud["depth"], w.temperature)
+    g = gpu_verify(target, w.draft, tr0, dr0, w.draft_tokens, bud["depth"], w.temperature,
+                   flags=flags)
     th, dh = host_f32(target).reshape(-1, V), host_f32(w.draft).reshape(-1, V)
     temps = w.temperature.cpu().numpy()
     reqs = np.arange(B) if sample is None else np.asarray(sample)
@@ -126,3 +127,13 @@ def test_c4full_bench_config_sampled():
     rep, g, depth = budget_case("c4full", sample=[0, 17, 45, 63])
     assert np.all(depth == 16)
     assert np.all(g["num_out"] == g["accepted_len"] + 1)
+
+
+@pytest.mark.parametrize("name,sample", [("c2", None), ("c3_t0", None), ("c3", [0, 5, 13])])
+def test_streaming_row_pass(name, sample):
+    """The streaming row pass (each row pair read twice) instead of the team pass."""
+    full_depth_case(name, sample=sample, flags=sv.SV_FLAG_STREAMING_ROW_PASS)
+
+
+def test_streaming_row_pass_budget_ragged():
+    budget_case("c4", flags=sv.SV_FLAG_STREAMING_ROW_PASS)

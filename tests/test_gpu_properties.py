@@ -55,9 +55,10 @@ def to_dev(P, dtype):
     return torch.from_numpy(P).to(DEV).to(dtype)
 
 
+@pytest.mark.parametrize("row_pass", ["team", "stream"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("trial", range(8))
-def test_random_shapes(dtype, trial):
+def test_random_shapes(dtype, trial, row_pass):
     rng = np.random.default_rng(100 + trial)
     B = int(rng.integers(1, 9))
     D = int(rng.integers(0, 9))
@@ -74,7 +75,8 @@ def test_random_shapes(dtype, trial):
     rid = rng.integers(0, 2**32, size=B, dtype=np.uint64).astype(np.uint32)
     g = gpu_verify(Pd, Qd, tr0, dr0, torch.from_numpy(tokens).to(DEV).reshape(B, D),
                    torch.from_numpy(depth).to(DEV), torch.from_numpy(temps).to(DEV), seed=seed,
-                   step=step, request_id=torch.from_numpy(rid).to(DEV), V=V)
+                   step=step, request_id=torch.from_numpy(rid).to(DEV), V=V,
+                   flags=sv.SV_FLAG_STREAMING_ROW_PASS if row_pass == "stream" else 0)
     # the oracle sees exactly the device values, rows cut to V
     Ph = Pd.float().cpu().numpy()[:, :V].copy()
     Qh = Qd.float().cpu().numpy()[:, :V].copy()
