@@ -48,14 +48,21 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest() -> str:
+# Sources each row-pass kernel is built from: a counter summary stays valid
+# while these are unchanged.
+KERNEL_SOURCES = {
+    "k_rowteam": ["sv_rowteam.hip", "sv_block.hpp", "sv_device.hpp", "sv_internal.hpp"],
+    "k_rowpass": ["sv_rowpass.hip", "sv_block.hpp", "sv_device.hpp", "sv_internal.hpp"],
+}
+
+
+def source_digest(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lossless_draft_verification_softmax_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -218,7 +225,7 @@ def main():
                 for j in range(nev - 1)]
 
     achieved = rowpass_bytes / (rowpass_ms * 1e-3) / 1e9
-    digest = source_digest()
+    digest = source_digest(row_kernel)
     traffic = measured_traffic(row_kernel, args.workload, digest)
     value = n_pos * args.steps / (total_ms * 1e-3)
     res = {

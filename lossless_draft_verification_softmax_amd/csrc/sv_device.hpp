@@ -144,6 +144,21 @@ __device__ __forceinline__ SoftmaxPart wave_merge(SoftmaxPart p, float sl) {
   return {m, wave_sum(z)};
 }
 
+// The same merge with the maximum taken by v_max_f32, which the compiler
+// fuses with the DPP lane moves (the NaN-propagating maximum cannot be);
+// a NaN maximum in any lane is carried by a ballot instead.
+__device__ __forceinline__ SoftmaxPart wave_merge_fast(SoftmaxPart p, float sl) {
+  const bool nan = __ballot(p.m != p.m) != 0ull;
+  float m = wave_allreduce(p.m, [](float a, float b) { return fmaxf(a, b); });
+  float z = (p.m == -INFINITY || m == -INFINITY) ? 0.0f : p.z * exp2_fast((p.m - m) * sl);
+  z = wave_sum(z);
+  if (nan) {
+    m = __int_as_float(0x7fc00000);
+    z = m;
+  }
+  return {m, z};
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies whose high words are xored with the other two counter

@@ -46,7 +46,8 @@ struct PlanItem {
   int64_t drow;   // draft row index (row pairs)
   uint32_t code;  // request << 7 | position
   float T;        // temperature
-  uint32_t pad0, pad1;
+  float sl;       // log2(e) / T (0 at T = 0)
+  uint32_t pad;
 };
 
 struct VerifyParams {

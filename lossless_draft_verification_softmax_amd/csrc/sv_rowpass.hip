@@ -76,13 +76,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
     const int32_t op = carry_pairs + block_excl_scan_i(np, lds, &tp);
     const int32_t os = carry_singles + block_excl_scan_i(ns, lds, &ts);
     if (np > 0 || ns > 0) {
+      const float sl = (T > 0.0f) ? kLog2e / T : 0.0f;
       const int64_t t0 = p.target_row0[r];
       const int64_t d0 = (np > 0) ? p.draft_row0[r] : 0;
       for (int k = 0; k < np; ++k)
-        p.plan_pairs[op + k] = PlanItem{t0 + k, d0 + k, ((uint32_t)r << 7) | (uint32_t)k, T, 0u, 0u};
+        p.plan_pairs[op + k] = PlanItem{t0 + k, d0 + k, ((uint32_t)r << 7) | (uint32_t)k, T, sl, 0u};
       for (int j = 0; j < ns; ++j) {
         const int k = (T > 0.0f) ? n : j;
-        p.plan_singles[os + j] = PlanItem{t0 + k, 0, ((uint32_t)r << 7) | (uint32_t)k, T, 0u, 0u};
+        p.plan_singles[os + j] = PlanItem{t0 + k, 0, ((uint32_t)r << 7) | (uint32_t)k, T, sl, 0u};
       }
     }
     carry_pairs += tp;

@@ -23,20 +23,22 @@
 // wave that waited on a fresh global load (a poll) would also wait for all
 // of its earlier row loads; keeping polls out of the data waves keeps their
 // prefetches in flight.  For the same reason every data wave issues exactly
-// the same loads on every path (lanes and units without data read a fixed
-// dummy line), which lets the compiler wait on the oldest unit only.
+// the same loads on every path (lanes and units without data read a line of
+// -inf), which lets the compiler wait on the oldest unit only.
 //
 // Software pipeline, step s: the data waves issue the loads of unit s + 2,
-// take the first pass of unit s and then the second pass of unit s - 1,
-// whose team normalisers the communication wave has gathered while the data
-// waves were in the first pass of unit s.  Four register buffers rotate
-// (s - 1, s, and two units in flight).
+// take the first pass of unit s and then the second pass of unit s - 2,
+// whose slice they parked in LDS two steps earlier (two slots of
+// 2 * NV * 16 bytes per data thread; each thread reads back only what it
+// wrote) and whose team normalisers the communication wave gathered in the
+// previous step.  Three register buffers rotate (unit s and two units in
+// flight), and a member's wait for its team has a whole step of slack.
 //
 // Team exchange: member m publishes its slice states of its n-th row pair as
 // four 64-bit words (value bits | (n + 1) << 32) in ring slot n mod 4; a
 // reader accepts a word only if its tag is n + 1, so no fences are needed.
-// A member publishes n only after it has read every member's n - 1, and a
-// member publishes n - 1 only after it has read every member's n - 2, so a
+// A member publishes n only after it has read every member's n - 2, and a
+// member publishes n - 2 only after it has read every member's n - 3, so a
 // ring slot is never overwritten before all its readers are done.  The words
 // are cleared before each launch.  The wait is bounded; on expiry the kernel
 // sets an error word that the accept kernel turns into SV_BIT_SYNC_TIMEOUT
@@ -65,11 +67,15 @@ struct Regs {
   uint4 q[NV];
 };
 
+// A unit of work, held in scalar registers.
 struct UnitDesc {
-  int32_t kind;   // 0 none, 1 row pair, 2 single row
-  int32_t slice;  // slice index (team member for pairs)
-  int64_t pair_ordinal;
-  PlanItem item;  // rows, request / position, temperature
+  int64_t trow;     // target row index
+  int64_t drow;     // draft row index (row pairs)
+  uint32_t code;    // request << 7 | position
+  float sl;         // log2(e) / T
+  int32_t kind;     // 0 none, 1 row pair, 2 single row, 3 single row at T = 0
+  int32_t slice;    // slice index (team member for pairs)
+  int32_t ordinal;  // pair ordinal within the team
 };
 
 // Shared state, double-buffered by unit parity (see the step order above).
@@ -85,25 +91,24 @@ struct TeamLds {
 // through the constant address space, so that they become scalar loads that
 // count against the scalar-memory counter rather than the in-order vector-load
 // counter that tracks the rows in flight.
-__device__ __forceinline__ PlanItem load_item(const PlanItem* items, int64_t n) {
+__device__ __forceinline__ void load_item(UnitDesc& u, const PlanItem* items, int64_t n) {
   const __attribute__((address_space(4))) PlanItem* c =
       (const __attribute__((address_space(4))) PlanItem*)items;
-  PlanItem it;
-  it.trow = c[n].trow;
-  it.drow = c[n].drow;
-  it.code = c[n].code;
-  it.T = c[n].T;
-  it.pad0 = 0u;
-  it.pad1 = 0u;
-  return it;
+  u.trow = c[n].trow;
+  u.drow = c[n].drow;
+  u.code = c[n].code;
+  u.sl = c[n].sl;
 }
 
 __device__ __forceinline__ UnitDesc no_unit() {
   UnitDesc u;
+  u.trow = 0;
+  u.drow = 0;
+  u.code = 0u;
+  u.sl = 0.0f;
   u.kind = 0;
   u.slice = 0;
-  u.pair_ordinal = 0;
-  u.item = PlanItem{0, 0, 0u, 0.0f, 0u, 0u};
+  u.ordinal = 0;
   return u;
 }
 
@@ -114,16 +119,19 @@ __device__ __forceinline__ UnitDesc unit_at(const VerifyParams& p, int64_t j, in
   if (j >= n) return no_unit();
   UnitDesc u;
   if (j < my_pairs) {
+    load_item(u, p.plan_pairs, (int64_t)team + (int64_t)p.nteams * j);
     u.kind = 1;
-    u.item = load_item(p.plan_pairs, (int64_t)team + (int64_t)p.nteams * j);
     u.slice = member;
-    u.pair_ordinal = j;
+    u.ordinal = (int32_t)j;
   } else {
     const int64_t su = (int64_t)blockIdx.x + (int64_t)gridDim.x * (j - my_pairs);
-    u.kind = 2;
-    u.item = load_item(p.plan_singles, su / p.team);
+    const int64_t it = su / p.team;
+    load_item(u, p.plan_singles, it);
+    const __attribute__((address_space(4))) PlanItem* c =
+        (const __attribute__((address_space(4))) PlanItem*)p.plan_singles;
+    u.kind = (c[it].T == 0.0f) ? 3 : 2;
     u.slice = (int)(su % p.team);
-    u.pair_ordinal = 0;
+    u.ordinal = 0;
   }
   return u;
 }
@@ -133,7 +141,7 @@ __device__ __forceinline__ bool wants_alpha(const VerifyParams& p, const UnitDes
 }
 
 __device__ __forceinline__ int64_t unit_slot(const VerifyParams& p, const UnitDesc& u) {
-  const int64_t unit = (int64_t)(u.item.code >> 7) * (p.D + 1) + (u.item.code & 127u);
+  const int64_t unit = (int64_t)(u.code >> 7) * (p.D + 1) + (u.code & 127u);
   return unit * p.S1 + u.slice;
 }
 
@@ -154,9 +162,21 @@ __device__ __forceinline__ int64_t slice_vectors(const VerifyParams& p, const Un
   return u.kind == 0 ? 0 : (vhi - lo) / E::kPerVec;
 }
 
+// A 16-byte line of -inf elements (bf16, fp32): the loads of lanes without
+// data read it, so their values drop out of every max and sum unmasked.  It
+// is never written; it is not declared const so that it lives in the global
+// address space like the rows and the loads stay global loads.
+__device__ uint4 kNegInfLine[2] = {{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u},
+                                         {0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u}};
+
+template <typename E>
+__device__ __forceinline__ const uint4* neg_inf_line() {
+  return &kNegInfLine[E::kPerVec == 8 ? 0 : 1];
+}
+
 // Issues the 2 * NV loads of a unit.  Vectors outside the slice, the draft
-// row of a single row and every vector of an empty unit read the dummy line
-// instead; the passes mask them out.
+// row of a single row and every vector of an empty unit read the -inf line
+// instead.
 template <typename E, int NV>
 __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc& u, Regs<NV>& R,
                                           const uint4* dummy) {
@@ -164,8 +184,8 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
   constexpr int VEC = E::kPerVec;
   const int64_t lo = (int64_t)u.slice * p.team_len;
   const int64_t nvec = slice_vectors<E>(p, u);
-  const S* prow = row_ptr<E>(p.target, u.item.trow, p.stride) + lo;
-  const S* qrow = row_ptr<E>(p.draft, u.item.drow, p.stride) + lo;
+  const S* prow = row_ptr<E>(p.target, u.trow, p.stride) + lo;
+  const S* qrow = row_ptr<E>(p.draft, u.drow, p.stride) + lo;
   const bool pair = u.kind == 1;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -178,11 +198,6 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
   }
 }
 
-template <typename E>
-__device__ __forceinline__ uint4 masked(const uint4& v, bool in) {
-  const uint32_t w = E::kNegInfWord;
-  return in ? v : make_uint4(w, w, w, w);
-}
 
 // ---------------------------------------------------------------------------
 // Data waves.
@@ -196,12 +211,10 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
   constexpr int VEC = E::kPerVec;
   if (u.kind == 0) return;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const float T = u.item.T;
-  const int64_t nvec = slice_vectors<E>(p, u);
   int64_t lo, vhi, hi;
   slice_bounds<E>(p, u.slice, &lo, &vhi, &hi);
-  const auto* prow = row_ptr<E>(p.target, u.item.trow, p.stride);
-  if (u.kind == 2 && T == 0.0f) {
+  const auto* prow = row_ptr<E>(p.target, u.trow, p.stride);
+  if (u.kind == 3) {
     // arg max of this thread's vectors: best vector in order, then its first
     // maximal element (NaN propagates through the maximum)
     float best = -INFINITY;
@@ -210,7 +223,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
     for (int i = 0; i < NV; ++i) {
       const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
       float x[VEC];
-      E::unpack(masked<E>(R.p[i], v < nvec), x);
+      E::unpack(R.p[i], x);
       float cm = x[0];
 #pragma unroll
       for (int j = 1; j < VEC; ++j) cm = vmax(cm, x[j]);
@@ -240,12 +253,12 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
     if (lane == 0) L.am[b][wave] = a;
     return;
   }
-  const float sl = kLog2e / T;
+  const float sl = u.sl;
   float x[VEC * NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
-    E::unpack(masked<E>(R.p[i], v < nvec), *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
+    E::unpack(R.p[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
   }
   SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
   softmax_group<VEC * NV>(sp, x, sl);
@@ -257,17 +270,17 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
-      E::unpack(masked<E>(R.q[i], v < nvec), *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
+      E::unpack(R.q[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
     }
     softmax_group<VEC * NV>(sq, x, sl);
-    const auto* qrow = row_ptr<E>(p.draft, u.item.drow, p.stride);
+    const auto* qrow = row_ptr<E>(p.draft, u.drow, p.stride);
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
       float x1[1] = {E::load1(qrow, i)};
       softmax_group<1>(sq, x1, sl);
     }
   }
-  sp = wave_merge(sp, sl);
-  sq = wave_merge(sq, sl);
+  sp = wave_merge_fast(sp, sl);
+  sq = wave_merge_fast(sq, sl);
   if (lane == 0) {
     L.sm[b][wave][0] = sp;
     L.sm[b][wave][1] = sq;
@@ -281,18 +294,17 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
                                                  const Regs<NV>& R, TeamLds& L, int b) {
   constexpr int VEC = E::kPerVec;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const float sl = kLog2e / u.item.T;
+  const float sl = u.sl;
   const float cp = L.c[b][0], cq = L.c[b][1];
   const bool ok = L.ok[b] != 0;
   float acc = 0.0f;
   if (ok) {
-    const int64_t nvec = slice_vectors<E>(p, u);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
       float a[VEC], c[VEC], e[VEC];
-      E::unpack(masked<E>(R.p[i], v < nvec), a);
-      E::unpack(masked<E>(R.q[i], v < nvec), c);
+      E::unpack(R.p[i], a);
+      E::unpack(R.q[i], c);
 #pragma unroll
       for (int j = 0; j < VEC; ++j)
         e[j] = exp2_fast(fminf(__builtin_fmaf(a[j], sl, -cp), __builtin_fmaf(c[j], sl, -cq)));
@@ -305,8 +317,8 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
     }
     int64_t lo, vhi, hi;
     slice_bounds<E>(p, u.slice, &lo, &vhi, &hi);
-    const auto* prow = row_ptr<E>(p.target, u.item.trow, p.stride);
-    const auto* qrow = row_ptr<E>(p.draft, u.item.drow, p.stride);
+    const auto* prow = row_ptr<E>(p.target, u.trow, p.stride);
+    const auto* qrow = row_ptr<E>(p.draft, u.drow, p.stride);
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads)
       acc += exp2_fast(fminf(__builtin_fmaf(E::load1(prow, i), sl, -cp),
                              __builtin_fmaf(E::load1(qrow, i), sl, -cq)));
@@ -325,7 +337,7 @@ __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const Uni
   if (u.kind == 0) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t slot = unit_slot(p, u);
-  if (u.kind == 2 && u.item.T == 0.0f) {
+  if (u.kind == 3) {
     ArgMax a = (lane < kDataWaves) ? L.am[b][lane] : ArgMax{-INFINITY, INT32_MAX};
     for (int m = 1; m < kWave; m <<= 1) {
       ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
@@ -334,69 +346,83 @@ __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const Uni
     if (lane == 0) p.part_p[slot] = make_float2(a.v, __int_as_float(a.i));
     return;
   }
-  const float sl = kLog2e / u.item.T;
+  const float sl = u.sl;
   SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
   if (lane < kDataWaves) {
     sp = L.sm[b][lane][0];
     sq = L.sm[b][lane][1];
   }
-  sp = wave_merge(sp, sl);
-  sq = wave_merge(sq, sl);
+  sp = wave_merge_fast(sp, sl);
+  sq = wave_merge_fast(sq, sl);
   if (lane == 0) {
     p.part_p[slot] = make_float2(sp.m, sp.z);
     if (u.kind == 1) p.part_q[slot] = make_float2(sq.m, sq.z);
   }
   if (wants_alpha(p, u) && lane < 4) {
     const float v = lane == 0 ? sp.m : lane == 1 ? sp.z : lane == 2 ? sq.m : sq.z;
-    const uint64_t tag = (uint64_t)(uint32_t)(u.pair_ordinal + 1) << 32;
-    const int64_t rec = ((int64_t)team * 4 + (u.pair_ordinal & 3)) * p.team + member;
+    const uint64_t tag = (uint64_t)(uint32_t)(u.ordinal + 1) << 32;
+    const int64_t rec = ((int64_t)team * 4 + (u.ordinal & 3)) * p.team + member;
     __hip_atomic_store(&p.team_xch[rec * 4 + lane], tag | (uint64_t)__float_as_uint(v),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Waits until every member of the team has published row pair u, then
-// combines the members' states into the row log2 normalisers (member 0 also
-// stores the row states in its slots).
+// Loads of one member's exchange record (lane m < T reads member m's record
+// of row pair u).  Issued one window ahead of their use; they stay in flight
+// across the barrier.
+struct TeamPoll {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ TeamPoll team_poll(const VerifyParams& p, const UnitDesc& u,
+                                              int team) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t rec = ((int64_t)team * 4 + (u.ordinal & 3)) * p.team + lane;
+  TeamPoll t;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    t.w[k] = (lane < p.team) ? __hip_atomic_load(&p.team_xch[rec * 4 + k], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : 0ull;
+  return t;
+}
+
+// Completes the team wait for row pair u: the early poll t is checked first,
+// then the records are polled again until every member has published (or
+// the bounded wait expires).  Then the members' states are combined into the
+// row log2 normalisers (member 0 also stores the row states in its slots).
 __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const UnitDesc& u,
-                                               TeamLds& L, int b, int team, int member,
-                                               bool& failed) {
+                                               TeamPoll t, TeamLds& L, int b, int team,
+                                               int member, bool& failed) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nt = p.team;
-  const uint32_t need = (uint32_t)(u.pair_ordinal + 1);
-  const int64_t rec = ((int64_t)team * 4 + (u.pair_ordinal & 3)) * nt + lane;
-  uint64_t w[4] = {0, 0, 0, 0};
-  bool done = false;
-  const uint32_t limit = failed ? 1u : kSpinLimit;
-  for (uint32_t spin = 0; spin < limit; ++spin) {
+  const uint32_t need = (uint32_t)(u.ordinal + 1);
+  auto complete = [&](const TeamPoll& q) {
     bool mine = true;
-    if (lane < nt) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        w[k] = __hip_atomic_load(&p.team_xch[rec * 4 + k], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        mine = mine && (uint32_t)(w[k] >> 32) == need;
-      }
-    }
-    if (__all(mine)) {
-      done = true;
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
+    for (int k = 0; k < 4; ++k) mine = mine && (uint32_t)(q.w[k] >> 32) == need;
+    return __all(lane >= nt || mine) != 0;
+  };
+  bool done = complete(t);
+  const uint32_t limit = failed ? 1u : kSpinLimit;
+  for (uint32_t spin = 0; !done && spin < limit; ++spin) {
+    t = team_poll(p, u, team);
+    done = complete(t);
+    if (!done) __builtin_amdgcn_s_sleep(1);
   }
   if (!done) {
     if (!failed && lane == 0)
       __hip_atomic_store(p.sync_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     failed = true;
   }
-  const float sl = kLog2e / u.item.T;
+  const float sl = u.sl;
   SoftmaxPart a{-INFINITY, 0.0f}, c{-INFINITY, 0.0f};
   if (lane < nt) {
-    a = SoftmaxPart{__uint_as_float((uint32_t)w[0]), __uint_as_float((uint32_t)w[1])};
-    c = SoftmaxPart{__uint_as_float((uint32_t)w[2]), __uint_as_float((uint32_t)w[3])};
+    a = SoftmaxPart{__uint_as_float((uint32_t)t.w[0]), __uint_as_float((uint32_t)t.w[1])};
+    c = SoftmaxPart{__uint_as_float((uint32_t)t.w[2]), __uint_as_float((uint32_t)t.w[3])};
   }
-  a = wave_merge(a, sl);
-  c = wave_merge(c, sl);
+  a = wave_merge_fast(a, sl);
+  c = wave_merge_fast(c, sl);
   if (lane == 0) {
     // Member 0 replaces its slice states with the row states, so that the
     // accept kernel reads one slot per row of a pair.
@@ -437,58 +463,85 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
       n_single_units > blockIdx.x ? (n_single_units - 1 - blockIdx.x) / gridDim.x + 1 : 0;
   const int64_t n = my_pairs + my_singles;
 
-  // Both roles run steps s = 0 .. n with one barrier each, then a last one.
-  // Data step s: loads of unit s + 2, first pass of unit s, barrier, second
-  // pass of unit s - 1.  Communication window s (between barriers s and
-  // s + 1): sum of the second pass of unit s - 2, combination and publication
-  // of the first pass of unit s, team wait for unit s.  The team wait thus
-  // overlaps the data waves' next second and first passes.
+  // Both roles run steps s = 0 .. n + 1 with one barrier each, then a last
+  // one.  Data step s: loads of unit s + 2, first pass of unit s, unit s - 2
+  // taken out of its LDS parking slot and unit s parked there, barrier,
+  // second pass of unit s - 2.  Communication window s (between barriers s
+  // and s + 1): sum of the second pass of unit s - 3, combination and
+  // publication of the first pass of unit s, team wait for unit s - 1 (whose
+  // members published it a step earlier; its records were loaded at the end
+  // of the previous window), then the loads of unit s's records.
+  __shared__ uint4 park[2][2 * NV][kDataThreads];
   if (threadIdx.x < kDataThreads) {
-    const uint4* dummy = reinterpret_cast<const uint4*>(p.plan_counts);
-    Regs<NV> R0, R1, R2, R3;
+    const uint4* dummy = neg_inf_line<E>();
+    Regs<NV> R0, R1, R2;
     UnitDesc U0 = unit_at(p, 0, n, team, member, my_pairs);
     UnitDesc U1 = unit_at(p, 1, n, team, member, my_pairs);
-    UnitDesc U2 = no_unit(), U3 = no_unit();
+    UnitDesc U2 = no_unit();
     UnitDesc un = unit_at(p, 2, n, team, member, my_pairs);
+    UnitDesc up1 = no_unit(), up2 = no_unit();  // units s - 1 and s - 2 (parked)
     load_unit<E, NV>(p, U0, R0, dummy);
     load_unit<E, NV>(p, U1, R1, dummy);
-    // Step s: first pass on buffer s mod 4, second pass on buffer s - 1
-    // mod 4, loads into buffer s + 2 mod 4.
-    auto step = [&](int64_t s, const Regs<NV>& Rf, const UnitDesc& Uf, const Regs<NV>& Rs,
-                    const UnitDesc& Us, Regs<NV>& Rl, UnitDesc& Ul) {
+    // Step s: first pass on buffer s mod 3, loads into buffer s + 2 mod 3;
+    // the parking slot of units s and s - 2 is s mod 2.
+    auto step = [&](int64_t s, const Regs<NV>& Rf, const UnitDesc& Uf, Regs<NV>& Rl,
+                    UnitDesc& Ul) {
       Ul = un;
       load_unit<E, NV>(p, Ul, Rl, dummy);
       un = unit_at(p, s + 3, n, team, member, my_pairs);
       first_pass_data<E, NV>(p, Uf, Rf, L, (int)(s & 1));
+      // Swap unit s - 2 out of its parking slot and unit s in, so that the
+      // buffer of unit s is free before the second pass.
+      const int slot = (int)(s & 1);
+      Regs<NV> Rs;
+      if (wants_alpha(p, up2)) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          Rs.p[i] = park[slot][i][threadIdx.x];
+          Rs.q[i] = park[slot][NV + i][threadIdx.x];
+        }
+      }
+      if (wants_alpha(p, Uf)) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          park[slot][i][threadIdx.x] = Rf.p[i];
+          park[slot][NV + i][threadIdx.x] = Rf.q[i];
+        }
+      }
       lds_barrier();
-      if (wants_alpha(p, Us)) second_pass_data<E, NV>(p, Us, Rs, L, (int)((s - 1) & 1));
+      if (wants_alpha(p, up2)) second_pass_data<E, NV>(p, up2, Rs, L, (int)(s & 1));
+      up2 = up1;
+      up1 = Uf;
     };
-    for (int64_t s = 0;; s += 4) {
-      step(s, R0, U0, R3, U3, R2, U2);
-      if (s + 1 > n) break;
-      step(s + 1, R1, U1, R0, U0, R3, U3);
-      if (s + 2 > n) break;
-      step(s + 2, R2, U2, R1, U1, R0, U0);
-      if (s + 3 > n) break;
-      step(s + 3, R3, U3, R2, U2, R1, U1);
-      if (s + 4 > n) break;
+    for (int64_t s = 0;; s += 3) {
+      step(s, R0, U0, R2, U2);
+      if (s + 1 > n + 1) break;
+      step(s + 1, R1, U1, R0, U0);
+      if (s + 2 > n + 1) break;
+      step(s + 2, R2, U2, R1, U1);
+      if (s + 3 > n + 1) break;
     }
     lds_barrier();
   } else {
     bool failed = false;
-    UnitDesc um2 = no_unit(), um1 = no_unit();
-    for (int64_t s = 0; s <= n; ++s) {
+    UnitDesc um3 = no_unit(), um2 = no_unit(), um1 = no_unit();
+    TeamPoll early{{0ull, 0ull, 0ull, 0ull}};
+    for (int64_t s = 0; s <= n + 1; ++s) {
       const UnitDesc u = unit_at(p, s, n, team, member, my_pairs);
       lds_barrier();
-      if (wants_alpha(p, um2)) second_pass_comm(p, um2, L, (int)(s & 1));
+      if (wants_alpha(p, um3)) second_pass_comm(p, um3, L, (int)((s - 3) & 1));
       first_pass_comm(p, u, L, (int)(s & 1), team, member);
-      if (wants_alpha(p, u)) team_wait_comm(p, u, L, (int)(s & 1), team, member, failed);
+      if (wants_alpha(p, um1))
+        team_wait_comm(p, um1, early, L, (int)((s - 1) & 1), team, member, failed);
+      // early poll of unit s, checked in the next window
+      if (wants_alpha(p, u)) early = team_poll(p, u, team);
+      um3 = um2;
       um2 = um1;
       um1 = u;
     }
     lds_barrier();
-    // um2 is now the last unit, n - 1
-    if (wants_alpha(p, um2)) second_pass_comm(p, um2, L, (int)((n - 1) & 1));
+    // um3 is now unit n - 1
+    if (wants_alpha(p, um3)) second_pass_comm(p, um3, L, (int)((n - 1) & 1));
   }
 }
 
