@@ -12,8 +12,9 @@
 // team has published computes its slice of sum min(p, q) from the same
 // registers.  Nothing is read twice from memory.
 //
-// Each member walks a sequence of units (its team's row pairs, then a share
-// of the single rows: bonus rows at T > 0 and all target rows at T = 0).
+// Each member walks a sequence of units: its team's row pairs, then its
+// team's single rows (bonus rows at T > 0 and all target rows at T = 0),
+// always its own slice of the row.
 //
 // Workgroup layout: waves 0..14 are data waves, wave 15 is the communication
 // wave.  The data waves only load rows and reduce them to per-wave states
@@ -74,9 +75,26 @@ struct UnitDesc {
   uint32_t code;    // request << 7 | position
   float sl;         // log2(e) / T
   int32_t kind;     // 0 none, 1 row pair, 2 single row, 3 single row at T = 0
-  int32_t slice;    // slice index (team member for pairs)
   int32_t ordinal;  // pair ordinal within the team
 };
+
+// The workgroup's slice of every row it works on: elements [lo, hi), of
+// which [lo, vhi) are nvec whole 16-byte vectors.
+struct Slice {
+  int64_t lo, vhi, hi, nvec;
+};
+
+template <typename E>
+__device__ __forceinline__ Slice make_slice(const VerifyParams& p, int member) {
+  constexpr int VEC = E::kPerVec;
+  Slice sc;
+  sc.lo = (int64_t)member * p.team_len;
+  sc.hi = min(p.V, sc.lo + (int64_t)p.team_len);
+  if (sc.hi < sc.lo) sc.hi = sc.lo;
+  sc.nvec = (sc.hi - sc.lo) / VEC;
+  sc.vhi = sc.lo + sc.nvec * VEC;
+  return sc;
+}
 
 // Shared state, double-buffered by unit parity (see the step order above).
 struct TeamLds {
@@ -107,30 +125,27 @@ __device__ __forceinline__ UnitDesc no_unit() {
   u.code = 0u;
   u.sl = 0.0f;
   u.kind = 0;
-  u.slice = 0;
   u.ordinal = 0;
   return u;
 }
 
-// Unit j of this workgroup: its team's row pairs first, then single-row
-// slices dealt round-robin over the whole grid.
+// Unit j of this workgroup: its team's row pairs (items team, team + nteams,
+// ...) and then its team's single rows (dealt the same way); the workgroup
+// always takes slice `member` of the row.
 __device__ __forceinline__ UnitDesc unit_at(const VerifyParams& p, int64_t j, int64_t n,
-                                            int team, int member, int64_t my_pairs) {
+                                            int team, int64_t my_pairs) {
   if (j >= n) return no_unit();
   UnitDesc u;
   if (j < my_pairs) {
     load_item(u, p.plan_pairs, (int64_t)team + (int64_t)p.nteams * j);
     u.kind = 1;
-    u.slice = member;
     u.ordinal = (int32_t)j;
   } else {
-    const int64_t su = (int64_t)blockIdx.x + (int64_t)gridDim.x * (j - my_pairs);
-    const int64_t it = su / p.team;
+    const int64_t it = (int64_t)team + (int64_t)p.nteams * (j - my_pairs);
     load_item(u, p.plan_singles, it);
     const __attribute__((address_space(4))) PlanItem* c =
         (const __attribute__((address_space(4))) PlanItem*)p.plan_singles;
     u.kind = (c[it].T == 0.0f) ? 3 : 2;
-    u.slice = (int)(su % p.team);
     u.ordinal = 0;
   }
   return u;
@@ -140,26 +155,10 @@ __device__ __forceinline__ bool wants_alpha(const VerifyParams& p, const UnitDes
   return u.kind == 1 && p.alpha != nullptr;
 }
 
-__device__ __forceinline__ int64_t unit_slot(const VerifyParams& p, const UnitDesc& u) {
+__device__ __forceinline__ int64_t unit_slot(const VerifyParams& p, const UnitDesc& u,
+                                             int member) {
   const int64_t unit = (int64_t)(u.code >> 7) * (p.D + 1) + (u.code & 127u);
-  return unit * p.S1 + u.slice;
-}
-
-template <typename E>
-__device__ __forceinline__ void slice_bounds(const VerifyParams& p, int slice, int64_t* lo,
-                                             int64_t* vhi, int64_t* hi) {
-  constexpr int VEC = E::kPerVec;
-  *lo = (int64_t)slice * p.team_len;
-  *hi = min(p.V, *lo + (int64_t)p.team_len);
-  if (*hi < *lo) *hi = *lo;
-  *vhi = *lo + ((*hi - *lo) / VEC) * VEC;
-}
-
-template <typename E>
-__device__ __forceinline__ int64_t slice_vectors(const VerifyParams& p, const UnitDesc& u) {
-  int64_t lo, vhi, hi;
-  slice_bounds<E>(p, u.slice, &lo, &vhi, &hi);
-  return u.kind == 0 ? 0 : (vhi - lo) / E::kPerVec;
+  return unit * p.S1 + member;
 }
 
 // A 16-byte line of -inf elements (bf16, fp32): the loads of lanes without
@@ -178,14 +177,13 @@ __device__ __forceinline__ const uint4* neg_inf_line() {
 // row of a single row and every vector of an empty unit read the -inf line
 // instead.
 template <typename E, int NV>
-__device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc& u, Regs<NV>& R,
-                                          const uint4* dummy) {
+__device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc& u,
+                                          const Slice& sc, Regs<NV>& R, const uint4* dummy) {
   using S = typename E::Storage;
   constexpr int VEC = E::kPerVec;
-  const int64_t lo = (int64_t)u.slice * p.team_len;
-  const int64_t nvec = slice_vectors<E>(p, u);
-  const S* prow = row_ptr<E>(p.target, u.trow, p.stride) + lo;
-  const S* qrow = row_ptr<E>(p.draft, u.drow, p.stride) + lo;
+  const int64_t nvec = u.kind == 0 ? 0 : sc.nvec;
+  const S* prow = row_ptr<E>(p.target, u.trow, p.stride) + sc.lo;
+  const S* qrow = row_ptr<E>(p.draft, u.drow, p.stride) + sc.lo;
   const bool pair = u.kind == 1;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -207,12 +205,12 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
 // wave into LDS.
 template <typename E, int NV>
 __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const UnitDesc& u,
-                                                const Regs<NV>& R, TeamLds& L, int b) {
+                                                const Slice& sc, const Regs<NV>& R, TeamLds& L,
+                                                int b) {
   constexpr int VEC = E::kPerVec;
   if (u.kind == 0) return;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  int64_t lo, vhi, hi;
-  slice_bounds<E>(p, u.slice, &lo, &vhi, &hi);
+  const int64_t lo = sc.lo, vhi = sc.vhi, hi = sc.hi;
   const auto* prow = row_ptr<E>(p.target, u.trow, p.stride);
   if (u.kind == 3) {
     // arg max of this thread's vectors: best vector in order, then its first
@@ -221,7 +219,6 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
     int bi = -1;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
       float x[VEC];
       E::unpack(R.p[i], x);
       float cm = x[0];
@@ -256,10 +253,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
   const float sl = u.sl;
   float x[VEC * NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
-    E::unpack(R.p[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
-  }
+  for (int i = 0; i < NV; ++i) E::unpack(R.p[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
   SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
   softmax_group<VEC * NV>(sp, x, sl);
   for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
@@ -268,10 +262,8 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
   }
   if (u.kind == 1) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+    for (int i = 0; i < NV; ++i)
       E::unpack(R.q[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
-    }
     softmax_group<VEC * NV>(sq, x, sl);
     const auto* qrow = row_ptr<E>(p.draft, u.drow, p.stride);
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
@@ -291,7 +283,8 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
 // team's normalisers; one sum per wave into LDS.
 template <typename E, int NV>
 __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const UnitDesc& u,
-                                                 const Regs<NV>& R, TeamLds& L, int b) {
+                                                 const Slice& sc, const Regs<NV>& R, TeamLds& L,
+                                                 int b) {
   constexpr int VEC = E::kPerVec;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const float sl = u.sl;
@@ -301,7 +294,6 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
   if (ok) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
       float a[VEC], c[VEC], e[VEC];
       E::unpack(R.p[i], a);
       E::unpack(R.q[i], c);
@@ -315,11 +307,9 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
       }
       acc += e[0];
     }
-    int64_t lo, vhi, hi;
-    slice_bounds<E>(p, u.slice, &lo, &vhi, &hi);
     const auto* prow = row_ptr<E>(p.target, u.trow, p.stride);
     const auto* qrow = row_ptr<E>(p.draft, u.drow, p.stride);
-    for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads)
+    for (int64_t i = sc.vhi + threadIdx.x; i < sc.hi; i += kDataThreads)
       acc += exp2_fast(fminf(__builtin_fmaf(E::load1(prow, i), sl, -cp),
                              __builtin_fmaf(E::load1(qrow, i), sl, -cq)));
   }
@@ -336,7 +326,7 @@ __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const Uni
                                                 const TeamLds& L, int b, int team, int member) {
   if (u.kind == 0) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t slot = unit_slot(p, u);
+  const int64_t slot = unit_slot(p, u, member);
   if (u.kind == 3) {
     ArgMax a = (lane < kDataWaves) ? L.am[b][lane] : ArgMax{-INFINITY, INT32_MAX};
     for (int m = 1; m < kWave; m <<= 1) {
@@ -427,7 +417,7 @@ __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const Unit
     // Member 0 replaces its slice states with the row states, so that the
     // accept kernel reads one slot per row of a pair.
     if (member == 0) {
-      const int64_t slot = unit_slot(p, u);
+      const int64_t slot = unit_slot(p, u, 0);
       p.part_p[slot] = make_float2(a.m, a.z);
       p.part_q[slot] = make_float2(c.m, c.z);
     }
@@ -440,11 +430,11 @@ __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const Unit
 
 // Sum of the data waves' second-pass sums into the partial slot.
 __device__ __forceinline__ void second_pass_comm(const VerifyParams& p, const UnitDesc& u,
-                                                 const TeamLds& L, int b) {
+                                                 const TeamLds& L, int b, int member) {
   const int lane = threadIdx.x & (kWave - 1);
   float a = (lane < kDataWaves) ? L.acc[b][lane] : 0.0f;
   a = wave_sum(a);
-  if (lane == 0) p.part_a[unit_slot(p, u)] = a;
+  if (lane == 0) p.part_a[unit_slot(p, u, member)] = a;
 }
 
 // ---------------------------------------------------------------------------
@@ -456,12 +446,15 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
   const int team = (int)blockIdx.x / nt;
   const int member = (int)blockIdx.x % nt;
   const int64_t n_pairs = p.plan_counts[0];
-  const int64_t n_single_units = (int64_t)p.plan_counts[1] * nt;
+  const int64_t n_singles = p.plan_counts[1];
+  // workgroups past the last whole team have no work
+  const bool in_team = team < p.nteams;
   const int64_t my_pairs =
-      (team < p.nteams && n_pairs > team) ? (n_pairs - 1 - team) / p.nteams + 1 : 0;
+      (in_team && n_pairs > team) ? (n_pairs - 1 - team) / p.nteams + 1 : 0;
   const int64_t my_singles =
-      n_single_units > blockIdx.x ? (n_single_units - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+      (in_team && n_singles > team) ? (n_singles - 1 - team) / p.nteams + 1 : 0;
   const int64_t n = my_pairs + my_singles;
+  const Slice sc = make_slice<E>(p, member);
 
   // Both roles run steps s = 0 .. n + 1 with one barrier each, then a last
   // one.  Data step s: loads of unit s + 2, first pass of unit s, unit s - 2
@@ -475,21 +468,21 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
   if (threadIdx.x < kDataThreads) {
     const uint4* dummy = neg_inf_line<E>();
     Regs<NV> R0, R1, R2;
-    UnitDesc U0 = unit_at(p, 0, n, team, member, my_pairs);
-    UnitDesc U1 = unit_at(p, 1, n, team, member, my_pairs);
+    UnitDesc U0 = unit_at(p, 0, n, team, my_pairs);
+    UnitDesc U1 = unit_at(p, 1, n, team, my_pairs);
     UnitDesc U2 = no_unit();
-    UnitDesc un = unit_at(p, 2, n, team, member, my_pairs);
+    UnitDesc un = unit_at(p, 2, n, team, my_pairs);
     UnitDesc up1 = no_unit(), up2 = no_unit();  // units s - 1 and s - 2 (parked)
-    load_unit<E, NV>(p, U0, R0, dummy);
-    load_unit<E, NV>(p, U1, R1, dummy);
+    load_unit<E, NV>(p, U0, sc, R0, dummy);
+    load_unit<E, NV>(p, U1, sc, R1, dummy);
     // Step s: first pass on buffer s mod 3, loads into buffer s + 2 mod 3;
     // the parking slot of units s and s - 2 is s mod 2.
     auto step = [&](int64_t s, const Regs<NV>& Rf, const UnitDesc& Uf, Regs<NV>& Rl,
                     UnitDesc& Ul) {
       Ul = un;
-      load_unit<E, NV>(p, Ul, Rl, dummy);
-      un = unit_at(p, s + 3, n, team, member, my_pairs);
-      first_pass_data<E, NV>(p, Uf, Rf, L, (int)(s & 1));
+      load_unit<E, NV>(p, Ul, sc, Rl, dummy);
+      un = unit_at(p, s + 3, n, team, my_pairs);
+      first_pass_data<E, NV>(p, Uf, sc, Rf, L, (int)(s & 1));
       // Swap unit s - 2 out of its parking slot and unit s in, so that the
       // buffer of unit s is free before the second pass.
       const int slot = (int)(s & 1);
@@ -509,7 +502,7 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
         }
       }
       lds_barrier();
-      if (wants_alpha(p, up2)) second_pass_data<E, NV>(p, up2, Rs, L, (int)(s & 1));
+      if (wants_alpha(p, up2)) second_pass_data<E, NV>(p, up2, sc, Rs, L, (int)(s & 1));
       up2 = up1;
       up1 = Uf;
     };
@@ -527,9 +520,9 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     UnitDesc um3 = no_unit(), um2 = no_unit(), um1 = no_unit();
     TeamPoll early{{0ull, 0ull, 0ull, 0ull}};
     for (int64_t s = 0; s <= n + 1; ++s) {
-      const UnitDesc u = unit_at(p, s, n, team, member, my_pairs);
+      const UnitDesc u = unit_at(p, s, n, team, my_pairs);
       lds_barrier();
-      if (wants_alpha(p, um3)) second_pass_comm(p, um3, L, (int)((s - 3) & 1));
+      if (wants_alpha(p, um3)) second_pass_comm(p, um3, L, (int)((s - 3) & 1), member);
       first_pass_comm(p, u, L, (int)(s & 1), team, member);
       if (wants_alpha(p, um1))
         team_wait_comm(p, um1, early, L, (int)((s - 1) & 1), team, member, failed);
@@ -541,13 +534,13 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     }
     lds_barrier();
     // um3 is now unit n - 1
-    if (wants_alpha(p, um3)) second_pass_comm(p, um3, L, (int)((n - 1) & 1));
+    if (wants_alpha(p, um3)) second_pass_comm(p, um3, L, (int)((n - 1) & 1), member);
   }
 }
 
 // Team geometry for a row of V elements: NV <= 2 16-byte vectors per data
-// thread per row (four buffers of two rows stay in registers), T members per
-// row.  Returns false if a row needs more than 64 members (the caller then
+// thread per row (three buffers of two rows stay in registers, two more are
+// parked in LDS), T members per row.  Returns false if a row needs more than 64 members (the caller then
 // uses the streaming row pass).
 bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
                    int32_t* slice_len) {
