@@ -271,8 +271,8 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
       softmax_group<1>(sq, x1, sl);
     }
   }
-  sp = wave_merge_fast(sp, sl);
-  sq = wave_merge_fast(sq, sl);
+  sp = wave_merge_ref(sp, sl);
+  sq = wave_merge_ref(sq, sl);
   if (lane == 0) {
     L.sm[b][wave][0] = sp;
     L.sm[b][wave][1] = sq;
