@@ -63,6 +63,9 @@ typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
 #define SV_FLAG_FORCE_FP64_DRAW 1u /* take every T > 0 draw on the float64 path */
 #define SV_FLAG_STREAMING_ROW_PASS 2u /* use the streaming row pass (two reads of each row
                                          pair) instead of the register-resident team pass */
+#define SV_FLAG_EXACT_FP64_MASSES 4u  /* float64 draws: compute every tile mass directly
+                                         with the float64 normalisers (a second pass over the
+                                         row) instead of from the one-pass decomposition */
 
 /* sv_diag.bits */
 #define SV_BIT_BAD_DEPTH 1u        /* depth[r] outside [0, D_max]                      */

@@ -37,7 +37,8 @@ sv_status validate_verify(const sv_verify_args* a, size_t* need) {
   if (a->B < 0 || a->D_max < 0 || a->D_max > SV_MAX_DEPTH) return SV_ERR_INVALID_ARGUMENT;
   if (a->V < 1 || a->V > INT32_MAX || a->row_stride < a->V) return SV_ERR_INVALID_ARGUMENT;
   if (a->dtype != SV_DTYPE_BF16 && a->dtype != SV_DTYPE_FP32) return SV_ERR_UNSUPPORTED;
-  if (a->flags & ~(SV_FLAG_FORCE_FP64_DRAW | SV_FLAG_STREAMING_ROW_PASS)) return SV_ERR_UNSUPPORTED;
+  if (a->flags & ~(SV_FLAG_FORCE_FP64_DRAW | SV_FLAG_STREAMING_ROW_PASS | SV_FLAG_EXACT_FP64_MASSES))
+    return SV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * (a->D_max + 1) > (int64_t)INT32_MAX / 64) return SV_ERR_INVALID_ARGUMENT;
   if (a->B == 0) {
     *need = 0;
@@ -129,6 +130,10 @@ sv_status sv_verify_batch(const sv_verify_args* a, void* stream) {
   p.seg_zp64 = reinterpret_cast<double*>(ws + L.seg_zp64);
   p.seg_zq64 = reinterpret_cast<double*>(ws + L.seg_zq64);
   p.seg_w64 = reinterpret_cast<double*>(ws + L.seg_w64);
+  p.seg_a64 = reinterpret_cast<double*>(ws + L.seg_a64);
+  p.seg_t64 = reinterpret_cast<double*>(ws + L.seg_t64);
+  p.seg_u32 = reinterpret_cast<int32_t*>(ws + L.seg_u32);
+  p.seg_e64 = reinterpret_cast<double*>(ws + L.seg_e64);
   p.fb_count = reinterpret_cast<int32_t*>(ws + L.fb_count);
   p.fb_list = reinterpret_cast<int32_t*>(ws + L.fb_list);
   p.plan_pairs = reinterpret_cast<sv::PlanItem*>(ws + L.plan_pairs);

@@ -13,9 +13,11 @@
 //                   inside it -> token.  A draw whose float32 CDF margin is
 //                   under 1e-5 (or that rounding leaves undecided) is queued
 //                   for float64.
-//   k_draw_z64      float64 normalisers (tile partials) of queued requests
-//   k_draw_mass64   float64 tile masses of queued requests
-//   k_draw_pick64   the float64 pick
+//   k_draw_tile64   one float64 pass over the rows of queued requests: tile
+//                   normaliser partials and the one-pass split of the tile
+//                   residual masses
+//   k_draw_pick64   float64 tile masses (from the split, or directly where
+//                   it is not certain), then the float64 pick
 // The float64 kernels walk the queue on a fixed grid, so an empty queue costs
 // one short dispatch each.
 #include <hip/hip_runtime.h>
@@ -155,13 +157,15 @@ __device__ __forceinline__ Weights32<E> weights32(const VerifyParams& p, const D
   return w;
 }
 
-// Float64 weights: the temperature is applied by division, the normalisers
+// Float64 weights: the temperature is applied as a multiplication by the
+// float64 reciprocal of T (one extra rounding, about 1e-16 relative, where a
+// division would cost ten float64 operations per element); the normalisers
 // are float64 sums of exp((x - max) / T).
 template <typename E>
 struct Weights64 {
   const typename E::Storage* prow;
   const typename E::Storage* qrow;
-  double T, mp, mq, lnzp, lnzq;
+  double invT, mp, mq, lnzp, lnzq;
   bool unnormalised;  // w = exp((x - mp) / T): residual mass was zero
   __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, double (&w)[kPer]) const {
     float a[kPer];
@@ -169,15 +173,15 @@ struct Weights64 {
     if (unnormalised || !qrow) {
       const double off = unnormalised ? 0.0 : lnzp;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) w[j] = exp(((double)a[j] - mp) / T - off);
+      for (int j = 0; j < kPer; ++j) w[j] = exp(((double)a[j] - mp) * invT - off);
       return;
     }
     float b[kPer];
     load8<E>(qrow, i0, hi, b);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const double pv = exp(((double)a[j] - mp) / T - lnzp);
-      const double qv = exp(((double)b[j] - mq) / T - lnzq);
+      const double pv = exp(((double)a[j] - mp) * invT - lnzp);
+      const double qv = exp(((double)b[j] - mq) * invT - lnzq);
       w[j] = pv > qv ? pv - qv : 0.0;
     }
   }
@@ -372,7 +376,7 @@ __device__ __forceinline__ Weights64<E> weights64(const VerifyParams& p, const D
   w.qrow = (st.mode == kDrawResidual && !unnormalised)
                ? static_cast<const typename E::Storage*>(p.draft) + st.qrow * p.stride
                : nullptr;
-  w.T = st.T;
+  w.invT = 1.0 / (double)st.T;
   w.mp = st.mp;
   w.mq = st.mq;
   w.lnzp = 0.0;
@@ -381,33 +385,119 @@ __device__ __forceinline__ Weights64<E> weights64(const VerifyParams& p, const D
   return w;
 }
 
-// Float64 normaliser partials of one tile: sum exp((x - max) / T).
+// Float64 pass over one tile of a queued draw row: the normaliser partials
+// sum exp((x - max) / T) of p and q, and the one-pass split of the residual
+// mass.  With rho = Zq / Zp, an element's residual weight is
+// max(0, ep rho - eq) / Zq (ep, eq the unnormalised exponentials).  Against
+// the float32 estimate rho_e of rho, d = ep rho_e - eq is computed with one
+// rounding (fma); elements with d > tau ep rho_e are certainly positive,
+// those with d < -tau ep rho_e certainly not, once |rho / rho_e - 1| <= tau / 2
+// holds (checked by the pick).  Over the certain-positive elements the tile
+// keeps D = sum d and A = sum ep, and its residual mass is then
+// (D + (rho - rho_e) A) / Zq, free of cancellation.  Equal logits (a = b,
+// common once both rows are rounded to bfloat16) have eq = kappa ep with one
+// kappa = exp((mp - mq) / T) for the whole row, so they are kept apart as
+// S = sum ep and add S max(0, (Zq - kappa Zp) / (Zp Zq)).  The few other
+// elements in between keep their (ep, eq) (up to kDrawKeep64 per tile, in
+// element order) and the pick adds their exact weights; a tile with more is
+// recomputed directly.
+constexpr double kTau64 = 1e-4;
+
 template <typename E>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_z64(VerifyParams p) {
-  __shared__ double lds[kDrawThreads / kWave];
+__global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
+  __shared__ double lds[kDrawThreads / kWave][5];
+  __shared__ int32_t ldsu[kDrawThreads / kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int64_t items = (int64_t)(*p.fb_count) * p.S2;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int r = p.fb_list[it / p.S2];
     const int64_t tile = it % p.S2;
     const DrawState st = p.req[r];
-    const Weights64<E> w = weights64<E>(p, st, true);
+    const bool residual = st.mode == kDrawResidual;
+    const double invT = 1.0 / (double)st.T;
+    const double rho_e = residual ? exp2((double)st.lzq - (double)st.lzp) : 0.0;
     const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
     const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
-    double e[kPer];
-    w(i0, hi, e);
-    const double zp = block_sum256<double>(sum8(e), lds);
-    double zq = 0.0;
-    if (st.mode == kDrawResidual) {
-      float b[kPer];
+    float a[kPer], b[kPer];
+    load8<E>(static_cast<const typename E::Storage*>(p.target) + st.prow * p.stride, i0, hi, a);
+    if (residual)
       load8<E>(static_cast<const typename E::Storage*>(p.draft) + st.qrow * p.stride, i0, hi, b);
+    double zp = 0.0, zq = 0.0, D = 0.0, A = 0.0, S = 0.0;
+    double kep[kPer], keq[kPer];
+    int32_t U = 0;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) e[j] = exp(((double)b[j] - (double)st.mq) / (double)st.T);
-      zq = block_sum256<double>(sum8(e), lds);
+    for (int j = 0; j < kPer; ++j) {
+      const double ep = exp(((double)a[j] - (double)st.mp) * invT);
+      zp += ep;
+      if (residual) {
+        const double eq = exp(((double)b[j] - (double)st.mq) * invT);
+        zq += eq;
+        const double d = fma(ep, rho_e, -eq);
+        const double tol = kTau64 * ep * rho_e;
+        if (a[j] == b[j]) {
+          S += ep;
+        } else if (d > tol) {
+          D += d;
+          A += ep;
+        } else if (d >= -tol && (ep > 0.0 || eq > 0.0)) {
+          kep[U] = ep;
+          keq[U] = eq;
+          ++U;
+        }
+      }
     }
+    // kept elements: positions by an exclusive scan of the counts in thread
+    // order, so the list is in element order
+    int32_t incl = U;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int32_t o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == kWave - 1) ldsu[wave] = incl;
+    __syncthreads();
+    int32_t base = 0, total = 0;
+    for (int w = 0; w < kDrawThreads / kWave; ++w) {
+      if (w < wave) base += ldsu[w];
+      total += ldsu[w];
+    }
+    base += incl - U;
+    const int64_t o = (int64_t)r * p.S2 + tile;
+    if (total <= kDrawKeep64) {
+      double* keep = p.seg_e64 + o * (kDrawKeep64 * 2);
+      for (int k = 0; k < U; ++k) {
+        keep[2 * (base + k)] = kep[k];
+        keep[2 * (base + k) + 1] = keq[k];
+      }
+    }
+    // block sums in a fixed order
+    for (int m = 1; m < kWave; m <<= 1) {
+      zp += shfl_xor_d(zp, m);
+      zq += shfl_xor_d(zq, m);
+      D += shfl_xor_d(D, m);
+      A += shfl_xor_d(A, m);
+      S += shfl_xor_d(S, m);
+    }
+    __syncthreads();
+    if (lane == 0) {
+      lds[wave][0] = zp;
+      lds[wave][1] = zq;
+      lds[wave][2] = D;
+      lds[wave][3] = A;
+      lds[wave][4] = S;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-      p.seg_zp64[(int64_t)r * p.S2 + tile] = zp;
-      p.seg_zq64[(int64_t)r * p.S2 + tile] = zq;
+      double t[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+      for (int w = 0; w < kDrawThreads / kWave; ++w)
+        for (int k = 0; k < 5; ++k) t[k] += lds[w][k];
+      p.seg_zp64[o] = t[0];
+      p.seg_zq64[o] = t[1];
+      p.seg_w64[o] = t[2];
+      p.seg_a64[o] = t[3];
+      p.seg_t64[o] = t[4];
+      p.seg_u32[o] = total;
     }
+    __syncthreads();
   }
 }
 
@@ -419,45 +509,60 @@ __device__ __forceinline__ double merge_z64(const double* parts, int64_t S2, dou
 }
 
 template <typename E>
-__device__ __forceinline__ Weights64<E> full_weights64(const VerifyParams& p, const DrawState& st,
-                                                       int r, bool unnormalised, double* lds) {
-  Weights64<E> w = weights64<E>(p, st, unnormalised);
-  const double zp = merge_z64(p.seg_zp64 + (int64_t)r * p.S2, p.S2, lds);
-  w.lnzp = log(zp);
-  if (st.mode == kDrawResidual) {
-    const double zq = merge_z64(p.seg_zq64 + (int64_t)r * p.S2, p.S2, lds);
-    w.lnzq = log(zq);
-  }
-  return w;
-}
-
-template <typename E>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_mass64(VerifyParams p) {
-  __shared__ double lds[kDrawThreads / kWave];
-  const int64_t items = (int64_t)(*p.fb_count) * p.S2;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int r = p.fb_list[it / p.S2];
-    const int64_t tile = it % p.S2;
-    const DrawState st = p.req[r];
-    const Weights64<E> w = full_weights64<E>(p, st, r, false, lds);
-    const double m = tile_mass<double>(w, tile, p.V, lds);
-    if (threadIdx.x == 0) p.seg_w64[(int64_t)r * p.S2 + tile] = m;
-  }
-}
-
-template <typename E>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   __shared__ PickLds<double> L;
   __shared__ double lds[kDrawThreads / kWave];
+  __shared__ int s_redo[kDrawThreads];
   const int r = blockIdx.x;
   const DrawState st = p.req[r];
   if (st.mode == kDrawNone || !st.need64) return;
+  const bool residual = st.mode == kDrawResidual;
+  double* masses = p.seg_w64 + (int64_t)r * p.S2;
+  const double Zp = merge_z64(p.seg_zp64 + (int64_t)r * p.S2, p.S2, lds);
+  const double Zq = residual ? merge_z64(p.seg_zq64 + (int64_t)r * p.S2, p.S2, lds) : 1.0;
+  Weights64<E> w = weights64<E>(p, st, false);
+  w.lnzp = log(Zp);
+  w.lnzq = log(Zq);
+  // Tile masses: from the one-pass split where it is certain, else directly.
+  const double rho = Zq / Zp;
+  const double rho_e = residual ? exp2((double)st.lzq - (double)st.lzp) : 0.0;
+  const bool split_ok = residual && (p.flags & SV_FLAG_EXACT_FP64_MASSES) == 0u &&
+                        fabs(rho / rho_e - 1.0) <= 0.5 * kTau64;
+  // residual weight per unit of ep of an equal-logit pair
+  const double kappa = exp(((double)st.mp - (double)st.mq) * w.invT);
+  const double g_tie = fmax(0.0, (Zq - kappa * Zp) / (Zp * Zq));
+  for (int64_t base = 0; base < p.S2; base += kDrawThreads) {
+    const int64_t t = base + threadIdx.x;
+    int redo = 0;
+    if (t < p.S2) {
+      const int64_t o = (int64_t)r * p.S2 + t;
+      if (!residual) {
+        masses[t] = p.seg_zp64[o] / Zp;
+      } else if (split_ok && p.seg_u32[o] <= kDrawKeep64) {
+        double m = (masses[t] + (rho - rho_e) * p.seg_a64[o]) / Zq + p.seg_t64[o] * g_tie;
+        const double* keep = p.seg_e64 + o * (kDrawKeep64 * 2);
+        for (int k = 0; k < p.seg_u32[o]; ++k)
+          m += fmax(0.0, keep[2 * k] / Zp - keep[2 * k + 1] / Zq);
+        masses[t] = m;
+      } else {
+        redo = 1;
+      }
+    }
+    s_redo[threadIdx.x] = redo;
+    __syncthreads();
+    for (int k = 0; k < kDrawThreads && base + k < p.S2; ++k) {
+      if (!s_redo[k]) continue;  // uniform: every thread reads the same flag
+      const double m = tile_mass<double>(w, base + k, p.V, lds);
+      if (threadIdx.x == 0) masses[base + k] = m;
+    }
+    __syncthreads();
+  }
   // Residual mass (float64): the sum of the tile masses, same order as pick.
   double R = 0.0;
   {
     double carry = 0.0;
     for (int64_t base = 0; base < p.S2; base += kDrawThreads) {
-      const double m = (base + threadIdx.x < p.S2) ? p.seg_w64[(int64_t)r * p.S2 + base + threadIdx.x] : 0.0;
+      const double m = (base + threadIdx.x < p.S2) ? masses[base + threadIdx.x] : 0.0;
       double tot;
       scan256<double>(m, lds, &tot);
       carry = carry + tot;
@@ -467,24 +572,23 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   const bool unnorm = !(R > 0.0);
   PickResult res;
   if (!unnorm) {
-    const Weights64<E> w = full_weights64<E>(p, st, r, false, lds);
-    res = pick<double>(p.seg_w64 + (int64_t)r * p.S2, p.S2, p.V, (double)st.u, w, L);
+    res = pick<double>(masses, p.S2, p.V, (double)st.u, w, L);
   } else {
     // p = q to float64 precision: draw from p (unnormalised tile partials).
-    const Weights64<E> w = weights64<E>(p, st, true);
-    res = pick<double>(p.seg_zp64 + (int64_t)r * p.S2, p.S2, p.V, (double)st.u, w, L);
+    const Weights64<E> wu = weights64<E>(p, st, true);
+    res = pick<double>(p.seg_zp64 + (int64_t)r * p.S2, p.S2, p.V, (double)st.u, wu, L);
   }
   if (!res.found) {
     // t rounded to or past the total: the last token of non-zero weight.
     __shared__ unsigned long long s_last1;
     if (threadIdx.x == 0) s_last1 = 0ull;
     __syncthreads();
-    const Weights64<E> w = unnorm ? weights64<E>(p, st, true) : full_weights64<E>(p, st, r, false, lds);
+    const Weights64<E> wl = unnorm ? weights64<E>(p, st, true) : w;
     for (int64_t tile = 0; tile < p.S2; ++tile) {
       const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
       const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
       double e[kPer];
-      w(i0, hi, e);
+      wl(i0, hi, e);
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
         if (e[j] > 0.0) atomicMax(&s_last1, (unsigned long long)(i0 + j + 1));
@@ -507,8 +611,7 @@ static void launch_draw_t(const VerifyParams& p, hipStream_t stream) {
   const unsigned gx = (unsigned)(p.S2 < 1024 ? p.S2 : 1024);
   hipLaunchKernelGGL(k_draw_mass32<E>, dim3(gx, (unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
   hipLaunchKernelGGL(k_draw_pick32<E>, dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
-  hipLaunchKernelGGL(k_draw_z64<E>, dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
-  hipLaunchKernelGGL(k_draw_mass64<E>, dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL(k_draw_tile64<E>, dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
   hipLaunchKernelGGL(k_draw_pick64<E>, dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
 }
 

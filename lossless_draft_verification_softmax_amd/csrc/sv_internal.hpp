@@ -14,6 +14,9 @@ enum DrawMode : int32_t { kDrawNone = 0, kDrawResidual = 1, kDrawBonus = 2 };
 
 // Elements per draw tile (256 threads x 8).
 constexpr int kDrawTile = 2048;
+// float64 draw: uncertain-sign elements kept per tile (more: the tile is
+// recomputed directly)
+constexpr int kDrawKeep64 = 16;
 // Largest grid of the team row pass, and most members per row.
 constexpr int kMaxTeamGrid = 1024;
 constexpr int kMaxTeam = 64;
@@ -83,7 +86,11 @@ struct VerifyParams {
   float* seg_w32;    // [B][S2]
   double* seg_zp64;  // [B][S2]
   double* seg_zq64;  // [B][S2]
-  double* seg_w64;   // [B][S2]
+  double* seg_w64;   // [B][S2]  float64 tile masses (first the sums D of the one-pass split)
+  double* seg_a64;   // [B][S2]  float64 sums A of the one-pass split
+  double* seg_t64;   // [B][S2]  float64 sums of ep over equal logit pairs
+  int32_t* seg_u32;  // [B][S2]  elements of a tile whose residual sign was not certain
+  double* seg_e64;   // [B][S2][kDrawKeep64][2]  their (ep, eq), in element order
   int32_t* fb_count; // requests queued for the float64 draw
   int32_t* fb_list;  // [B]
   PlanItem* plan_pairs;    // [B * D]        row pairs at T > 0
@@ -121,7 +128,8 @@ inline void draw_geometry(int64_t V, int32_t* S2, int32_t* seg2) {
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WorkspaceLayout {
-  size_t part_p, part_q, part_a, req, seg_w32, seg_zp64, seg_zq64, seg_w64, fb_count, fb_list,
+  size_t part_p, part_q, part_a, req, seg_w32, seg_zp64, seg_zq64, seg_w64, seg_a64, seg_t64, seg_u32, seg_e64,
+      fb_count, fb_list,
       plan_pairs, plan_singles, plan_counts, team_xch, sync_error, total;
   int32_t slots;
 };
@@ -143,6 +151,10 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
   L.seg_zp64 = off; off += align256((size_t)B * S2 * sizeof(double));
   L.seg_zq64 = off; off += align256((size_t)B * S2 * sizeof(double));
   L.seg_w64 = off; off += align256((size_t)B * S2 * sizeof(double));
+  L.seg_a64 = off; off += align256((size_t)B * S2 * sizeof(double));
+  L.seg_t64 = off; off += align256((size_t)B * S2 * sizeof(double));
+  L.seg_u32 = off; off += align256((size_t)B * S2 * sizeof(int32_t));
+  L.seg_e64 = off; off += align256((size_t)B * S2 * kDrawKeep64 * 2 * sizeof(double));
   L.fb_count = off; off += align256(sizeof(int32_t));
   L.fb_list = off; off += align256((size_t)B * sizeof(int32_t));
   L.plan_pairs = off; off += align256((size_t)B * (size_t)D * sizeof(PlanItem));

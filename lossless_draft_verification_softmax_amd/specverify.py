@@ -28,6 +28,7 @@ SV_MAX_DEPTH = 64
 SV_MAX_BUDGET_POSITIONS = 4096
 SV_FLAG_FORCE_FP64_DRAW = 1
 SV_FLAG_STREAMING_ROW_PASS = 2
+SV_FLAG_EXACT_FP64_MASSES = 4
 SV_NUM_STAGE_EVENTS = 5
 
 BIT_BAD_DEPTH = 1

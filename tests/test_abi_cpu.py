@@ -85,7 +85,7 @@ def test_verify_validation_codes(sv):
     assert call(sv, _args(sv, V=0)) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(sv, _args(sv, row_stride=32)) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(sv, _args(sv, dtype=7)) == sv.SV_ERR_UNSUPPORTED
-    assert call(sv, _args(sv, flags=4)) == sv.SV_ERR_UNSUPPORTED
+    assert call(sv, _args(sv, flags=8)) == sv.SV_ERR_UNSUPPORTED
     assert call(sv, _args(sv, target_logits=None)) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(sv, _args(sv, draft_row0=None)) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(sv, _args(sv, target_logits=(1 << 20) + 2)) == sv.SV_ERR_UNSUPPORTED

@@ -59,6 +59,22 @@ def test_c2_forced_fp64_draws():
     assert rep[0]["fp64_draws"] == rep[0]["requests"]
 
 
+def test_c2_forced_fp64_draws_exact_masses():
+    """Every float64 tile mass computed directly instead of from the one-pass
+    split; the draws must match the oracle the same way."""
+    rep = full_depth_case("c2", seeds=(0, 1),
+                          flags=sv.SV_FLAG_FORCE_FP64_DRAW | sv.SV_FLAG_EXACT_FP64_MASSES)
+    assert all(r["fp64_draws"] == r["requests"] for r in rep)
+
+
+def test_c4full_forced_fp64_draws_sampled():
+    """Float64 draws on full 151936-entry rows (75 tiles), split against direct."""
+    a = budget_case("c4full", sample=[0, 17, 45, 63], flags=sv.SV_FLAG_FORCE_FP64_DRAW)[1]
+    b = budget_case("c4full", sample=[0, 17, 45, 63],
+                    flags=sv.SV_FLAG_FORCE_FP64_DRAW | sv.SV_FLAG_EXACT_FP64_MASSES)[1]
+    assert np.array_equal(a["out_tokens"], b["out_tokens"])
+
+
 def test_c3_block_t0_full():
     full_depth_case("c3_t0")
 
