@@ -60,8 +60,9 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, in
   __shared__ int32_t hist[256];
   __shared__ float red[kBudgetWaves];
   __shared__ int32_t wtot[kBudgetWaves];
-  __shared__ int32_t s_valid, s_need;
+  __shared__ int32_t s_valid, s_need, s_whole;
   __shared__ uint64_t s_prefix;
+  __shared__ uint64_t s_min[kBudgetWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int N = B * D;
@@ -110,10 +111,13 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, in
 
   // Radix select of the Keff-th largest key.  After digit round d, s_prefix
   // holds its top 8 (d + 1) bits and s_need its rank among the keys that
-  // share them.
+  // share them.  When every key sharing the prefix is kept (s_need equals
+  // their count), the threshold is the smallest of them and the remaining
+  // rounds are skipped.
   if (tid == 0) {
     s_prefix = 0ull;
     s_need = Keff;
+    s_whole = 0;
   }
   uint64_t thr = ~0ull;  // nothing kept when Keff == 0
   if (Keff > 0) {
@@ -145,12 +149,35 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, in
             if (run < need && need <= run + h[j]) {
               s_prefix = prefix | ((uint64_t)(255 - 4 * lane - j) << shift);
               s_need = need - run;
+              s_whole = (need - run == h[j]) ? 1 : 0;
             }
             run += h[j];
           }
         }
       }
       __syncthreads();
+      if (s_whole && d < 7) {
+        // smallest key among those sharing the selected top 8 (d + 1) bits
+        const uint64_t pre = s_prefix;
+        uint64_t mn = ~0ull;
+#pragma unroll
+        for (int j = 0; j < kKeySlots; ++j)
+          if (j * kBudgetThreads + tid < N && (key[j] >> shift) == (pre >> shift) && key[j] < mn)
+            mn = key[j];
+        for (int m = 1; m < kWave; m <<= 1) {
+          const uint32_t lo32 = __shfl_xor((uint32_t)(mn & 0xffffffffull), m);
+          const uint32_t hi32 = __shfl_xor((uint32_t)(mn >> 32), m);
+          const uint64_t o = ((uint64_t)hi32 << 32) | lo32;
+          mn = o < mn ? o : mn;
+        }
+        if (lane == 0) s_min[wave] = mn;
+        __syncthreads();
+        uint64_t t = s_min[0];
+        for (int w2 = 1; w2 < kBudgetWaves; ++w2) t = s_min[w2] < t ? s_min[w2] : t;
+        s_prefix = t;  // every thread writes the same value
+        __syncthreads();
+        break;
+      }
     }
     thr = s_prefix;
   }
