@@ -159,20 +159,20 @@ __device__ __forceinline__ SoftmaxPart wave_merge_fast(SoftmaxPart p, float sl) 
   return {m, z};
 }
 
-// Wave merge against lane 0's maximum instead of the wave maximum: the sum
-// is rescaled to 2^(m_0 sl), which needs no max reduction.  When some lane's
-// maximum exceeds m_0 by more than 64 / sl (scale factors above 2^64), or a
-// maximum is NaN or infinite, or lane 0 is empty, the exact merge is taken
-// instead.  The result (m, z) is a valid state either way: its value is
-// z 2^(m sl) whether or not m is the largest element.
+// Wave merge against lane 0's maximum instead of the wave maximum: each sum
+// is rescaled to 2^(m_0 sl), which needs no max reduction.  The result
+// (m_0, z) is a valid state whether or not m_0 is the largest element: its
+// value is z 2^(m_0 sl).  A rescaled sum above 2^100 (or NaN), a non-finite
+// m_0 or an empty lane 0 takes the exact merge instead.  So every element x
+// under a merged state satisfies (x - m) sl <= 106, through any number of
+// such merges, and sums stay far from float32 overflow.
 __device__ __forceinline__ SoftmaxPart wave_merge_ref(SoftmaxPart p, float sl) {
   const float m0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.m)));
-  const float d = (p.m - m0) * sl;
   const bool empty = p.m == -INFINITY;
-  if (__ballot(!empty && !(d <= 64.0f)) != 0ull || !(fabsf(m0) < INFINITY))
+  const float zs = empty ? 0.0f : p.z * exp2_fast((p.m - m0) * sl);
+  if (__ballot(!(zs <= 0x1p100f)) != 0ull || !(fabsf(m0) < INFINITY))
     return wave_merge_fast(p, sl);
-  const float z = empty ? 0.0f : p.z * exp2_fast(d);
-  return {m0, wave_sum(z)};
+  return {m0, wave_sum(zs)};
 }
 
 // ---------------------------------------------------------------------------

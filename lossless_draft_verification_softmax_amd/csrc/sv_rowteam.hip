@@ -342,8 +342,8 @@ __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const Uni
     sp = L.sm[b][lane][0];
     sq = L.sm[b][lane][1];
   }
-  sp = wave_merge_fast(sp, sl);
-  sq = wave_merge_fast(sq, sl);
+  sp = wave_merge_ref(sp, sl);
+  sq = wave_merge_ref(sq, sl);
   if (lane == 0) {
     p.part_p[slot] = make_float2(sp.m, sp.z);
     if (u.kind == 1) p.part_q[slot] = make_float2(sq.m, sq.z);
@@ -411,8 +411,8 @@ __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const Unit
     a = SoftmaxPart{__uint_as_float((uint32_t)t.w[0]), __uint_as_float((uint32_t)t.w[1])};
     c = SoftmaxPart{__uint_as_float((uint32_t)t.w[2]), __uint_as_float((uint32_t)t.w[3])};
   }
-  a = wave_merge_fast(a, sl);
-  c = wave_merge_fast(c, sl);
+  a = wave_merge_ref(a, sl);
+  c = wave_merge_ref(c, sl);
   if (lane == 0) {
     // Member 0 replaces its slice states with the row states, so that the
     // accept kernel reads one slot per row of a pair.

@@ -240,3 +240,43 @@ def test_accept_stats_match_oracle():
         assert np.allclose(g["per_depth"].cpu().numpy().reshape(3, D), o["per_depth"], rtol=1e-5,
                            atol=1e-6)
         assert np.allclose(g["summary"].cpu().numpy(), o["summary"], rtol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("row_pass", ["team", "stream"])
+def test_extreme_logit_ranges(dtype, row_pass):
+    """Rows whose logits span hundreds of units at full vocabulary: spikes of
+    +150..+300 placed in different slices of a row, one slice far below the
+    rest, and temperatures 0.3 and 1.  Partial states of such rows differ by
+    far more than the float32 range, so every merge (in the row pass and in
+    the accept kernel) has to rescale against the true maximum."""
+    rng = np.random.default_rng(4242)
+    B, D, V = 4, 3, 151936
+    temps = np.array([0.3, 1.0, 0.3, 1.0], np.float32)
+    P, Q, tokens = random_batch(rng, B, D, V, V, dtype, temps, scale=3.0, noise=1.0)
+    for i in range(P.shape[0]):
+        j = int(rng.integers(0, V))
+        P[i, j] += float(rng.uniform(150.0, 300.0))
+        lo = int(rng.integers(0, V - 20000))
+        P[i, lo:lo + 20000] -= 200.0
+    for i in range(Q.shape[0]):
+        j = int(rng.integers(0, V))
+        Q[i, j] += float(rng.uniform(150.0, 300.0))
+    # drafts that sometimes hit the spikes
+    for r in range(B):
+        for k in range(D):
+            if rng.random() < 0.5:
+                tokens[r, k] = int(np.argmax(Q[r * D + k]))
+    Pd, Qd = to_dev(P, dtype), to_dev(Q, dtype)
+    depth = np.full(B, D, np.int32)
+    tr0, dr0 = padded_offsets(B, D, DEV)
+    g = gpu_verify(Pd, Qd, tr0, dr0, torch.from_numpy(tokens).to(DEV),
+                   torch.from_numpy(depth).to(DEV), torch.from_numpy(temps).to(DEV), seed=9,
+                   flags=sv.SV_FLAG_STREAMING_ROW_PASS if row_pass == "stream" else 0)
+    Ph = Pd.float().cpu().numpy()
+    Qh = Qd.float().cpu().numpy()
+    o = oracle_verify(Ph, Qh, tr0.cpu().numpy(), dr0.cpu().numpy(), tokens, depth, temps,
+                      np.arange(B), seed=9)
+    rep = compare(g, o, np.arange(B), temps, depth)
+    assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"]
+    assert np.all(g["bits"] & sv.BIT_SYNC_TIMEOUT == 0)
