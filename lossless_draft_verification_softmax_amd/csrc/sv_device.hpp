@@ -175,6 +175,48 @@ __device__ __forceinline__ SoftmaxPart wave_merge_ref(SoftmaxPart p, float sl) {
   return {m0, wave_sum(zs)};
 }
 
+// Three wave sums over the same fixed tree, interleaved so that their
+// dependent chains overlap.
+__device__ __forceinline__ void wave_sum3(float& a, float& b, float& c) {
+  auto step = [&](auto f) {
+    a = a + f(a);
+    b = b + f(b);
+    c = c + f(c);
+  };
+  step([](float v) { return dpp_f<kDppQuadXor1>(v); });
+  step([](float v) { return dpp_f<kDppQuadXor2>(v); });
+  step([](float v) { return dpp_f<kDppHalfMirror>(v); });
+  step([](float v) { return dpp_f<kDppMirror>(v); });
+  auto plus = [](float x, float y) { return x + y; };
+  a = combine_rows16(a, plus);
+  b = combine_rows16(b, plus);
+  c = combine_rows16(c, plus);
+  a = combine_halves32(a, plus);
+  b = combine_halves32(b, plus);
+  c = combine_halves32(c, plus);
+}
+
+// wave_merge_ref on two states (q may be absent) and a plain wave sum, with
+// one fallback branch for both states: three independent reduction chains.
+__device__ __forceinline__ void wave_merge_ref2(SoftmaxPart& p, SoftmaxPart& q, bool has_q,
+                                                float& sum, float sl) {
+  const float m0p = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.m)));
+  const float m0q = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(q.m)));
+  float zp = (p.m == -INFINITY) ? 0.0f : p.z * exp2_fast((p.m - m0p) * sl);
+  float zq = (!has_q || q.m == -INFINITY) ? 0.0f : q.z * exp2_fast((q.m - m0q) * sl);
+  const bool bad_lane = !(zp <= 0x1p100f) || !(zq <= 0x1p100f);
+  if (__ballot(bad_lane) != 0ull || !(fabsf(m0p) < INFINITY) ||
+      (has_q && !(fabsf(m0q) < INFINITY))) {
+    p = wave_merge_fast(p, sl);
+    if (has_q) q = wave_merge_fast(q, sl);
+    sum = wave_sum(sum);
+    return;
+  }
+  wave_sum3(zp, zq, sum);
+  p = {m0p, zp};
+  if (has_q) q = {m0q, zq};
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies whose high words are xored with the other two counter

@@ -323,9 +323,20 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
 // Combines the data waves' first-pass states of a unit (a fixed reduction
 // tree over the lanes), writes the partial slots and publishes a pair.
 __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const UnitDesc& u,
-                                                const TeamLds& L, int b, int team, int member) {
-  if (u.kind == 0) return;
+                                                const TeamLds& L, int b, int team, int member,
+                                                const UnitDesc& ua, int ba) {
   const int lane = threadIdx.x & (kWave - 1);
+  // the second-pass sums of unit ua are reduced alongside (same tree as
+  // a lone wave sum)
+  const bool fin = wants_alpha(p, ua);
+  float acc = (fin && lane < kDataWaves) ? L.acc[ba][lane] : 0.0f;
+  if (u.kind == 0 || u.kind == 3) {
+    if (fin) {
+      acc = wave_sum(acc);
+      if (lane == 0) p.part_a[unit_slot(p, ua, member)] = acc;
+    }
+    if (u.kind == 0) return;
+  }
   const int64_t slot = unit_slot(p, u, member);
   if (u.kind == 3) {
     ArgMax a = (lane < kDataWaves) ? L.am[b][lane] : ArgMax{-INFINITY, INT32_MAX};
@@ -342,11 +353,11 @@ __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const Uni
     sp = L.sm[b][lane][0];
     sq = L.sm[b][lane][1];
   }
-  sp = wave_merge_ref(sp, sl);
-  sq = wave_merge_ref(sq, sl);
+  wave_merge_ref2(sp, sq, u.kind == 1, acc, sl);
   if (lane == 0) {
     p.part_p[slot] = make_float2(sp.m, sp.z);
     if (u.kind == 1) p.part_q[slot] = make_float2(sq.m, sq.z);
+    if (fin) p.part_a[unit_slot(p, ua, member)] = acc;
   }
   if (wants_alpha(p, u) && lane < 4) {
     const float v = lane == 0 ? sp.m : lane == 1 ? sp.z : lane == 2 ? sq.m : sq.z;
@@ -411,8 +422,8 @@ __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const Unit
     a = SoftmaxPart{__uint_as_float((uint32_t)t.w[0]), __uint_as_float((uint32_t)t.w[1])};
     c = SoftmaxPart{__uint_as_float((uint32_t)t.w[2]), __uint_as_float((uint32_t)t.w[3])};
   }
-  a = wave_merge_ref(a, sl);
-  c = wave_merge_ref(c, sl);
+  float none = 0.0f;
+  wave_merge_ref2(a, c, true, none, sl);
   if (lane == 0) {
     // Member 0 replaces its slice states with the row states, so that the
     // accept kernel reads one slot per row of a pair.
@@ -522,8 +533,7 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     for (int64_t s = 0; s <= n + 1; ++s) {
       const UnitDesc u = unit_at(p, s, n, team, my_pairs);
       lds_barrier();
-      if (wants_alpha(p, um3)) second_pass_comm(p, um3, L, (int)((s - 3) & 1), member);
-      first_pass_comm(p, u, L, (int)(s & 1), team, member);
+      first_pass_comm(p, u, L, (int)(s & 1), team, member, um3, (int)((s - 3) & 1));
       if (wants_alpha(p, um1))
         team_wait_comm(p, um1, early, L, (int)((s - 1) & 1), team, member, failed);
       // early poll of unit s, checked in the next window
