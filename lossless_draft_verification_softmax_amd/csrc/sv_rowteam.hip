@@ -527,12 +527,44 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     }
     lds_barrier();
   } else {
+    // The communication wave's short dependent chains gate every step; it
+    // issues ahead of the data waves that share its SIMD.
+    __builtin_amdgcn_s_setprio(3);
+    const int lane = threadIdx.x & (kWave - 1);
+    // Work items of units base .. base + 63, one per lane (code, T, log2(e)/T),
+    // loaded with one vector load per lane for 64 steps: a scalar load per
+    // step would be waited for at every barrier.
+    uint4 blk = make_uint4(0u, 0u, 0u, 0u);
+    auto load_block = [&](int64_t base) {
+      const int64_t j = base + lane;
+      blk = make_uint4(0u, 0u, 0u, 0u);
+      if (j < n) {
+        const PlanItem* it = (j < my_pairs)
+                                 ? p.plan_pairs + ((int64_t)team + (int64_t)p.nteams * j)
+                                 : p.plan_singles + ((int64_t)team + (int64_t)p.nteams * (j - my_pairs));
+        blk = *reinterpret_cast<const uint4*>(&it->code);
+      }
+    };
+    auto comm_unit = [&](int64_t s) {
+      if (s >= n) return no_unit();
+      const int l = (int)(s & 63);
+      UnitDesc u;
+      u.trow = 0;
+      u.drow = 0;
+      u.code = (uint32_t)__builtin_amdgcn_readlane((int)blk.x, l);
+      const float T = __int_as_float(__builtin_amdgcn_readlane((int)blk.y, l));
+      u.sl = __int_as_float(__builtin_amdgcn_readlane((int)blk.z, l));
+      u.kind = (s < my_pairs) ? 1 : (T == 0.0f ? 3 : 2);
+      u.ordinal = (s < my_pairs) ? (int32_t)s : 0;
+      return u;
+    };
     bool failed = false;
     UnitDesc um3 = no_unit(), um2 = no_unit(), um1 = no_unit();
     TeamPoll early{{0ull, 0ull, 0ull, 0ull}};
     for (int64_t s = 0; s <= n + 1; ++s) {
-      const UnitDesc u = unit_at(p, s, n, team, my_pairs);
       lds_barrier();
+      if ((s & 63) == 0) load_block(s);
+      const UnitDesc u = comm_unit(s);
       first_pass_comm(p, u, L, (int)(s & 1), team, member, um3, (int)((s - 3) & 1));
       if (wants_alpha(p, um1))
         team_wait_comm(p, um1, early, L, (int)((s - 1) & 1), team, member, failed);
