@@ -28,19 +28,22 @@
 // -inf), which lets the compiler wait on the oldest unit only.
 //
 // Software pipeline, step s: the data waves issue the loads of unit s + 2,
-// take the first pass of unit s and then the second pass of unit s - 2,
-// whose slice they parked in LDS two steps earlier (two slots of
-// 2 * NV * 16 bytes per data thread; each thread reads back only what it
-// wrote) and whose team normalisers the communication wave gathered in the
-// previous step.  Three register buffers rotate (unit s and two units in
-// flight), and a member's wait for its team has a whole step of slack.
+// take the first pass of unit s and then the second pass of unit s - 1.  The
+// first pass of a row pair keeps its exponentials 2^((x - m_t) sl) (m_t the
+// thread's maximum over its vectors) and parks them in LDS (one slot of
+// 2 * NV * VEC float32 values per data thread, VEC elements per 16-byte
+// vector; each thread reads back only what it wrote), so the second pass
+// sums min(ep Kp, eq Kq) with one Kp = 2^(m_t sl - c_p) per thread and row
+// instead of an exponential per element.  The communication wave gathers the
+// team normalisers of unit s in the same step.  Three register buffers
+// rotate (unit s and two units in flight).
 //
 // Team exchange: member m publishes its slice states of its n-th row pair as
 // four 64-bit words (value bits | (n + 1) << 32) in ring slot n mod 4; a
 // reader accepts a word only if its tag is n + 1, so no fences are needed.
-// A member publishes n only after it has read every member's n - 2, and a
-// member publishes n - 2 only after it has read every member's n - 3, so a
-// ring slot is never overwritten before all its readers are done.  The words
+// A member publishes n only after it has read every member's n - 1, which
+// every member published only after reading all of n - 2, so by then every
+// reader is done with n - 4, the previous user of the ring slot.  The words
 // are cleared before each launch.  The wait is bounded; on expiry the kernel
 // sets an error word that the accept kernel turns into SV_BIT_SYNC_TIMEOUT
 // on every request, and the member stops waiting.
@@ -200,16 +203,50 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
 // ---------------------------------------------------------------------------
 // Data waves.
 
+// (max, sum) of N values with their exponentials kept: e[i] = 2^(x[i] sl -
+// msl), msl = m sl (m = 0 if every value is -inf), summed in the order of
+// softmax_group from an empty state.
+template <int N>
+__device__ __forceinline__ SoftmaxPart softmax_keep(const float (&x)[N], float sl, float (&e)[N],
+                                                    float& msl) {
+  float cm = x[0];
+#pragma unroll
+  for (int i = 1; i + 1 < N; i += 2) cm = vmax3(cm, x[i], x[i + 1]);
+  if constexpr ((N % 2) == 0) cm = vmax(cm, x[N - 1]);
+  const float ms = (cm == -INFINITY) ? 0.0f : cm;
+  msl = ms * sl;
+#pragma unroll
+  for (int i = 0; i < N; ++i) e[i] = exp2_fast(__builtin_fmaf(x[i], sl, -msl));
+  constexpr int C = N < 8 ? N : 8;
+  static_assert(N % C == 0, "group size must be a multiple of the chunk");
+  float acc = 0.0f;
+#pragma unroll
+  for (int c = 0; c < N; c += C) {
+    float t[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) t[i] = e[c + i];
+#pragma unroll
+    for (int w = 1; w < C; w <<= 1) {
+#pragma unroll
+      for (int i = 0; i + w < C; i += 2 * w) t[i] += t[i + w];
+    }
+    acc = (c == 0) ? t[0] : acc + t[0];
+  }
+  return {cm, acc};
+}
+
 // First pass of a unit over this thread's vectors: (max, sum) of the slice
 // for p (and q for a pair), or the slice arg max at T = 0; one state per
 // wave into LDS.
 template <typename E, int NV>
 __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const UnitDesc& u,
                                                 const Slice& sc, const Regs<NV>& R, TeamLds& L,
-                                                int b) {
+                                                int b, float (&e)[2 * NV * E::kPerVec],
+                                                float& mslp, float& mslq) {
   constexpr int VEC = E::kPerVec;
   if (u.kind == 0) return;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int64_t lo = sc.lo, vhi = sc.vhi, hi = sc.hi;
   const auto* prow = row_ptr<E>(p.target, u.trow, p.stride);
   if (u.kind == 3) {
@@ -254,8 +291,8 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
   float x[VEC * NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) E::unpack(R.p[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
-  SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
-  softmax_group<VEC * NV>(sp, x, sl);
+  SoftmaxPart sq{-INFINITY, 0.0f};
+  SoftmaxPart sp = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[0]), mslp);
   for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
     float x1[1] = {E::load1(prow, i)};
     softmax_group<1>(sp, x1, sl);
@@ -264,7 +301,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
 #pragma unroll
     for (int i = 0; i < NV; ++i)
       E::unpack(R.q[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
-    softmax_group<VEC * NV>(sq, x, sl);
+    sq = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[VEC * NV]), mslq);
     const auto* qrow = row_ptr<E>(p.draft, u.drow, p.stride);
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
       float x1[1] = {E::load1(qrow, i)};
@@ -280,33 +317,50 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
 }
 
 // Second pass of a row pair: this thread's share of sum min(p, q) with the
-// team's normalisers; one sum per wave into LDS.
+// team's log2 normalisers c, from the exponentials kept by the first pass:
+// p = ep Kp and q = eq Kq with Kp = 2^(mslp - c_p), Kq = 2^(mslq - c_q), and
+// min(p, q) = Kp min(ep, eq Kq / Kp).  Kp <= 1 (the thread maximum is at most
+// the row maximum); a thread with Kp under 2^-60 holds p values that small
+// and adds nothing.  One sum per wave into LDS.
 template <typename E, int NV>
 __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const UnitDesc& u,
-                                                 const Slice& sc, const Regs<NV>& R, TeamLds& L,
-                                                 int b) {
+                                                 const Slice& sc,
+                                                 const uint4 (&ex)[2 * NV * E::kPerVec / 4],
+                                                 TeamLds& L, int b, float mslp, float mslq) {
   constexpr int VEC = E::kPerVec;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  constexpr int H = NV * VEC / 4;  // 16-byte vectors of one row's exponentials
+  static_assert(H == 1 || H % 2 == 0, "row exponentials are 1 or an even number of vectors");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const float sl = u.sl;
   const float cp = L.c[b][0], cq = L.c[b][1];
   const bool ok = L.ok[b] != 0;
   float acc = 0.0f;
   if (ok) {
+    const float kp = exp2_fast(mslp - cp), kq = exp2_fast(mslq - cq);
+    const float r = kp > 0x1p-60f ? kq / kp : 0.0f;
+    // chunks of G 16-byte vectors of each row
+    constexpr int G = H >= 2 ? 2 : 1;
+    float sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float a[VEC], c[VEC], e[VEC];
-      E::unpack(R.p[i], a);
-      E::unpack(R.q[i], c);
+    for (int c = 0; c < H; c += G) {
+      float m[4 * G];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j)
-        e[j] = exp2_fast(fminf(__builtin_fmaf(a[j], sl, -cp), __builtin_fmaf(c[j], sl, -cq)));
-#pragma unroll
-      for (int w = 1; w < VEC; w <<= 1) {
-#pragma unroll
-        for (int j = 0; j + w < VEC; j += 2 * w) e[j] += e[j + w];
+      for (int h = 0; h < G; ++h) {
+        const uint4 a = ex[c + h], q = ex[H + c + h];
+        m[4 * h + 0] = fminf(__uint_as_float(a.x), __uint_as_float(q.x) * r);
+        m[4 * h + 1] = fminf(__uint_as_float(a.y), __uint_as_float(q.y) * r);
+        m[4 * h + 2] = fminf(__uint_as_float(a.z), __uint_as_float(q.z) * r);
+        m[4 * h + 3] = fminf(__uint_as_float(a.w), __uint_as_float(q.w) * r);
       }
-      acc += e[0];
+#pragma unroll
+      for (int w = 1; w < 4 * G; w <<= 1) {
+#pragma unroll
+        for (int j = 0; j + w < 4 * G; j += 2 * w) m[j] += m[j + w];
+      }
+      sum += m[0];
     }
+    acc = sum * kp;
     const auto* prow = row_ptr<E>(p.target, u.trow, p.stride);
     const auto* qrow = row_ptr<E>(p.draft, u.drow, p.stride);
     for (int64_t i = sc.vhi + threadIdx.x; i < sc.hi; i += kDataThreads)
@@ -369,8 +423,7 @@ __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const Uni
 }
 
 // Loads of one member's exchange record (lane m < T reads member m's record
-// of row pair u).  Issued one window ahead of their use; they stay in flight
-// across the barrier.
+// of row pair u).
 struct TeamPoll {
   uint64_t w[4];
 };
@@ -388,13 +441,13 @@ __device__ __forceinline__ TeamPoll team_poll(const VerifyParams& p, const UnitD
   return t;
 }
 
-// Completes the team wait for row pair u: the early poll t is checked first,
-// then the records are polled again until every member has published (or
-// the bounded wait expires).  Then the members' states are combined into the
-// row log2 normalisers (member 0 also stores the row states in its slots).
+// Team wait for row pair u: the records are polled until every member has
+// published (or the bounded wait expires).  Then the members' states are
+// combined into the row log2 normalisers (member 0 also stores the row
+// states in its slots).
 __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const UnitDesc& u,
-                                               TeamPoll t, TeamLds& L, int b, int team,
-                                               int member, bool& failed) {
+                                               TeamLds& L, int b, int team, int member,
+                                               bool& failed) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nt = p.team;
   const uint32_t need = (uint32_t)(u.ordinal + 1);
@@ -404,12 +457,13 @@ __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const Unit
     for (int k = 0; k < 4; ++k) mine = mine && (uint32_t)(q.w[k] >> 32) == need;
     return __all(lane >= nt || mine) != 0;
   };
+  TeamPoll t = team_poll(p, u, team);
   bool done = complete(t);
   const uint32_t limit = failed ? 1u : kSpinLimit;
   for (uint32_t spin = 0; !done && spin < limit; ++spin) {
+    __builtin_amdgcn_s_sleep(1);
     t = team_poll(p, u, team);
     done = complete(t);
-    if (!done) __builtin_amdgcn_s_sleep(1);
   }
   if (!done) {
     if (!failed && lane == 0)
@@ -467,15 +521,15 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
   const int64_t n = my_pairs + my_singles;
   const Slice sc = make_slice<E>(p, member);
 
-  // Both roles run steps s = 0 .. n + 1 with one barrier each, then a last
-  // one.  Data step s: loads of unit s + 2, first pass of unit s, unit s - 2
-  // taken out of its LDS parking slot and unit s parked there, barrier,
-  // second pass of unit s - 2.  Communication window s (between barriers s
-  // and s + 1): sum of the second pass of unit s - 3, combination and
-  // publication of the first pass of unit s, team wait for unit s - 1 (whose
-  // members published it a step earlier; its records were loaded at the end
-  // of the previous window), then the loads of unit s's records.
-  __shared__ uint4 park[2][2 * NV][kDataThreads];
+  // Both roles run steps s = 0 .. n with one barrier each, then a last one.
+  // Data step s: loads of unit s + 2, first pass of unit s, the
+  // exponentials of unit s - 1 taken out of the parking slot and those of
+  // unit s parked there, barrier, second pass of unit s - 1.  Communication window s
+  // (between barriers s and s + 1): sum of the second pass of unit s - 2,
+  // combination and publication of the first pass of unit s, team wait for
+  // unit s.
+  constexpr int kPark = 2 * NV * E::kPerVec / 4;
+  __shared__ uint4 park[kPark][kDataThreads];
   if (threadIdx.x < kDataThreads) {
     const uint4* dummy = neg_inf_line<E>();
     Regs<NV> R0, R1, R2;
@@ -483,47 +537,48 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     UnitDesc U1 = unit_at(p, 1, n, team, my_pairs);
     UnitDesc U2 = no_unit();
     UnitDesc un = unit_at(p, 2, n, team, my_pairs);
-    UnitDesc up1 = no_unit(), up2 = no_unit();  // units s - 1 and s - 2 (parked)
+    UnitDesc up = no_unit();  // unit s - 1 (parked)
+    float mslp1 = 0.0f, mslq1 = 0.0f;
     load_unit<E, NV>(p, U0, sc, R0, dummy);
     load_unit<E, NV>(p, U1, sc, R1, dummy);
-    // Step s: first pass on buffer s mod 3, loads into buffer s + 2 mod 3;
-    // the parking slot of units s and s - 2 is s mod 2.
+    // Step s: first pass on buffer s mod 3, loads into buffer s + 2 mod 3.
     auto step = [&](int64_t s, const Regs<NV>& Rf, const UnitDesc& Uf, Regs<NV>& Rl,
                     UnitDesc& Ul) {
       Ul = un;
       load_unit<E, NV>(p, Ul, sc, Rl, dummy);
       un = unit_at(p, s + 3, n, team, my_pairs);
-      first_pass_data<E, NV>(p, Uf, sc, Rf, L, (int)(s & 1));
-      // Swap unit s - 2 out of its parking slot and unit s in, so that the
-      // buffer of unit s is free before the second pass.
-      const int slot = (int)(s & 1);
-      Regs<NV> Rs;
-      if (wants_alpha(p, up2)) {
+      float e[2 * NV * E::kPerVec];
+      float mslp = 0.0f, mslq = 0.0f;
+      first_pass_data<E, NV>(p, Uf, sc, Rf, L, (int)(s & 1), e, mslp, mslq);
+      // Swap: unit s - 1 out of the parking slot, unit s in (each thread
+      // overwrites only the entries it has just read), before the barrier so
+      // that the LDS traffic overlaps the other waves' first passes.
+      uint4 ex[kPark];
+      if (wants_alpha(p, up)) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          Rs.p[i] = park[slot][i][threadIdx.x];
-          Rs.q[i] = park[slot][NV + i][threadIdx.x];
-        }
+        for (int k = 0; k < kPark; ++k) ex[k] = park[k][threadIdx.x];
       }
       if (wants_alpha(p, Uf)) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          park[slot][i][threadIdx.x] = Rf.p[i];
-          park[slot][NV + i][threadIdx.x] = Rf.q[i];
-        }
+        for (int k = 0; k < kPark; ++k)
+          park[k][threadIdx.x] = make_uint4(__float_as_uint(e[4 * k]), __float_as_uint(e[4 * k + 1]),
+                                            __float_as_uint(e[4 * k + 2]),
+                                            __float_as_uint(e[4 * k + 3]));
       }
       lds_barrier();
-      if (wants_alpha(p, up2)) second_pass_data<E, NV>(p, up2, sc, Rs, L, (int)(s & 1));
-      up2 = up1;
-      up1 = Uf;
+      if (wants_alpha(p, up))
+        second_pass_data<E, NV>(p, up, sc, ex, L, (int)((s - 1) & 1), mslp1, mslq1);
+      up = Uf;
+      mslp1 = mslp;
+      mslq1 = mslq;
     };
     for (int64_t s = 0;; s += 3) {
       step(s, R0, U0, R2, U2);
-      if (s + 1 > n + 1) break;
+      if (s + 1 > n) break;
       step(s + 1, R1, U1, R0, U0);
-      if (s + 2 > n + 1) break;
+      if (s + 2 > n) break;
       step(s + 2, R2, U2, R1, U1);
-      if (s + 3 > n + 1) break;
+      if (s + 3 > n) break;
     }
     lds_barrier();
   } else {
@@ -544,6 +599,10 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
                                  : p.plan_singles + ((int64_t)team + (int64_t)p.nteams * (j - my_pairs));
         blk = *reinterpret_cast<const uint4*>(&it->code);
       }
+      // Wait for the block here, once per 64 steps: the compiler cannot
+      // track this conditional load across iterations and would otherwise
+      // wait for every outstanding load (the team polls) before each read.
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     };
     auto comm_unit = [&](int64_t s) {
       if (s >= n) return no_unit();
@@ -559,31 +618,27 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
       return u;
     };
     bool failed = false;
-    UnitDesc um3 = no_unit(), um2 = no_unit(), um1 = no_unit();
-    TeamPoll early{{0ull, 0ull, 0ull, 0ull}};
-    for (int64_t s = 0; s <= n + 1; ++s) {
+    UnitDesc um2 = no_unit(), um1 = no_unit();
+    for (int64_t s = 0; s <= n; ++s) {
       lds_barrier();
       if ((s & 63) == 0) load_block(s);
       const UnitDesc u = comm_unit(s);
-      first_pass_comm(p, u, L, (int)(s & 1), team, member, um3, (int)((s - 3) & 1));
-      if (wants_alpha(p, um1))
-        team_wait_comm(p, um1, early, L, (int)((s - 1) & 1), team, member, failed);
-      // early poll of unit s, checked in the next window
-      if (wants_alpha(p, u)) early = team_poll(p, u, team);
-      um3 = um2;
+      first_pass_comm(p, u, L, (int)(s & 1), team, member, um2, (int)((s - 2) & 1));
+      if (wants_alpha(p, u)) team_wait_comm(p, u, L, (int)(s & 1), team, member, failed);
       um2 = um1;
       um1 = u;
     }
     lds_barrier();
-    // um3 is now unit n - 1
-    if (wants_alpha(p, um3)) second_pass_comm(p, um3, L, (int)((n - 1) & 1), member);
+    // um2 is now unit n - 1
+    if (wants_alpha(p, um2)) second_pass_comm(p, um2, L, (int)((n - 1) & 1), member);
   }
 }
 
 // Team geometry for a row of V elements: NV <= 2 16-byte vectors per data
-// thread per row (three buffers of two rows stay in registers, two more are
-// parked in LDS), T members per row.  Returns false if a row needs more than 64 members (the caller then
-// uses the streaming row pass).
+// thread per row (three buffers of two rows stay in registers, the
+// exponentials of one more row pair are parked in LDS), T members per row.
+// Returns false if a row needs more than 64 members (the caller then uses
+// the streaming row pass).
 bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
                    int32_t* slice_len) {
   const int64_t vec = (dtype == SV_DTYPE_BF16) ? 8 : 4;
