@@ -210,6 +210,7 @@ __device__ __forceinline__ T tile_mass(const W& weights, int64_t tile, int64_t V
 struct PickResult {
   int64_t y;
   double margin;
+  double R;  // total of the tile masses
   int found;
 };
 
@@ -228,33 +229,38 @@ struct PickLds {
 // The draw given per-tile masses: scan the masses (rounds of 256 tiles, carry
 // in order) for the total R and the crossing tile, then scan inside it.  The
 // first y with C(y) > t = u * R wins; margin = min(t - C(y-1), C(y) - t).
+// When the tiles fit one round (S2 <= 256) the one scan gives both the total
+// and every tile's inclusive value.
 template <typename T, typename W>
 __device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W& weights,
                            PickLds<T>& L) {
   const int tid = threadIdx.x;
-  // total
-  T carry = T(0);
-  for (int64_t base = 0; base < S2; base += kDrawThreads) {
-    const T m = (base + tid < S2) ? masses[base + tid] : T(0);
-    T tot;
-    scan256<T>(m, L.scan, &tot);
-    carry = carry + tot;
-  }
-  const T R = carry;
-  const T t = u * R;
+  const int lane = tid & (kWave - 1);
   if (tid == 0) {
     L.found = 0;
     L.tile = -1;
   }
-  __syncthreads();
-  // crossing tile: the first tile whose inclusive cumulative mass exceeds t
-  carry = T(0);
+  T carry = T(0);
+  T m1 = T(0), incl1 = T(0);  // this thread's tile (single round)
   for (int64_t base = 0; base < S2; base += kDrawThreads) {
     const T m = (base + tid < S2) ? masses[base + tid] : T(0);
     T tot;
-    const T incl = carry + scan256<T>(m, L.scan, &tot);
+    const T incl = scan256<T>(m, L.scan, &tot);
+    m1 = m;
+    incl1 = incl;
+    carry = carry + tot;
+  }
+  const T R = carry;
+  const T t = u * R;
+  // crossing tile: the first tile whose inclusive cumulative mass exceeds t
+  carry = T(0);
+  for (int64_t base = 0; base < S2; base += kDrawThreads) {
+    T m = m1, incl = incl1, tot = R;
+    if (S2 > kDrawThreads) {
+      m = (base + tid < S2) ? masses[base + tid] : T(0);
+      incl = carry + scan256<T>(m, L.scan, &tot);
+    }
     T excl = shfl_up1(incl);
-    const int lane = tid & (kWave - 1);
     // exclusive value across wave boundaries: previous thread's inclusive
     if (lane == kWave - 1) L.last[tid / kWave] = incl;
     __syncthreads();
@@ -280,7 +286,7 @@ __device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W&
     carry = carry + tot;
     __syncthreads();
   }
-  PickResult res{-1, 0.0, 0};
+  PickResult res{-1, 0.0, (double)R, 0};
   const int tile = L.tile;
   if (tile < 0) return res;  // t at or past the total: undecided
   const T c0 = L.c0;
@@ -292,7 +298,6 @@ __device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W&
   T tot;
   const T incl = scan256<T>(sum8(w), L.scan, &tot);
   T excl = shfl_up1(incl);
-  const int lane = tid & (kWave - 1);
   if (lane == kWave - 1) L.last[tid / kWave] = incl;
   __syncthreads();
   if (lane == 0) excl = (tid == 0) ? T(0) : L.last[tid / kWave - 1];
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick32(VerifyParams p) {
   const DrawState st = p.req[r];
   if (st.mode == kDrawNone) return;
   const Weights32<E> w = weights32<E>(p, st);
-  PickResult res{-1, 0.0, 0};
+  PickResult res{-1, 0.0, 0.0, 0};
   const bool force64 = (p.flags & SV_FLAG_FORCE_FP64_DRAW) != 0u;
   if (!force64) res = pick<float>(p.seg_w32 + (int64_t)r * p.S2, p.S2, p.V, st.u, w, L);
   if (threadIdx.x == 0) {
@@ -501,25 +506,49 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
   }
 }
 
-// Full-row float64 normaliser from the tile partials (fixed-order tree).
-__device__ __forceinline__ double merge_z64(const double* parts, int64_t S2, double* lds) {
-  double z = 0.0;
-  for (int64_t j = threadIdx.x; j < S2; j += kDrawThreads) z += parts[j];
-  return block_sum256<double>(z, lds);
+// Full-row float64 normalisers of both rows from the tile partials (the same
+// fixed-order tree for each), in one block reduction.
+__device__ __forceinline__ void merge_z64(const double* pp, const double* pq, int64_t S2,
+                                          double (*lds)[2], double& zp, double& zq) {
+  double a = 0.0, b = 0.0;
+  for (int64_t j = threadIdx.x; j < S2; j += kDrawThreads) {
+    a += pp[j];
+    if (pq) b += pq[j];
+  }
+  for (int m = 1; m < kWave; m <<= 1) {
+    a += shfl_xor_d(a, m);
+    b += shfl_xor_d(b, m);
+  }
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (lane == 0) {
+    lds[wave][0] = a;
+    lds[wave][1] = b;
+  }
+  __syncthreads();
+  zp = 0.0;
+  zq = 0.0;
+  for (int w = 0; w < kDrawThreads / kWave; ++w) {
+    zp += lds[w][0];
+    zq += lds[w][1];
+  }
+  __syncthreads();
 }
 
 template <typename E>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   __shared__ PickLds<double> L;
   __shared__ double lds[kDrawThreads / kWave];
+  __shared__ double lds2[kDrawThreads / kWave][2];
   __shared__ int s_redo[kDrawThreads];
   const int r = blockIdx.x;
   const DrawState st = p.req[r];
   if (st.mode == kDrawNone || !st.need64) return;
   const bool residual = st.mode == kDrawResidual;
   double* masses = p.seg_w64 + (int64_t)r * p.S2;
-  const double Zp = merge_z64(p.seg_zp64 + (int64_t)r * p.S2, p.S2, lds);
-  const double Zq = residual ? merge_z64(p.seg_zq64 + (int64_t)r * p.S2, p.S2, lds) : 1.0;
+  double Zp, Zq;
+  merge_z64(p.seg_zp64 + (int64_t)r * p.S2, residual ? p.seg_zq64 + (int64_t)r * p.S2 : nullptr,
+            p.S2, lds2, Zp, Zq);
+  if (!residual) Zq = 1.0;
   Weights64<E> w = weights64<E>(p, st, false);
   w.lnzp = log(Zp);
   w.lnzq = log(Zq);
@@ -531,6 +560,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   // residual weight per unit of ep of an equal-logit pair
   const double kappa = exp(((double)st.mp - (double)st.mq) * w.invT);
   const double g_tie = fmax(0.0, (Zq - kappa * Zp) / (Zp * Zq));
+  const double izp = 1.0 / Zp, izq = 1.0 / Zq;
   for (int64_t base = 0; base < p.S2; base += kDrawThreads) {
     const int64_t t = base + threadIdx.x;
     int redo = 0;
@@ -539,10 +569,16 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
       if (!residual) {
         masses[t] = p.seg_zp64[o] / Zp;
       } else if (split_ok && p.seg_u32[o] <= kDrawKeep64) {
-        double m = (masses[t] + (rho - rho_e) * p.seg_a64[o]) / Zq + p.seg_t64[o] * g_tie;
-        const double* keep = p.seg_e64 + o * (kDrawKeep64 * 2);
-        for (int k = 0; k < p.seg_u32[o]; ++k)
-          m += fmax(0.0, keep[2 * k] / Zp - keep[2 * k + 1] / Zq);
+        const int32_t nk = p.seg_u32[o];
+        double m = (masses[t] + (rho - rho_e) * p.seg_a64[o]) * izq + p.seg_t64[o] * g_tie;
+        // the whole list is loaded at once (entries past nk are unused)
+        const double2* keep = reinterpret_cast<const double2*>(p.seg_e64 + o * (kDrawKeep64 * 2));
+        double2 kv[kDrawKeep64];
+#pragma unroll
+        for (int k = 0; k < kDrawKeep64; ++k) kv[k] = keep[k];
+#pragma unroll
+        for (int k = 0; k < kDrawKeep64; ++k)
+          if (k < nk) m += fmax(0.0, kv[k].x * izp - kv[k].y * izq);
         masses[t] = m;
       } else {
         redo = 1;
@@ -557,24 +593,12 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
     }
     __syncthreads();
   }
-  // Residual mass (float64): the sum of the tile masses, same order as pick.
-  double R = 0.0;
-  {
-    double carry = 0.0;
-    for (int64_t base = 0; base < p.S2; base += kDrawThreads) {
-      const double m = (base + threadIdx.x < p.S2) ? masses[base + threadIdx.x] : 0.0;
-      double tot;
-      scan256<double>(m, lds, &tot);
-      carry = carry + tot;
-    }
-    R = carry;
-  }
-  const bool unnorm = !(R > 0.0);
-  PickResult res;
-  if (!unnorm) {
-    res = pick<double>(masses, p.S2, p.V, (double)st.u, w, L);
-  } else {
-    // p = q to float64 precision: draw from p (unnormalised tile partials).
+  // The pick scans the tile masses once for the residual mass R and the
+  // crossing tile.  R = 0 (p = q to float64 precision): draw from p, from the
+  // unnormalised tile partials.
+  PickResult res = pick<double>(masses, p.S2, p.V, (double)st.u, w, L);
+  const bool unnorm = !(res.R > 0.0);
+  if (unnorm) {
     const Weights64<E> wu = weights64<E>(p, st, true);
     res = pick<double>(p.seg_zp64 + (int64_t)r * p.S2, p.S2, p.V, (double)st.u, wu, L);
   }
