@@ -102,6 +102,16 @@ def lib() -> ctypes.CDLL:
     L.svo_accept_stats.argtypes = [_i32p, _f64p, _i32p, ctypes.c_int32, ctypes.c_int32, _f64p,
                                    _f64p, _f64p]
     L.svo_accept_stats.restype = ctypes.c_int
+    L.svo_draft_confidence.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32, _i64p, _i32p, _i32p, _f32p, _f32p]
+    L.svo_draft_confidence.restype = ctypes.c_int
+    L.svo_table_latency.argtypes = [ctypes.c_int32, _i32p, _f32p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32]
+    L.svo_table_latency.restype = ctypes.c_double
+    L.svo_select_budget_ratio.argtypes = [_f32p, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                          ctypes.c_int32, _f64p, ctypes.c_int32, _i32p, _f32p,
+                                          _i32p, _i64p, _f64p, _i32p, _i64p, _i64p, _f64p]
+    L.svo_select_budget_ratio.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -292,6 +302,58 @@ def fixed_depth(B: int, D: int, K: int) -> np.ndarray:
     depth = np.zeros(B, dtype=np.int32)
     lib().svo_fixed_depth(B, D, int(K), _p(depth, _i32p))
     return depth
+
+
+# ---- drafter confidence and keep-ratio choice --------------------------------
+
+def draft_confidence(draft, draft_row0, draft_tokens, temperature, depth=None):
+    """conf[r, k] = softmax(draft row draft_row0[r] + k / T_r)[d_rk] (T = 0 read as 1)
+    for k < depth[r]; 0 past the depth; NaN for invalid rows, tokens, depths or
+    temperatures.  draft: (rows, V) float32; draft_tokens: (B, D_max) int32."""
+    x = _f32(draft)
+    V = x.shape[1]
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    B, D = tok.shape
+    dr0 = np.ascontiguousarray(draft_row0, dtype=np.int64)
+    T = np.ascontiguousarray(temperature, dtype=np.float32)
+    dep = None if depth is None else np.ascontiguousarray(depth, dtype=np.int32)
+    conf = np.zeros((B, D), dtype=np.float32)
+    st = lib().svo_draft_confidence(_p(x, _f32p), V, V, B, D, _p(dr0, _i64p), _p(tok, _i32p),
+                                    _p(dep, _i32p), _p(T, _f32p), _p(conf, _f32p))
+    if st != 0:
+        raise ValueError("svo_draft_confidence: invalid argument")
+    return conf
+
+
+def table_latency(table_batch, table_latency_rows, j: int, B: int) -> float:
+    tb = np.ascontiguousarray(table_batch, dtype=np.int32)
+    tl = np.ascontiguousarray(table_latency_rows, dtype=np.float32)
+    return lib().svo_table_latency(tb.size, _p(tb, _i32p), _p(tl, _f32p), tl.shape[1], int(j), int(B))
+
+
+def select_budget_ratio(conf, ratios, table_batch, table_latency_rows, max_depth=None):
+    """D-cut keep-ratio choice.  table_latency_rows: (n_batch, n_ratios)."""
+    c = _f32(conf)
+    B, D = c.shape
+    rr = np.ascontiguousarray(ratios, dtype=np.float64)
+    tb = np.ascontiguousarray(table_batch, dtype=np.int32)
+    tl = np.ascontiguousarray(table_latency_rows, dtype=np.float32)
+    md = None if max_depth is None else np.ascontiguousarray(max_depth, dtype=np.int32)
+    choice = np.zeros(1, dtype=np.int32)
+    K = np.zeros(1, dtype=np.int64)
+    proj = np.zeros(rr.size, dtype=np.float64)
+    depth = np.zeros(B, dtype=np.int32)
+    dr0 = np.zeros(B, dtype=np.int64)
+    tr0 = np.zeros(B, dtype=np.int64)
+    util = np.zeros(2, dtype=np.float64)
+    st = lib().svo_select_budget_ratio(_p(c, _f32p), B, D, _p(md, _i32p), rr.size, _p(rr, _f64p),
+                                       tb.size, _p(tb, _i32p), _p(tl, _f32p), _p(choice, _i32p),
+                                       _p(K, _i64p), _p(proj, _f64p), _p(depth, _i32p),
+                                       _p(dr0, _i64p), _p(tr0, _i64p), _p(util, _f64p))
+    if st != 0:
+        raise ValueError("svo_select_budget_ratio: invalid argument")
+    return dict(choice=int(choice[0]), K=int(K[0]), projected=proj, depth=depth, draft_row0=dr0,
+                target_row0=tr0, utility=util)
 
 
 # ---- statistics ------------------------------------------------------------

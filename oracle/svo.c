@@ -502,3 +502,119 @@ int svo_accept_stats(const int32_t* depth, const double* alpha, const int32_t* a
   }
   return SVO_OK;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Drafter confidence ("AngelSpec: specialize the drafter..." section "D-cut",
+ * Figure 3 panel 1: the drafter emits confidence-scored candidate tokens;
+ * equation A-hat multiplies these confidences along a request).  Reading:
+ * the confidence of draft token d at position k is the drafter's own
+ * probability of it, q_k(d) = softmax(draft row k / T)[d]; a greedy drafter
+ * (T = 0) is scored by its softmax at T = 1.  NaN marks an invalid row,
+ * token, depth or temperature (the budget reads NaN as 0); positions at or
+ * past the request's depth get 0. */
+int svo_draft_confidence(const float* draft, int64_t V, int64_t row_stride, int32_t B,
+                         int32_t D_max, const int64_t* draft_row0, const int32_t* draft_tokens,
+                         const int32_t* depth, const float* temperature, float* conf) {
+  if (B < 0 || D_max < 0 || V < 1 || row_stride < V || !conf) return SVO_ERR_INVALID_ARGUMENT;
+  if (B > 0 && D_max > 0 && (!draft || !draft_row0 || !draft_tokens || !temperature))
+    return SVO_ERR_INVALID_ARGUMENT;
+  for (int32_t r = 0; r < B; ++r) {
+    const int32_t n = depth ? depth[r] : D_max;
+    const double T = (double)temperature[r];
+    const int bad_request = n < 0 || n > D_max || !(T >= 0.0) || isinf(T);
+    const double Te = T > 0.0 ? T : 1.0;
+    for (int32_t k = 0; k < D_max; ++k) {
+      float* out = &conf[(int64_t)r * D_max + k];
+      if (bad_request) {
+        *out = NAN;
+        continue;
+      }
+      if (k >= n) {
+        *out = 0.0f;
+        continue;
+      }
+      const float* row = draft + (draft_row0[r] + k) * row_stride;
+      const int32_t d = draft_tokens[(int64_t)r * D_max + k];
+      if (d < 0 || (int64_t)d >= V || !svo_row_valid(row, V)) {
+        *out = NAN;
+        continue;
+      }
+      *out = (float)svo_prob(row, V, Te, d);
+    }
+  }
+  return SVO_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* D-cut's keep ratio ("AngelSpec: specialize the drafter..." section
+ * "D-cut": each step the ratio is chosen among a few values, by default
+ * 0.25, 0.5, 0.75 and 1, from a runtime cost table profiled across batch
+ * sizes and keep ratios (Figure 3 panel 2), as the one that maximises
+ * projected throughput rather than kept length).  Readings:
+ *  - ratio j keeps K_j = ceil(rho_j * N) draft positions, N = the number of
+ *    drafted positions (sum of the depth limits), since K counts draft
+ *    positions (the budget widget keeps 24 of 48 at rho = 1/2);
+ *  - projected tokens of ratio j = B + U_j, U_j = the kept utility of the
+ *    global top-K_j (equation A-hat summed over the batch: expected accepted
+ *    drafts) plus the one token every request emits;
+ *  - its latency is the table's, linearly interpolated in the batch size
+ *    between the two nearest profiled sizes and clamped at the ends;
+ *  - the first ratio (in the given order) with the largest tokens / latency
+ *    wins, and its allocation is returned. */
+double svo_table_latency(int32_t n_batch, const int32_t* table_batch, const float* table_latency,
+                         int32_t n_ratios, int32_t j, int32_t B) {
+  if (B <= table_batch[0]) return (double)table_latency[j];
+  if (B >= table_batch[n_batch - 1]) return (double)table_latency[(int64_t)(n_batch - 1) * n_ratios + j];
+  int32_t i = 0;
+  while (table_batch[i + 1] < B) ++i;
+  const double lo = (double)table_latency[(int64_t)i * n_ratios + j];
+  const double hi = (double)table_latency[(int64_t)(i + 1) * n_ratios + j];
+  const double f = (double)(B - table_batch[i]) / (double)(table_batch[i + 1] - table_batch[i]);
+  return lo + (hi - lo) * f;
+}
+
+int svo_select_budget_ratio(const float* conf, int32_t B, int32_t D_max, const int32_t* max_depth,
+                            int32_t n_ratios, const double* ratios, int32_t n_batch,
+                            const int32_t* table_batch, const float* table_latency,
+                            int32_t* choice, int64_t* K_chosen, double* projected,
+                            int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
+                            double* utility) {
+  if (B < 0 || D_max < 0 || n_ratios < 1 || n_batch < 1 || !ratios || !table_batch ||
+      !table_latency || !choice || !K_chosen || !depth)
+    return SVO_ERR_INVALID_ARGUMENT;
+  for (int32_t j = 0; j < n_ratios; ++j)
+    if (!(ratios[j] >= 0.0 && ratios[j] <= 1.0)) return SVO_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < n_batch; ++i) {
+    if (i > 0 && !(table_batch[i] > table_batch[i - 1])) return SVO_ERR_INVALID_ARGUMENT;
+    for (int32_t j = 0; j < n_ratios; ++j) {
+      const float l = table_latency[(int64_t)i * n_ratios + j];
+      if (!(l > 0.0f) || isinf(l)) return SVO_ERR_INVALID_ARGUMENT;
+    }
+  }
+  int64_t N = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    int32_t lim = max_depth ? max_depth[r] : D_max;
+    if (lim < 0) lim = 0;
+    if (lim > D_max) lim = D_max;
+    N += lim;
+  }
+  int32_t best = -1;
+  double best_tp = 0.0;
+  for (int32_t j = 0; j < n_ratios; ++j) {
+    const int64_t K = (int64_t)ceil(ratios[j] * (double)N);
+    double u[2];
+    int st = svo_allocate_budget(conf, B, D_max, max_depth, K, depth, NULL, NULL, u);
+    if (st != SVO_OK) return st;
+    const double lat = svo_table_latency(n_batch, table_batch, table_latency, n_ratios, j, B);
+    const double tp = ((double)B + u[0]) / lat;
+    if (projected) projected[j] = tp;
+    if (best < 0 || tp > best_tp) {
+      best = j;
+      best_tp = tp;
+    }
+  }
+  *choice = best;
+  *K_chosen = (int64_t)ceil(ratios[best] * (double)N);
+  return svo_allocate_budget(conf, B, D_max, max_depth, *K_chosen, depth, draft_row0, target_row0,
+                             utility);
+}

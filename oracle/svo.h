@@ -156,6 +156,32 @@ int svo_allocate_budget(const float* conf, int32_t B, int32_t D_max, const int32
  * depth, floor(K / B), and the first K mod B requests get one more. */
 void svo_fixed_depth(int32_t B, int32_t D_max, int64_t K, int32_t* depth);
 
+/* Drafter confidence: conf[r * D_max + k] = softmax(draft row / T_r)[d]
+ * (T_r = 0 read as 1) for k < depth[r] (depth NULL = D_max), row
+ * draft_row0[r] + k of a buffer with row_stride elements per row, d =
+ * draft_tokens[r * D_max + k]; 0 for k >= depth[r]; NaN for an invalid row,
+ * token, depth or temperature. */
+int svo_draft_confidence(const float* draft, int64_t V, int64_t row_stride, int32_t B,
+                         int32_t D_max, const int64_t* draft_row0, const int32_t* draft_tokens,
+                         const int32_t* depth, const float* temperature, float* conf);
+
+/* Latency of ratio j at batch size B from a table of n_batch ascending
+ * batch sizes x n_ratios latencies (row-major): linear interpolation between
+ * the two nearest sizes, clamped at the ends. */
+double svo_table_latency(int32_t n_batch, const int32_t* table_batch, const float* table_latency,
+                         int32_t n_ratios, int32_t j, int32_t B);
+
+/* D-cut keep-ratio choice: for each ratio j, K_j = ceil(rho_j * N) (N = sum
+ * of the depth limits), projected[j] = (B + kept utility of the top K_j) /
+ * latency_j; choice = the first j with the largest projected value, K_chosen
+ * = K_choice, and the allocation of svo_allocate_budget at that K. */
+int svo_select_budget_ratio(const float* conf, int32_t B, int32_t D_max, const int32_t* max_depth,
+                            int32_t n_ratios, const double* ratios, int32_t n_batch,
+                            const int32_t* table_batch, const float* table_latency,
+                            int32_t* choice, int64_t* K_chosen, double* projected,
+                            int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
+                            double* utility);
+
 /* ---- statistics --------------------------------------------------------------- */
 
 /* expected_len[r] = sum_{m < n_r} prod_{k <= m} alpha[r][k];
