@@ -218,6 +218,72 @@ sv_status sv_accept_stats(const int32_t* depth, const float* alpha, const int32_
                           int32_t B, int32_t D_max, float* expected_len, float* per_depth,
                           float* summary, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * sv_draft_confidence -- the drafter's confidence in each drafted token, the
+ * scores the D-cut budget ranks ("AngelSpec: specialize the drafter...",
+ * section "D-cut": Figure 3 panel 1, confidence-scored candidate tokens;
+ * equation A-hat multiplies them along a request).
+ *
+ * conf[r * D_max + k] = softmax(draft row / T_r)[d] for k < n_r, where the
+ * row is draft_row0[r] + k of draft_logits (row_stride elements per row),
+ * d = draft_tokens[r * D_max + k], n_r = depth[r] (depth NULL: D_max) and
+ * T_r = temperature[r], read as 1 when it is 0 (a greedy drafter is scored
+ * by its softmax probability).  conf is 0 for k >= n_r and NaN where the row
+ * has a NaN or +inf or is all -inf, d is outside [0, V), or the request's
+ * temperature or depth is invalid (sv_allocate_budget reads NaN as 0).
+ *
+ * All arrays are device memory owned by the caller; conf is float [B, D_max].
+ * Layout requirements as for sv_verify_batch (16-byte aligned logits,
+ * row_stride a multiple of 8 (bf16) / 4 (fp32) elements, >= V).  workspace:
+ * device memory of at least sv_draft_confidence_workspace_bytes bytes,
+ * 256-byte aligned, scratch.  Errors: SV_ERR_INVALID_ARGUMENT for bad sizes
+ * or null pointers, SV_ERR_UNSUPPORTED for the dtype or layout,
+ * SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_DEVICE if a launch fails; nothing is
+ * launched on an error.  Stream-ordered, no host synchronisation.
+ * ------------------------------------------------------------------------- */
+size_t sv_draft_confidence_workspace_bytes(sv_dtype dtype, int32_t B, int32_t D_max, int64_t V);
+
+sv_status sv_draft_confidence(sv_dtype dtype, int32_t B, int32_t D_max, int64_t V,
+                              int64_t row_stride, const void* draft_logits,
+                              const int64_t* draft_row0, const int32_t* draft_tokens,
+                              const int32_t* depth, const float* temperature, float* conf,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sv_select_budget_ratio -- D-cut's keep ratio ("AngelSpec: specialize the
+ * drafter...", section "D-cut": each step the ratio is chosen among a few
+ * values, by default 0.25, 0.5, 0.75 and 1, from a runtime latency table
+ * profiled across batch sizes and keep ratios, as the one that maximises
+ * projected throughput; Figure 3 panel 2), followed by the budget of
+ * sv_allocate_budget at the chosen K.
+ *
+ * With N = sum over requests of min(max(max_depth[r], 0), D_max) drafted
+ * positions, ratio j keeps K_j = ceil(ratios[j] * N) positions and projects
+ * (B + U_j) / latency_j tokens per unit time, U_j the kept utility (the sum
+ * of the kept prefix-confidence products).  latency_j comes from the host
+ * table table_latency[i * n_ratios + j] (n_batch rows, table_batch[i]
+ * strictly ascending batch sizes), linearly interpolated in B between the
+ * two nearest sizes and clamped at the ends.  The first j with the largest
+ * projected value is chosen.
+ *
+ * Host inputs: ratios [n_ratios] in [0, 1], 1 <= n_ratios <= SV_MAX_RATIOS;
+ * table_batch [n_batch]; table_latency [n_batch * n_ratios], finite and > 0.
+ * Device inputs: conf [B, D_max], max_depth [B] or NULL.  Device outputs:
+ * choice [1], K_chosen [1], projected [n_ratios] (optional), and depth,
+ * draft_row0, target_row0, utility as sv_allocate_budget.  Requires
+ * B * D_max <= SV_MAX_BUDGET_POSITIONS.  Errors: SV_ERR_INVALID_ARGUMENT
+ * before any launch, SV_ERR_DEVICE if the launch fails.
+ * ------------------------------------------------------------------------- */
+#define SV_MAX_RATIOS 8
+
+sv_status sv_select_budget_ratio(const float* conf, int32_t B, int32_t D_max,
+                                 const int32_t* max_depth, int32_t n_ratios,
+                                 const double* ratios, int32_t n_batch,
+                                 const int32_t* table_batch, const float* table_latency,
+                                 int32_t* choice, int64_t* K_chosen, float* projected,
+                                 int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
+                                 float* utility, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -161,6 +161,101 @@ sv_status sv_allocate_budget(const float* conf, int32_t B, int32_t D_max,
   return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
+size_t sv_draft_confidence_workspace_bytes(sv_dtype dtype, int32_t B, int32_t D_max, int64_t V) {
+  if (B < 0 || D_max < 0 || V < 1 || V > INT32_MAX) return 0;
+  if (dtype != SV_DTYPE_BF16 && dtype != SV_DTYPE_FP32) return 0;
+  const int64_t rows = (int64_t)B * D_max;
+  const int64_t nseg = sv::confidence_segments(dtype, V);
+  if (rows * nseg > (int64_t)INT32_MAX) return 0;
+  const size_t bytes = (size_t)rows * (size_t)nseg * sizeof(float2);
+  return bytes == 0 ? 256 : (bytes + 255) / 256 * 256;
+}
+
+sv_status sv_draft_confidence(sv_dtype dtype, int32_t B, int32_t D_max, int64_t V,
+                              int64_t row_stride, const void* draft_logits,
+                              const int64_t* draft_row0, const int32_t* draft_tokens,
+                              const int32_t* depth, const float* temperature, float* conf,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SV_DTYPE_BF16 && dtype != SV_DTYPE_FP32) return SV_ERR_UNSUPPORTED;
+  if (B < 0 || D_max < 0 || V < 1 || V > INT32_MAX || row_stride < V)
+    return SV_ERR_INVALID_ARGUMENT;
+  const size_t need = sv_draft_confidence_workspace_bytes(dtype, B, D_max, V);
+  if (need == 0) return SV_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * D_max == 0) return SV_OK;
+  if (!draft_logits || !draft_row0 || !draft_tokens || !temperature || !conf)
+    return SV_ERR_INVALID_ARGUMENT;
+  const int64_t vec = (dtype == SV_DTYPE_BF16) ? 8 : 4;
+  if (!aligned16(draft_logits) || row_stride % vec != 0) return SV_ERR_UNSUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+  sv::ConfParams c{};
+  c.dtype = dtype;
+  c.B = B;
+  c.D = D_max;
+  c.V = V;
+  c.stride = row_stride;
+  c.logits = draft_logits;
+  c.row0 = draft_row0;
+  c.tokens = draft_tokens;
+  c.depth = depth;
+  c.temperature = temperature;
+  c.conf = conf;
+  c.part = static_cast<float2*>(workspace);
+  c.nseg = sv::confidence_segments(dtype, V);
+  const hipError_t e = sv::launch_confidence(c, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
+sv_status sv_select_budget_ratio(const float* conf, int32_t B, int32_t D_max,
+                                 const int32_t* max_depth, int32_t n_ratios,
+                                 const double* ratios, int32_t n_batch,
+                                 const int32_t* table_batch, const float* table_latency,
+                                 int32_t* choice, int64_t* K_chosen, float* projected,
+                                 int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
+                                 float* utility, void* stream) {
+  if (B < 0 || D_max < 0) return SV_ERR_INVALID_ARGUMENT;
+  if (B > SV_MAX_BUDGET_POSITIONS || (int64_t)B * D_max > SV_MAX_BUDGET_POSITIONS)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (n_ratios < 1 || n_ratios > SV_MAX_RATIOS || !ratios) return SV_ERR_INVALID_ARGUMENT;
+  if (n_batch < 1 || !table_batch || !table_latency) return SV_ERR_INVALID_ARGUMENT;
+  for (int32_t j = 0; j < n_ratios; ++j)
+    if (!(ratios[j] >= 0.0 && ratios[j] <= 1.0)) return SV_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < n_batch; ++i) {
+    if (i > 0 && !(table_batch[i] > table_batch[i - 1])) return SV_ERR_INVALID_ARGUMENT;
+    for (int32_t j = 0; j < n_ratios; ++j) {
+      const float l = table_latency[(int64_t)i * n_ratios + j];
+      if (!(l > 0.0f && l < INFINITY)) return SV_ERR_INVALID_ARGUMENT;
+    }
+  }
+  if (!choice || !K_chosen || !depth || (B > 0 && D_max > 0 && !conf))
+    return SV_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SV_OK;
+  // Latency of each ratio at this batch size: linear in the batch size
+  // between the two nearest profiled sizes, clamped at the table's ends.
+  sv::RatioArgs ra{};
+  ra.n = n_ratios;
+  int32_t lo = 0;
+  while (lo + 1 < n_batch && table_batch[lo + 1] < B) ++lo;
+  for (int32_t j = 0; j < n_ratios; ++j) {
+    ra.ratio[j] = ratios[j];
+    const double a = table_latency[(int64_t)lo * n_ratios + j];
+    if (B <= table_batch[0]) {
+      ra.latency[j] = (double)table_latency[j];
+    } else if (B >= table_batch[n_batch - 1]) {
+      ra.latency[j] = (double)table_latency[(int64_t)(n_batch - 1) * n_ratios + j];
+    } else {
+      const double b = table_latency[(int64_t)(lo + 1) * n_ratios + j];
+      const double f = (double)(B - table_batch[lo]) / (double)(table_batch[lo + 1] - table_batch[lo]);
+      ra.latency[j] = a + (b - a) * f;
+    }
+  }
+  const hipError_t e = sv::launch_budget_ratio(conf, B, D_max, max_depth, ra, choice, K_chosen,
+                                               projected, depth, draft_row0, target_row0, utility,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
 sv_status sv_accept_stats(const int32_t* depth, const float* alpha, const int32_t* accepted_len,
                           int32_t B, int32_t D_max, float* expected_len, float* per_depth,
                           float* summary, void* stream) {

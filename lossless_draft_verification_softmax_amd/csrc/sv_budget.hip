@@ -48,29 +48,32 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
 // position within its request's limit, 0 elsewhere.  Within a request the
 // scores do not increase with the position (confidences are clamped to
 // [0, 1]) and ~index decreases, so a request's keys strictly decrease and the
-// global top K keeps a prefix of every request.  The kernel therefore needs
+// global top K keeps a prefix of every request.  The kernels therefore need
 // only the K-th largest key t (a radix select, eight 8-bit digits from the
-// top) and counts per request the keys >= t; no sort.
-__global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, int32_t B, int32_t D,
-                                                           const int32_t* max_depth, int64_t K,
-                                                           int32_t* depth, int64_t* draft_row0,
-                                                           int64_t* target_row0, float* utility) {
-  __shared__ uint64_t keys[SV_MAX_BUDGET_POSITIONS];
-  __shared__ int32_t counts[SV_MAX_BUDGET_POSITIONS];
-  __shared__ int32_t hist[256];
-  __shared__ float red[kBudgetWaves];
-  __shared__ int32_t wtot[kBudgetWaves];
-  __shared__ int32_t s_valid, s_need, s_whole;
-  __shared__ uint64_t s_prefix;
-  __shared__ uint64_t s_min[kBudgetWaves];
+// top) and count per request the keys >= t; no sort.
+struct BudgetLds {
+  uint64_t keys[SV_MAX_BUDGET_POSITIONS];
+  int32_t counts[SV_MAX_BUDGET_POSITIONS];
+  int32_t hist[256];
+  float red[kBudgetWaves];
+  int32_t wtot[kBudgetWaves];
+  int32_t s_valid, s_need, s_whole;
+  uint64_t s_prefix;
+  uint64_t s_min[kBudgetWaves];
+};
+
+// Prefix-confidence products and keys; returns this thread's share of the
+// sum of all scores.  Leaves the keys in registers (key[j] = slot
+// j * kBudgetThreads + tid) and the number of valid positions in s_valid.
+__device__ float build_keys(const float* conf, int32_t B, int32_t D, const int32_t* max_depth,
+                            BudgetLds& S, uint64_t (&key)[kKeySlots]) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int N = B * D;
-  for (int r = tid; r < B; r += kBudgetThreads) counts[r] = 0;
-  if (tid == 0) s_valid = 0;
+  for (int r = tid; r < B; r += kBudgetThreads) S.counts[r] = 0;
+  if (tid == 0) S.s_valid = 0;
   // One coalesced pass stages the confidences in the key slots (as float
   // bits); the product loop then reads LDS.
-  for (int i = tid; i < N; i += kBudgetThreads) keys[i] = (uint64_t)__float_as_uint(conf[i]);
+  for (int i = tid; i < N; i += kBudgetThreads) S.keys[i] = (uint64_t)__float_as_uint(conf[i]);
   __syncthreads();
 
   // Prefix-confidence products, left to right in float32, one request per
@@ -84,134 +87,139 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, in
     for (int k = 0; k < D; ++k) {
       const int idx = r * D + k;
       if (k >= lim) {  // past this request's limit: key 0, never kept
-        keys[idx] = 0ull;
+        S.keys[idx] = 0ull;
         continue;
       }
-      float c = __uint_as_float((uint32_t)keys[idx]);
+      float c = __uint_as_float((uint32_t)S.keys[idx]);
       if (!(c >= 0.0f)) c = 0.0f;  // NaN and negatives read as 0
       if (c > 1.0f) c = 1.0f;
       sc = sc * c;
       total += sc;
-      keys[idx] = ((uint64_t)__float_as_uint(sc) << 32) | (uint64_t)(~(uint32_t)idx);
+      S.keys[idx] = ((uint64_t)__float_as_uint(sc) << 32) | (uint64_t)(~(uint32_t)idx);
     }
     valid += lim;
   }
-  atomicAdd(&s_valid, valid);
+  atomicAdd(&S.s_valid, valid);
   __syncthreads();
-
-  uint64_t key[kKeySlots];
 #pragma unroll
   for (int j = 0; j < kKeySlots; ++j) {
     const int i = j * kBudgetThreads + tid;
-    key[j] = i < N ? keys[i] : 0ull;
+    key[j] = i < N ? S.keys[i] : 0ull;
   }
-  int64_t kk = K < 0 ? 0 : K;
-  if (kk > s_valid) kk = s_valid;
-  const int32_t Keff = (int32_t)kk;
+  return total;
+}
 
-  // Radix select of the Keff-th largest key.  After digit round d, s_prefix
-  // holds its top 8 (d + 1) bits and s_need its rank among the keys that
-  // share them.  When every key sharing the prefix is kept (s_need equals
-  // their count), the threshold is the smallest of them and the remaining
-  // rounds are skipped.
+// The Keff-th largest key (~0 when Keff == 0: nothing kept).  After digit
+// round d, s_prefix holds its top 8 (d + 1) bits and s_need its rank among
+// the keys that share them.  When every key sharing the prefix is kept
+// (s_need equals their count), the threshold is the smallest of them and the
+// remaining rounds are skipped.
+__device__ uint64_t select_threshold(const uint64_t (&key)[kKeySlots], int N, int32_t Keff,
+                                     BudgetLds& S) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  __syncthreads();  // every thread is done with the previous call's state
   if (tid == 0) {
-    s_prefix = 0ull;
-    s_need = Keff;
-    s_whole = 0;
+    S.s_prefix = 0ull;
+    S.s_need = Keff;
+    S.s_whole = 0;
   }
-  uint64_t thr = ~0ull;  // nothing kept when Keff == 0
-  if (Keff > 0) {
-    for (int d = 0; d < 8; ++d) {
-      const int shift = 56 - 8 * d;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      const uint64_t prefix = s_prefix;
-      const int32_t need = s_need;
+  if (Keff <= 0) return ~0ull;
+  for (int d = 0; d < 8; ++d) {
+    const int shift = 56 - 8 * d;
+    if (tid < 256) S.hist[tid] = 0;
+    __syncthreads();
+    const uint64_t prefix = S.s_prefix;
+    const int32_t need = S.s_need;
 #pragma unroll
-      for (int j = 0; j < kKeySlots; ++j) {
-        // keys sharing the selected top bits (all keys in round 0)
-        const bool match = d == 0 || (key[j] >> (shift + 8)) == (prefix >> (shift + 8));
-        if (match && j * kBudgetThreads + tid < N)
-          atomicAdd(&hist[(int)((key[j] >> shift) & 255u)], 1);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane l holds digits 255 - 4 l .. 252 - 4 l (descending)
-        int32_t h[4];
+    for (int j = 0; j < kKeySlots; ++j) {
+      // keys sharing the selected top bits (all keys in round 0)
+      const bool match = d == 0 || (key[j] >> (shift + 8)) == (prefix >> (shift + 8));
+      if (match && j * kBudgetThreads + tid < N)
+        atomicAdd(&S.hist[(int)((key[j] >> shift) & 255u)], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds digits 255 - 4 l .. 252 - 4 l (descending)
+      int32_t h[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) h[j] = hist[255 - 4 * lane - j];
-        const int32_t sum = h[0] + h[1] + h[2] + h[3];
-        const int32_t incl = wave_incl_scan(sum);
-        int32_t run = incl - sum;
-        if (run < need && need <= incl) {
+      for (int j = 0; j < 4; ++j) h[j] = S.hist[255 - 4 * lane - j];
+      const int32_t sum = h[0] + h[1] + h[2] + h[3];
+      const int32_t incl = wave_incl_scan(sum);
+      int32_t run = incl - sum;
+      if (run < need && need <= incl) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (run < need && need <= run + h[j]) {
-              s_prefix = prefix | ((uint64_t)(255 - 4 * lane - j) << shift);
-              s_need = need - run;
-              s_whole = (need - run == h[j]) ? 1 : 0;
-            }
-            run += h[j];
+        for (int j = 0; j < 4; ++j) {
+          if (run < need && need <= run + h[j]) {
+            S.s_prefix = prefix | ((uint64_t)(255 - 4 * lane - j) << shift);
+            S.s_need = need - run;
+            S.s_whole = (need - run == h[j]) ? 1 : 0;
           }
+          run += h[j];
         }
-      }
-      __syncthreads();
-      if (s_whole && d < 7) {
-        // smallest key among those sharing the selected top 8 (d + 1) bits
-        const uint64_t pre = s_prefix;
-        uint64_t mn = ~0ull;
-#pragma unroll
-        for (int j = 0; j < kKeySlots; ++j)
-          if (j * kBudgetThreads + tid < N && (key[j] >> shift) == (pre >> shift) && key[j] < mn)
-            mn = key[j];
-        for (int m = 1; m < kWave; m <<= 1) {
-          const uint32_t lo32 = __shfl_xor((uint32_t)(mn & 0xffffffffull), m);
-          const uint32_t hi32 = __shfl_xor((uint32_t)(mn >> 32), m);
-          const uint64_t o = ((uint64_t)hi32 << 32) | lo32;
-          mn = o < mn ? o : mn;
-        }
-        if (lane == 0) s_min[wave] = mn;
-        __syncthreads();
-        uint64_t t = s_min[0];
-        for (int w2 = 1; w2 < kBudgetWaves; ++w2) t = s_min[w2] < t ? s_min[w2] : t;
-        s_prefix = t;  // every thread writes the same value
-        __syncthreads();
-        break;
       }
     }
-    thr = s_prefix;
+    __syncthreads();
+    if (S.s_whole && d < 7) {
+      // smallest key among those sharing the selected top 8 (d + 1) bits
+      const uint64_t pre = S.s_prefix;
+      uint64_t mn = ~0ull;
+#pragma unroll
+      for (int j = 0; j < kKeySlots; ++j)
+        if (j * kBudgetThreads + tid < N && (key[j] >> shift) == (pre >> shift) && key[j] < mn)
+          mn = key[j];
+      for (int m = 1; m < kWave; m <<= 1) {
+        const uint32_t lo32 = __shfl_xor((uint32_t)(mn & 0xffffffffull), m);
+        const uint32_t hi32 = __shfl_xor((uint32_t)(mn >> 32), m);
+        const uint64_t o = ((uint64_t)hi32 << 32) | lo32;
+        mn = o < mn ? o : mn;
+      }
+      if (lane == 0) S.s_min[wave] = mn;
+      __syncthreads();
+      uint64_t t = S.s_min[0];
+      for (int w2 = 1; w2 < kBudgetWaves; ++w2) t = S.s_min[w2] < t ? S.s_min[w2] : t;
+      S.s_prefix = t;  // every thread writes the same value
+      __syncthreads();
+      break;
+    }
   }
+  return S.s_prefix;
+}
 
-  // Kept positions per request and the kept utility.
+// Kept positions per request (counts), the kept utility (block sum) and the
+// packed row offsets: exclusive scans of c_r (draft rows) and c_r + 1
+// (target rows) over the requests; thread t takes kKeySlots consecutive
+// requests.
+__device__ float write_allocation(const uint64_t (&key)[kKeySlots], int32_t B, int32_t D,
+                                  uint64_t thr, BudgetLds& S, int32_t* depth,
+                                  int64_t* draft_row0, int64_t* target_row0) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int N = B * D;
   float kept = 0.0f;
 #pragma unroll
   for (int j = 0; j < kKeySlots; ++j) {
     const int i = j * kBudgetThreads + tid;
     if (i < N && key[j] != 0ull && key[j] >= thr) {
-      atomicAdd(&counts[i / D], 1);
+      atomicAdd(&S.counts[i / D], 1);
       kept += __uint_as_float((uint32_t)(key[j] >> 32));
     }
   }
   __syncthreads();
-  kept = block_sum_budget(kept, red);
-  total = block_sum_budget(total, red);
-
-  // Packed row offsets: exclusive scans of c_r (draft rows) and c_r + 1
-  // (target rows) over the requests; thread t takes kKeySlots consecutive
-  // requests.
+  kept = block_sum_budget(kept, S.red);
   int32_t c[kKeySlots];
   int32_t mine = 0;
 #pragma unroll
   for (int j = 0; j < kKeySlots; ++j) {
     const int r = tid * kKeySlots + j;
-    c[j] = r < B ? counts[r] : 0;
+    c[j] = r < B ? S.counts[r] : 0;
     mine += c[j];
   }
   const int32_t wincl = wave_incl_scan(mine);
-  if (lane == kWave - 1) wtot[wave] = wincl;
+  if (lane == kWave - 1) S.wtot[wave] = wincl;
   __syncthreads();
   int32_t before = wincl - mine;
-  for (int w = 0; w < wave; ++w) before += wtot[w];
+  for (int w = 0; w < wave; ++w) before += S.wtot[w];
   int64_t dr = before;
 #pragma unroll
   for (int j = 0; j < kKeySlots; ++j) {
@@ -223,7 +231,22 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, in
     }
     dr += c[j];
   }
-  if (utility && tid == 0) {
+  return kept;
+}
+
+__global__ __launch_bounds__(kBudgetThreads) void k_budget(const float* conf, int32_t B, int32_t D,
+                                                           const int32_t* max_depth, int64_t K,
+                                                           int32_t* depth, int64_t* draft_row0,
+                                                           int64_t* target_row0, float* utility) {
+  __shared__ BudgetLds S;
+  uint64_t key[kKeySlots];
+  float total = build_keys(conf, B, D, max_depth, S, key);
+  int64_t kk = K < 0 ? 0 : K;
+  if (kk > S.s_valid) kk = S.s_valid;
+  const uint64_t thr = select_threshold(key, B * D, (int32_t)kk, S);
+  const float kept = write_allocation(key, B, D, thr, S, depth, draft_row0, target_row0);
+  total = block_sum_budget(total, S.red);
+  if (utility && threadIdx.x == 0) {
     utility[0] = kept;
     utility[1] = total;
   }
@@ -234,6 +257,71 @@ hipError_t launch_budget(const float* conf, int32_t B, int32_t D, const int32_t*
                          float* utility, hipStream_t stream) {
   hipLaunchKernelGGL(k_budget, dim3(1), dim3(kBudgetThreads), 0, stream, conf, B, D, max_depth, K,
                      depth, draft_row0, target_row0, utility);
+  return hipGetLastError();
+}
+
+// D-cut's keep ratio ("AngelSpec: specialize the drafter...", section
+// "D-cut": the ratio is picked each step from a few values by a runtime
+// cost table so as to maximise projected throughput, not kept length).
+// Ratio j keeps K_j = ceil(rho_j N) of the N drafted positions; its
+// projected tokens are B (one per request) plus the kept utility U_j (the
+// sum of the kept prefix-confidence products, equation A-hat over the
+// batch), divided by the latency the caller's table gives this batch size.
+// The first ratio with the largest value wins; its allocation is written
+// as by k_budget.
+__global__ __launch_bounds__(kBudgetThreads) void k_budget_ratio(
+    const float* conf, int32_t B, int32_t D, const int32_t* max_depth, RatioArgs ra,
+    int32_t* choice, int64_t* K_chosen, float* projected, int32_t* depth, int64_t* draft_row0,
+    int64_t* target_row0, float* utility) {
+  __shared__ BudgetLds S;
+  const int tid = threadIdx.x;
+  const int N = B * D;
+  uint64_t key[kKeySlots];
+  float total = build_keys(conf, B, D, max_depth, S, key);
+  const int64_t valid = S.s_valid;
+  int best = -1;
+  double best_tp = 0.0;
+  uint64_t best_thr = ~0ull;
+  int64_t best_K = 0;
+  for (int j = 0; j < ra.n; ++j) {
+    int64_t Kj = (int64_t)ceil(ra.ratio[j] * (double)valid);
+    if (Kj > valid) Kj = valid;
+    const uint64_t thr = select_threshold(key, N, (int32_t)Kj, S);
+    float kept = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kKeySlots; ++s) {
+      const int i = s * kBudgetThreads + tid;
+      if (i < N && key[s] != 0ull && key[s] >= thr) kept += __uint_as_float((uint32_t)(key[s] >> 32));
+    }
+    kept = block_sum_budget(kept, S.red);
+    const double tp = ((double)B + (double)kept) / ra.latency[j];
+    if (projected && tid == 0) projected[j] = (float)tp;
+    if (best < 0 || tp > best_tp) {  // block-uniform values: every thread agrees
+      best = j;
+      best_tp = tp;
+      best_thr = thr;
+      best_K = Kj;
+    }
+  }
+  const float kept = write_allocation(key, B, D, best_thr, S, depth, draft_row0, target_row0);
+  total = block_sum_budget(total, S.red);
+  if (tid == 0) {
+    *choice = best;
+    *K_chosen = best_K;
+    if (utility) {
+      utility[0] = kept;
+      utility[1] = total;
+    }
+  }
+}
+
+hipError_t launch_budget_ratio(const float* conf, int32_t B, int32_t D, const int32_t* max_depth,
+                               const RatioArgs& ra, int32_t* choice, int64_t* K_chosen,
+                               float* projected, int32_t* depth, int64_t* draft_row0,
+                               int64_t* target_row0, float* utility, hipStream_t stream) {
+  hipLaunchKernelGGL(k_budget_ratio, dim3(1), dim3(kBudgetThreads), 0, stream, conf, B, D,
+                     max_depth, ra, choice, K_chosen, projected, depth, draft_row0, target_row0,
+                     utility);
   return hipGetLastError();
 }
 

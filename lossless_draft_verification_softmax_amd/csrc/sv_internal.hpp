@@ -180,4 +180,34 @@ hipError_t launch_stats(const int32_t* depth, const float* alpha, const int32_t*
                         int32_t B, int32_t D, float* expected_len, float* per_depth,
                         float* summary, hipStream_t stream);
 
+// Drafter confidence (sv_confidence.hip).
+struct ConfParams {
+  sv_dtype dtype;
+  int32_t B, D;
+  int64_t V, stride;
+  const void* logits;
+  const int64_t* row0;     // [B] first draft row of each request
+  const int32_t* tokens;   // [B, D]
+  const int32_t* depth;    // [B] or null (= D)
+  const float* temperature;
+  float* conf;             // [B, D]
+  float2* part;            // [B * D][nseg] segment states (workspace)
+  int64_t nseg;
+};
+int64_t confidence_segments(sv_dtype dtype, int64_t V);
+hipError_t launch_confidence(const ConfParams& c, hipStream_t stream);
+
+// Keep-ratio choice (sv_budget.hip): the candidate ratios and their
+// latencies at this batch size.
+constexpr int kMaxRatios = SV_MAX_RATIOS;
+struct RatioArgs {
+  int32_t n;
+  double ratio[kMaxRatios];
+  double latency[kMaxRatios];
+};
+hipError_t launch_budget_ratio(const float* conf, int32_t B, int32_t D, const int32_t* max_depth,
+                               const RatioArgs& ra, int32_t* choice, int64_t* K_chosen,
+                               float* projected, int32_t* depth, int64_t* draft_row0,
+                               int64_t* target_row0, float* utility, hipStream_t stream);
+
 }  // namespace sv

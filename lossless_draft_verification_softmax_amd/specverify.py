@@ -40,7 +40,10 @@ BIT_FP64_DRAW = 32
 BIT_SYNC_TIMEOUT = 64
 
 EXPORTS = ["sv_status_string", "sv_version", "sv_k_rho", "sv_allocate_budget",
-           "sv_verify_workspace_bytes", "sv_verify_batch", "sv_accept_stats"]
+           "sv_verify_workspace_bytes", "sv_verify_batch", "sv_accept_stats",
+           "sv_draft_confidence_workspace_bytes", "sv_draft_confidence", "sv_select_budget_ratio"]
+MAX_RATIOS = 8
+DCUT_RATIOS = (0.25, 0.5, 0.75, 1.0)
 
 
 class SvDiag(ctypes.Structure):
@@ -97,6 +100,19 @@ def load() -> ctypes.CDLL:
     L.sv_allocate_budget.restype = ctypes.c_int
     L.sv_accept_stats.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     L.sv_accept_stats.restype = ctypes.c_int
+    L.sv_draft_confidence_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_int64]
+    L.sv_draft_confidence_workspace_bytes.restype = ctypes.c_size_t
+    L.sv_draft_confidence.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                      vp]
+    L.sv_draft_confidence.restype = ctypes.c_int
+    L.sv_select_budget_ratio.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_double), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(ctypes.c_float), vp, vp, vp, vp, vp, vp,
+                                         vp, vp]
+    L.sv_select_budget_ratio.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -164,6 +180,76 @@ def allocate_budget(conf: torch.Tensor, K: int, max_depth: torch.Tensor | None =
                                    _ptr(out["draft_row0"]), _ptr(out["target_row0"]),
                                    _ptr(out["utility"]), _stream(dev))
     _check(st, "sv_allocate_budget")
+    return out
+
+
+class DraftConfidence:
+    """The drafter's confidence q_k(d_k) of every drafted token, computed on
+    the GPU from the draft rows (sv_draft_confidence).  Holds its workspace."""
+
+    def __init__(self, B: int, D_max: int, V: int, dtype: torch.dtype, device):
+        self.B, self.D, self.V = B, D_max, V
+        self.device = torch.device(device)
+        self.code = _dtype_code(dtype)
+        nbytes = int(load().sv_draft_confidence_workspace_bytes(self.code, B, D_max, V))
+        if nbytes == 0:
+            raise ValueError("sv_draft_confidence: unsupported sizes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.conf = torch.empty((B, D_max), dtype=torch.float32, device=self.device)
+
+    def __call__(self, draft: torch.Tensor, draft_row0: torch.Tensor, draft_tokens: torch.Tensor,
+                 temperature: torch.Tensor, depth: torch.Tensor | None = None) -> torch.Tensor:
+        rows, stride = _rows_view(draft)
+        if rows.shape[-1] != self.V or _dtype_code(rows.dtype) != self.code:
+            raise ValueError("draft logits do not match the sizes this object was built for")
+        dr0 = draft_row0.to(device=self.device, dtype=torch.int64).contiguous()
+        tok = draft_tokens.to(device=self.device, dtype=torch.int32).contiguous()
+        T = temperature.to(device=self.device, dtype=torch.float32).contiguous()
+        dep = None if depth is None else depth.to(device=self.device, dtype=torch.int32).contiguous()
+        self._keep = (dr0, tok, T, dep)
+        st = load().sv_draft_confidence(self.code, self.B, self.D, self.V, stride, _ptr(rows),
+                                        _ptr(dr0), _ptr(tok), _ptr(dep), _ptr(T), _ptr(self.conf),
+                                        _ptr(self.workspace), self.workspace.numel(),
+                                        _stream(self.device))
+        _check(st, "sv_draft_confidence")
+        return self.conf
+
+
+def draft_confidence(draft, draft_row0, draft_tokens, temperature, depth=None) -> torch.Tensor:
+    B, D = draft_tokens.shape
+    return DraftConfidence(B, D, draft.shape[-1], draft.dtype, draft.device)(
+        draft, draft_row0, draft_tokens, temperature, depth).clone()
+
+
+def select_budget_ratio(conf: torch.Tensor, table_batch, table_latency, ratios=DCUT_RATIOS,
+                        max_depth: torch.Tensor | None = None) -> dict:
+    """D-cut keep-ratio choice on the GPU, then the budget at the chosen K.
+    table_latency: (len(table_batch), len(ratios)) latencies (host values)."""
+    assert conf.is_cuda and conf.dtype == torch.float32 and conf.is_contiguous()
+    B, D = conf.shape
+    dev = conf.device
+    rr = [float(x) for x in ratios]
+    tb = [int(x) for x in table_batch]
+    tl = [float(x) for row in table_latency for x in row]
+    if len(tl) != len(tb) * len(rr):
+        raise ValueError("table_latency must have one row per batch size and one column per ratio")
+    c_r = (ctypes.c_double * len(rr))(*rr)
+    c_b = (ctypes.c_int32 * len(tb))(*tb)
+    c_l = (ctypes.c_float * len(tl))(*tl)
+    out = dict(choice=torch.empty(1, dtype=torch.int32, device=dev),
+               K=torch.empty(1, dtype=torch.int64, device=dev),
+               projected=torch.empty(len(rr), dtype=torch.float32, device=dev),
+               depth=torch.empty(B, dtype=torch.int32, device=dev),
+               draft_row0=torch.empty(B, dtype=torch.int64, device=dev),
+               target_row0=torch.empty(B, dtype=torch.int64, device=dev),
+               utility=torch.empty(2, dtype=torch.float32, device=dev))
+    md = None if max_depth is None else max_depth.to(device=dev, dtype=torch.int32).contiguous()
+    st = load().sv_select_budget_ratio(_ptr(conf), B, D, _ptr(md), len(rr), c_r, len(tb), c_b, c_l,
+                                       _ptr(out["choice"]), _ptr(out["K"]), _ptr(out["projected"]),
+                                       _ptr(out["depth"]), _ptr(out["draft_row0"]),
+                                       _ptr(out["target_row0"]), _ptr(out["utility"]),
+                                       _stream(dev))
+    _check(st, "sv_select_budget_ratio")
     return out
 
 

@@ -108,3 +108,56 @@ def test_budget_and_stats_validation_codes(sv):
     assert lib.sv_accept_stats(fake, None, fake, 4, 65, None, None, None, None) == 1
     assert lib.sv_accept_stats(None, None, fake, 4, 3, None, None, None, None) == 1
     assert lib.sv_accept_stats(None, None, None, 0, 3, None, None, None, None) == 0
+
+
+def test_confidence_validation_codes(sv):
+    lib = sv.load()
+    fake = 1 << 20  # a 256-byte aligned fake device address; nothing is dereferenced
+    ws = lib.sv_draft_confidence_workspace_bytes(0, 64, 16, 151936)
+    assert ws == 64 * 16 * 19 * 8  # 19 segments of 8192 bf16 elements, one float2 each
+    assert lib.sv_draft_confidence_workspace_bytes(0, 0, 16, 100) == 256
+    assert lib.sv_draft_confidence_workspace_bytes(7, 4, 4, 100) == 0
+    assert lib.sv_draft_confidence_workspace_bytes(1, 4, 4, 0) == 0
+
+    def call(dtype=0, B=4, D=3, V=1000, stride=1000, logits=fake, row0=fake, tok=fake, dep=None,
+             T=fake, conf=fake, ws_ptr=fake, ws_bytes=1 << 20):
+        return lib.sv_draft_confidence(dtype, B, D, V, stride, logits, row0, tok, dep, T, conf,
+                                       ws_ptr, ws_bytes, None)
+
+    assert call(dtype=5) == sv.SV_ERR_UNSUPPORTED
+    assert call(B=-1) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(stride=999) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(B=0) == sv.SV_OK
+    assert call(D=0) == sv.SV_OK
+    assert call(logits=None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(tok=None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(logits=fake + 4) == sv.SV_ERR_UNSUPPORTED
+    assert call(stride=1004) == sv.SV_ERR_UNSUPPORTED      # not a multiple of 8 bf16 elements
+    assert call(ws_ptr=fake + 16) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(ws_bytes=8) == sv.SV_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_ratio_validation_codes(sv):
+    lib = sv.load()
+    fake = 1 << 20
+    D = ctypes.c_double
+    I = ctypes.c_int32
+    F = ctypes.c_float
+
+    def call(B=4, Dm=3, ratios=(0.25, 0.5), tb=(4,), tl=(1.0, 2.0), choice=fake, conf=fake):
+        r = (D * len(ratios))(*ratios) if ratios is not None else None
+        return lib.sv_select_budget_ratio(conf, B, Dm, None, len(ratios or ()), r, len(tb),
+                                          (I * len(tb))(*tb), (F * len(tl))(*tl), choice, fake,
+                                          None, fake, None, None, None, None)
+
+    assert call(B=0) == sv.SV_OK
+    assert call(B=-1) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(B=100, Dm=64) == sv.SV_ERR_INVALID_ARGUMENT   # over SV_MAX_BUDGET_POSITIONS
+    assert call(ratios=()) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(ratios=(0.5,) * 9, tl=(1.0,) * 9) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(ratios=(0.5, 1.5)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(tb=(4, 4), tl=(1.0, 2.0, 1.0, 2.0)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(tl=(1.0, 0.0)) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(tl=(1.0, float("inf"))) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(choice=None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(conf=None) == sv.SV_ERR_INVALID_ARGUMENT

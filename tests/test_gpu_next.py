@@ -1,0 +1,154 @@
+"""GPU parity of the drafter confidence (sv_draft_confidence) and the D-cut
+keep-ratio choice (sv_select_budget_ratio) against the oracle, through the
+C ABI: the c4 batch at full size, both dtypes, ragged vocabularies with
+padded row strides (NaN in the padding, never read), masked and invalid
+rows, greedy requests, depth limits, and the choice's tie rules."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lossless_draft_verification_softmax_amd import specverify as sv
+from lossless_draft_verification_softmax_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+CONF_RTOL = 1e-5      # float32 normalisers against the oracle's long double
+CONF_ATOL = 1e-12
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sv.load()
+
+
+def check_conf(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.array_equal(np.isnan(gpu), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.all(np.abs(gpu[ok] - ref[ok]) <= CONF_RTOL * np.abs(ref[ok]) + CONF_ATOL), (
+        np.max(np.abs(gpu[ok] - ref[ok]) / np.maximum(np.abs(ref[ok]), 1e-30)))
+
+
+def test_confidence_c4_full_batch():
+    """Every (request, position) of the 64 x 16 x 151936 bf16 batch."""
+    w = synth.make("c4", device=DEV)
+    B, D, V = w.B, w.D, w.V
+    draft = w.draft.reshape(B * D, V)
+    dr0 = torch.arange(B, dtype=torch.int64, device=DEV) * D
+    conf = sv.draft_confidence(draft, dr0, w.draft_tokens, w.temperature)
+    torch.cuda.synchronize()
+    ref = oracle.draft_confidence(draft.float().cpu().numpy(), dr0.cpu().numpy(),
+                                  w.draft_tokens.cpu().numpy(), w.temperature.cpu().numpy())
+    check_conf(conf.cpu().numpy(), ref)
+    assert np.all(ref > 0) and np.all(ref <= 1)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V", [1, 7, 1000, 8191, 8193, 40000])
+def test_confidence_ragged_vocab_and_padding(dtype, V):
+    rng = np.random.default_rng(V)
+    B, D = 5, 4
+    vec = 8 if dtype == torch.bfloat16 else 4
+    stride = (V + vec - 1) // vec * vec + vec
+    rows = B * D + 3
+    X = (3.0 * rng.standard_normal((rows, stride))).astype(np.float32)
+    X[:, V:] = np.nan
+    X = torch.from_numpy(X).to(dtype).float().numpy()  # the values the GPU sees
+    X[:, V:] = np.nan
+    dr0 = np.array([0, 4, 8, 12, 17], dtype=np.int64)
+    tok = rng.integers(0, V, size=(B, D)).astype(np.int32)
+    T = np.array([1.0, 0.0, 0.6, 2.5, 1.0], np.float32)
+    depth = np.array([4, 3, 0, 4, 2], np.int32)
+    Xd = torch.from_numpy(X).to(dtype).to(DEV)
+    conf = sv.draft_confidence(Xd[:, :V], torch.from_numpy(dr0).to(DEV), torch.from_numpy(tok).to(DEV),
+                               torch.from_numpy(T).to(DEV), torch.from_numpy(depth).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.draft_confidence(np.ascontiguousarray(X[:, :V]), dr0, tok, T, depth)
+    check_conf(conf.cpu().numpy(), ref)
+
+
+def test_confidence_invalid_and_masked_rows():
+    V, B, D = 300, 4, 3
+    X = np.zeros((B * D, V), np.float32)
+    X[0, 5] = -np.inf                  # masked token scored: 0
+    X[1, :] = -np.inf                  # all masked: NaN
+    X[2, 9] = np.nan                   # NaN row
+    X[3, 100] = np.inf                 # +inf row
+    X[4, 7] = 30.0                     # a confident drafter
+    tok = np.array([[5, 0, 0], [0, 7, 299], [300, -1, 2], [1, 2, 3]], np.int32)
+    T = np.array([1.0, 0.7, 1.0, -2.0], np.float32)
+    depth = np.array([3, 3, 3, 3], np.int32)
+    dr0 = np.arange(B, dtype=np.int64) * D
+    conf = sv.draft_confidence(torch.from_numpy(X).to(DEV), torch.from_numpy(dr0).to(DEV),
+                               torch.from_numpy(tok).to(DEV), torch.from_numpy(T).to(DEV),
+                               torch.from_numpy(depth).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.draft_confidence(X, dr0, tok, T, depth)
+    check_conf(conf.cpu().numpy(), ref)
+    c = conf.cpu().numpy()
+    assert c[0, 0] == 0.0 and np.isnan(c[0, 1]) and np.isnan(c[0, 2])
+    assert c[1, 1] > 0.999999
+    assert np.isnan(c[2, 0]) and np.isnan(c[2, 1])
+    assert np.isnan(c[3]).all()
+
+
+def beta_conf(rng, B, D):
+    c = np.empty((B, D), np.float32)
+    c[: B // 2] = rng.beta(8, 2, size=(B // 2, D))
+    c[B // 2:] = rng.beta(3, 3, size=(B - B // 2, D))
+    return c
+
+
+def check_choice(conf, ratios, tb, tl, max_depth=None):
+    g = sv.select_budget_ratio(torch.from_numpy(conf).to(DEV), tb, tl, ratios,
+                               None if max_depth is None else torch.from_numpy(max_depth).to(DEV))
+    torch.cuda.synchronize()
+    o = oracle.select_budget_ratio(conf, ratios, tb, tl, max_depth)
+    proj = g["projected"].cpu().numpy().astype(np.float64)
+    assert np.allclose(proj, o["projected"], rtol=1e-5)
+    j = int(g["choice"].item())
+    # the choice is a best ratio up to float32 rounding of the utilities
+    assert o["projected"][j] >= o["projected"].max() * (1 - 1e-5)
+    B, D = conf.shape
+    lim = np.full(B, D) if max_depth is None else np.clip(max_depth, 0, D)
+    K = int(g["K"].item())
+    assert K == math.ceil(ratios[j] * int(lim.sum()))
+    ob = oracle.allocate_budget(conf, K, max_depth)
+    assert np.array_equal(g["depth"].cpu().numpy(), ob["depth"])
+    assert np.array_equal(g["draft_row0"].cpu().numpy(), ob["draft_row0"])
+    assert np.array_equal(g["target_row0"].cpu().numpy(), ob["target_row0"])
+    return j, o
+
+
+def test_ratio_choice_c4_confidences():
+    rng = np.random.default_rng(11)
+    B, D = 64, 16
+    ratios = list(sv.DCUT_RATIOS)
+    tb = [16, 32, 64, 128]
+    for trial in range(20):
+        conf = beta_conf(rng, B, D)
+        base = rng.uniform(10, 20, size=(len(tb), 1))
+        slope = rng.uniform(0.0, 40.0)
+        tl = (base + slope * np.array(ratios)[None, :]).astype(np.float32)
+        md = rng.integers(0, D + 1, size=B).astype(np.int32) if trial % 3 == 0 else None
+        check_choice(conf, ratios, tb, tl, md)
+
+
+def test_ratio_choice_ties_and_extremes():
+    rng = np.random.default_rng(12)
+    conf = beta_conf(rng, 64, 16)
+    ratios = list(sv.DCUT_RATIOS)
+    j, _ = check_choice(conf, ratios, [64], [[5.0, 5.0, 5.0, 5.0]])
+    assert j == 3                                   # equal latencies: the largest budget
+    z = np.zeros((64, 16), np.float32)
+    j, _ = check_choice(z, ratios, [64], [[4.0, 2.0, 2.0, 3.0]])
+    assert j == 1                                   # equal projections: the first listed
+    j, _ = check_choice(conf, [0.5], [8, 128], [[1.0], [3.0]])   # interpolated, one ratio
+    assert j == 0
+    check_choice(conf[:3, :5].copy(), [0.0, 1.0], [1], [[1.0, 1.5]])
