@@ -165,9 +165,9 @@ size_t sv_draft_confidence_workspace_bytes(sv_dtype dtype, int32_t B, int32_t D_
   if (B < 0 || D_max < 0 || V < 1 || V > INT32_MAX) return 0;
   if (dtype != SV_DTYPE_BF16 && dtype != SV_DTYPE_FP32) return 0;
   const int64_t rows = (int64_t)B * D_max;
-  const int64_t nseg = sv::confidence_segments(dtype, V);
-  if (rows * nseg > (int64_t)INT32_MAX) return 0;
-  const size_t bytes = (size_t)rows * (size_t)nseg * sizeof(float2);
+  const int64_t nstate = sv::confidence_states(dtype, V);  // per row
+  if (rows * nstate > (int64_t)INT32_MAX) return 0;
+  const size_t bytes = (size_t)rows * (size_t)nstate * sizeof(float2);
   return bytes == 0 ? 256 : (bytes + 255) / 256 * 256;
 }
 

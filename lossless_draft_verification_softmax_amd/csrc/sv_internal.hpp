@@ -191,10 +191,11 @@ struct ConfParams {
   const int32_t* depth;    // [B] or null (= D)
   const float* temperature;
   float* conf;             // [B, D]
-  float2* part;            // [B * D][nseg] segment states (workspace)
-  int64_t nseg;
+  float2* part;            // [B * D][nseg][waves] wavefront states (workspace)
+  int64_t nseg;            // segments per row
 };
 int64_t confidence_segments(sv_dtype dtype, int64_t V);
+int64_t confidence_states(sv_dtype dtype, int64_t V);
 hipError_t launch_confidence(const ConfParams& c, hipStream_t stream);
 
 // Keep-ratio choice (sv_budget.hip): the candidate ratios and their

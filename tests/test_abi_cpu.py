@@ -114,7 +114,7 @@ def test_confidence_validation_codes(sv):
     lib = sv.load()
     fake = 1 << 20  # a 256-byte aligned fake device address; nothing is dereferenced
     ws = lib.sv_draft_confidence_workspace_bytes(0, 64, 16, 151936)
-    assert ws == 64 * 16 * 19 * 8  # 19 segments of 8192 bf16 elements, one float2 each
+    assert ws == 64 * 16 * 10 * 4 * 8  # 10 segments of 2048 vectors, a float2 per wavefront
     assert lib.sv_draft_confidence_workspace_bytes(0, 0, 16, 100) == 256
     assert lib.sv_draft_confidence_workspace_bytes(7, 4, 4, 100) == 0
     assert lib.sv_draft_confidence_workspace_bytes(1, 4, 4, 0) == 0
