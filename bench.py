@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -131,6 +132,67 @@ def cpu_baseline(w, target_packed, depth, tr0, dr0, seconds: float):
                        f"positions) of the {w.name} batch, one request per call on "
                        f"{workers} host threads, {elapsed:.1f} s wall; budget "
                        f"{budget_s * 1e3:.2f} ms single-threaded")
+
+
+def draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize):
+    """The budget's inputs, timed apart from the verification step: the
+    drafter confidence q_k(d_k) of every drafted position (one pass over the
+    draft rows, rotating the input copies), and D-cut's keep-ratio choice
+    from a cost table profiled here by timing the verification step at each
+    ratio's budget."""
+    B, D, V = w.B, w.D, w.V
+    dc = sv.DraftConfidence(B, D, V, w.dtype, copies[0][1].device)
+    drafts = [d.reshape(B * D, V) for _, d in copies]
+    for i in range(6):
+        dc(drafts[i % len(drafts)], dr0, w.draft_tokens, w.temperature)
+    torch.cuda.synchronize()
+    n = 40
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        dc(drafts[i % len(drafts)], dr0, w.draft_tokens, w.temperature)
+    e1.record()
+    torch.cuda.synchronize()
+    conf_us = e0.elapsed_time(e1) / n * 1e3
+    conf_bytes = B * D * V * esize
+    conf = dc.conf.clone()
+    # cost table: verification step time at each ratio's K on this batch
+    ratios = list(sv.DCUT_RATIOS)
+    lat = []
+    for rho in ratios:
+        K = math.ceil(rho * B * D)
+        b = sv.allocate_budget(conf, K)
+        for v in verifiers:  # padded target rows: row r (D + 1) + k
+            v.prepare(w.target.reshape(-1, V), w.draft, torch.arange(B, device=conf.device) * (D + 1),
+                      dr0, w.draft_tokens, b["depth"], w.temperature, seed=0, step=0)
+        for i in range(3):
+            verifiers[i % len(verifiers)].run()
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(10):
+            verifiers[i % len(verifiers)].run()
+        e1.record()
+        torch.cuda.synchronize()
+        lat.append(e0.elapsed_time(e1) / 10 * 1e3)
+    for i in range(3):
+        sel = sv.select_budget_ratio(conf, [B], [lat], ratios)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        sel = sv.select_budget_ratio(conf, [B], [lat], ratios)
+    e1.record()
+    torch.cuda.synchronize()
+    sel_us = e0.elapsed_time(e1) / n * 1e3
+    ach = conf_bytes / (conf_us * 1e-6) / 1e9
+    return {
+        "draft_confidence": {"kernels": "k_conf_part + k_conf_final", "us": round(conf_us, 2),
+                             "algorithmic_bytes": conf_bytes, "achieved_GBps": round(ach, 1),
+                             "frac": round(ach / HBM_PEAK_GBS, 4)},
+        "ratio_choice": {"kernel": "k_budget_ratio", "us": round(sel_us, 2),
+                         "ratios": ratios, "verify_us_at_ratio": [round(x, 1) for x in lat],
+                         "projected_tokens_per_us": [round(float(x), 5) for x in sel["projected"].cpu()],
+                         "choice": int(sel["choice"].item()), "K": int(sel["K"].item())},
+    }
 
 
 def main():
@@ -286,6 +348,8 @@ def main():
         "expected_mean_accepted_length": round(float(stats_out["summary"][1]), 4),
         "source_digest": digest,
     }
+    if D > 0 and draft_rows > 0:
+        res["draft_side"] = draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize)
     if args.calib_copy_mb:
         # a plain device copy of known size: scales rocprofv3's byte counters
         # and gives the copy bandwidth for context (read + write bytes / time)
