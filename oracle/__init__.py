@@ -372,3 +372,70 @@ def accept_stats(depth, alpha_mat, accepted_len, D_max: int):
     if st != 0:
         raise ValueError("svo_accept_stats: invalid argument")
     return dict(expected_len=e, per_depth=pd[: 3 * D_max].reshape(3, D_max), summary=sm)
+
+
+# ---- multi-step decoding on a Markov target ---------------------------------
+# The decode loop the pages' eval server runs ([T] "The MTP path": MAL and
+# position-wise acceptance measured over whole generations; [A] "MTP": a
+# block of drafts is verified in one target pass and one rejection
+# invalidates the rest).  Synthetic "models": a first-order Markov chain, so
+# the target row (and the draft row) for a context is the table row of its
+# last token.
+
+def draft_uniform(seed: int, request_id: int, step: int, position: int) -> float:
+    """Uniform for the draft token at `position`: word 2 of the Philox block of
+    counter (position, request_id, step, 0), whose words 0 and 1 feed that
+    position's accept test and draw (reading: the drafter samples on the
+    verifier's stream)."""
+    w = philox([position, request_id, step, 0], [seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF])
+    return u24(int(w[2]))
+
+
+def sample_draft(Q_row, T: float, u: float) -> tuple[int, float]:
+    """The drafter's token: inverse CDF of softmax(Q / T) at u; arg max at T = 0."""
+    if T == 0.0:
+        return argmax(Q_row), float("inf")
+    return sample_target(Q_row, T, u)
+
+
+def markov_decode(P_table, Q_table, start, D: int, temperature, steps: int, seed: int = 0,
+                  request_id=None):
+    """Runs `steps` decode steps for every request: draft D tokens from the
+    draft table (row = previous token), verify them against the target table
+    rows of the same contexts, keep the emitted tokens, continue from the last
+    one.  Returns per-step lists of emitted tokens, accepted lengths, the
+    smallest draft / accept / draw margins met, and the drafts."""
+    P_table = _f32(P_table)
+    Q_table = _f32(Q_table)
+    B = len(start)
+    rid = list(range(B)) if request_id is None else [int(x) for x in request_id]
+    last = [int(t) for t in start]
+    emitted, taus, drafts = [], [], []
+    min_margin = {"draft": float("inf"), "accept": float("inf"), "draw": float("inf")}
+    for step in range(steps):
+        em_s, tau_s, dr_s = [], [], []
+        for r in range(B):
+            T = float(temperature[r])
+            ctx = [last[r]]
+            d = []
+            for k in range(D):
+                y, m = sample_draft(Q_table[ctx[-1]], T, draft_uniform(seed, rid[r], step, k))
+                min_margin["draft"] = min(min_margin["draft"], m)
+                d.append(y)
+                ctx.append(y)
+            ua = [uniforms(seed, rid[r], step, k)[0] for k in range(D)]
+            us = [uniforms(seed, rid[r], step, k)[1] for k in range(D + 1)]
+            tau, out, am, dm, bits = verify_request(P_table[ctx], Q_table[ctx[:D]] if D else None,
+                                                    d, T, ua, us)
+            if bits:
+                raise ValueError(f"invalid request in the decode loop (bits {bits})")
+            min_margin["accept"] = min(min_margin["accept"], am)
+            min_margin["draw"] = min(min_margin["draw"], dm)
+            em_s.append([int(x) for x in out])
+            tau_s.append(int(tau))
+            dr_s.append(d)
+            last[r] = int(out[-1])
+        emitted.append(em_s)
+        taus.append(tau_s)
+        drafts.append(dr_s)
+    return dict(emitted=emitted, tau=taus, drafts=drafts, margins=min_margin)
