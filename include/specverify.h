@@ -284,6 +284,36 @@ sv_status sv_select_budget_ratio(const float* conf, int32_t B, int32_t D_max,
                                  int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
                                  float* utility, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * sv_sample_rows -- one token per request drawn from softmax(row / T) on the
+ * verifier's Philox stream: the drafter's step of the decode loop ("AngelSpec:
+ * specialize the drafter...", section "MTP": the drafter proposes a block that
+ * the target verifies in one pass; tradepoint.io page, "The MTP path":
+ * acceptance measured over whole generations).
+ *
+ * Request r draws from row row_base + row_index[r * index_stride] of logits
+ * (row_stride elements per row; the caller guarantees the row exists) with
+ * u = (w2 >> 8) * 2^-24, w2 word 2 of Philox4x32-10(key = (seed low, seed
+ * high), counter = (position, request_id[r], step, 0)) -- words 0 and 1 of
+ * that block are sv_verify_batch's accept and draw uniforms at the same
+ * position.  The token is the smallest y whose cumulative weight exceeds
+ * u * R, weights exp((x - max) / T) in float64 and R their sum; at T = 0 the
+ * first arg max.  tokens[r * token_stride] receives it, or -1 when
+ * row_index is negative, the temperature is negative, NaN or infinite, or
+ * the row holds a NaN or +inf or only -inf.  Strides let successive calls
+ * chain a drafter: call k reads the tokens call k - 1 wrote.
+ *
+ * Device arrays owned by the caller: row_index, temperature, request_id
+ * (NULL: r), tokens.  Errors: SV_ERR_UNSUPPORTED (dtype),
+ * SV_ERR_INVALID_ARGUMENT (sizes, strides, null pointers) before any launch;
+ * SV_ERR_DEVICE if the launch fails.  One workgroup per request.
+ * ------------------------------------------------------------------------- */
+sv_status sv_sample_rows(sv_dtype dtype, int32_t B, int64_t V, int64_t row_stride,
+                         const void* logits, int64_t row_base, const int32_t* row_index,
+                         int64_t index_stride, const float* temperature,
+                         const uint32_t* request_id, uint64_t seed, uint32_t step,
+                         uint32_t position, int32_t* tokens, int64_t token_stride, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -256,6 +256,38 @@ sv_status sv_select_budget_ratio(const float* conf, int32_t B, int32_t D_max,
   return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
+sv_status sv_sample_rows(sv_dtype dtype, int32_t B, int64_t V, int64_t row_stride,
+                         const void* logits, int64_t row_base, const int32_t* row_index,
+                         int64_t index_stride, const float* temperature,
+                         const uint32_t* request_id, uint64_t seed, uint32_t step,
+                         uint32_t position, int32_t* tokens, int64_t token_stride, void* stream) {
+  if (dtype != SV_DTYPE_BF16 && dtype != SV_DTYPE_FP32) return SV_ERR_UNSUPPORTED;
+  if (B < 0 || V < 1 || V > INT32_MAX || row_stride < V || row_base < 0 || index_stride < 0 ||
+      token_stride < 1)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SV_OK;
+  if (!logits || !row_index || !temperature || !tokens) return SV_ERR_INVALID_ARGUMENT;
+  sv::SampleParams p{};
+  p.dtype = dtype;
+  p.B = B;
+  p.V = V;
+  p.stride = row_stride;
+  p.logits = logits;
+  p.row_base = row_base;
+  p.row_index = row_index;
+  p.index_stride = index_stride;
+  p.temperature = temperature;
+  p.request_id = request_id;
+  p.seed_lo = (uint32_t)(seed & 0xffffffffull);
+  p.seed_hi = (uint32_t)(seed >> 32);
+  p.step = step;
+  p.position = position;
+  p.tokens = tokens;
+  p.token_stride = token_stride;
+  const hipError_t e = sv::launch_sample(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
 sv_status sv_accept_stats(const int32_t* depth, const float* alpha, const int32_t* accepted_len,
                           int32_t B, int32_t D_max, float* expected_len, float* per_depth,
                           float* summary, void* stream) {

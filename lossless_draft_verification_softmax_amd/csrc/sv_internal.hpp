@@ -211,4 +211,21 @@ hipError_t launch_budget_ratio(const float* conf, int32_t B, int32_t D, const in
                                float* projected, int32_t* depth, int64_t* draft_row0,
                                int64_t* target_row0, float* utility, hipStream_t stream);
 
+// Token sampler (sv_sample.hip).
+struct SampleParams {
+  sv_dtype dtype;
+  int32_t B;
+  int64_t V, stride;
+  const void* logits;
+  int64_t row_base;
+  const int32_t* row_index;  // row of request r: row_base + row_index[r * index_stride]
+  int64_t index_stride;
+  const float* temperature;
+  const uint32_t* request_id;  // or null: r
+  uint32_t seed_lo, seed_hi, step, position;
+  int32_t* tokens;             // token of request r at tokens[r * token_stride]
+  int64_t token_stride;
+};
+hipError_t launch_sample(const SampleParams& p, hipStream_t stream);
+
 }  // namespace sv

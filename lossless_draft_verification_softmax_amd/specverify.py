@@ -41,7 +41,8 @@ BIT_SYNC_TIMEOUT = 64
 
 EXPORTS = ["sv_status_string", "sv_version", "sv_k_rho", "sv_allocate_budget",
            "sv_verify_workspace_bytes", "sv_verify_batch", "sv_accept_stats",
-           "sv_draft_confidence_workspace_bytes", "sv_draft_confidence", "sv_select_budget_ratio"]
+           "sv_draft_confidence_workspace_bytes", "sv_draft_confidence", "sv_select_budget_ratio",
+           "sv_sample_rows"]
 MAX_RATIOS = 8
 DCUT_RATIOS = (0.25, 0.5, 0.75, 1.0)
 
@@ -113,6 +114,10 @@ def load() -> ctypes.CDLL:
                                          ctypes.POINTER(ctypes.c_float), vp, vp, vp, vp, vp, vp,
                                          vp, vp]
     L.sv_select_budget_ratio.restype = ctypes.c_int
+    L.sv_sample_rows.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, vp,
+                                 ctypes.c_int64, vp, ctypes.c_int64, vp, vp, ctypes.c_uint64,
+                                 ctypes.c_uint32, ctypes.c_uint32, vp, ctypes.c_int64, vp]
+    L.sv_sample_rows.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -251,6 +256,27 @@ def select_budget_ratio(conf: torch.Tensor, table_batch, table_latency, ratios=D
                                        _stream(dev))
     _check(st, "sv_select_budget_ratio")
     return out
+
+
+def sample_rows(logits: torch.Tensor, row_index: torch.Tensor, temperature: torch.Tensor,
+                tokens: torch.Tensor, *, seed: int = 0, step: int = 0, position: int = 0,
+                request_id: torch.Tensor | None = None, row_base: int = 0) -> torch.Tensor:
+    """One token per request from softmax(row / T) on the verifier's Philox
+    stream (sv_sample_rows).  row_index and tokens are int32 device tensors of
+    B entries (any stride: a column of a (B, D) matrix works); logits is
+    (rows, V) with contiguous rows."""
+    rows, stride = _rows_view(logits)
+    B = tokens.shape[0]
+    assert row_index.dtype == torch.int32 and tokens.dtype == torch.int32
+    assert row_index.shape[0] == B and temperature.shape[0] == B
+    T = temperature.to(dtype=torch.float32).contiguous()
+    rid = None if request_id is None else request_id.to(dtype=torch.int32).contiguous()
+    st = load().sv_sample_rows(_dtype_code(rows.dtype), B, rows.shape[-1], stride, _ptr(rows),
+                               int(row_base), _ptr(row_index), row_index.stride(0), _ptr(T),
+                               _ptr(rid), int(seed), int(step), int(position), _ptr(tokens),
+                               tokens.stride(0), _stream(rows.device))
+    _check(st, "sv_sample_rows")
+    return tokens
 
 
 @dataclass

@@ -404,25 +404,28 @@ def markov_decode(P_table, Q_table, start, D: int, temperature, steps: int, seed
     draft table (row = previous token), verify them against the target table
     rows of the same contexts, keep the emitted tokens, continue from the last
     one.  Returns per-step lists of emitted tokens, accepted lengths, the
-    smallest draft / accept / draw margins met, and the drafts."""
+    drafts and each request's (draft, accept, draw) margins, and the smallest
+    margins met."""
     P_table = _f32(P_table)
     Q_table = _f32(Q_table)
     B = len(start)
     rid = list(range(B)) if request_id is None else [int(x) for x in request_id]
     last = [int(t) for t in start]
-    emitted, taus, drafts = [], [], []
+    emitted, taus, drafts, step_margins = [], [], [], []
     min_margin = {"draft": float("inf"), "accept": float("inf"), "draw": float("inf")}
     for step in range(steps):
-        em_s, tau_s, dr_s = [], [], []
+        em_s, tau_s, dr_s, mg_s = [], [], [], []
         for r in range(B):
             T = float(temperature[r])
             ctx = [last[r]]
             d = []
+            dmin = float("inf")
             for k in range(D):
                 y, m = sample_draft(Q_table[ctx[-1]], T, draft_uniform(seed, rid[r], step, k))
-                min_margin["draft"] = min(min_margin["draft"], m)
+                dmin = min(dmin, m)
                 d.append(y)
                 ctx.append(y)
+            min_margin["draft"] = min(min_margin["draft"], dmin)
             ua = [uniforms(seed, rid[r], step, k)[0] for k in range(D)]
             us = [uniforms(seed, rid[r], step, k)[1] for k in range(D + 1)]
             tau, out, am, dm, bits = verify_request(P_table[ctx], Q_table[ctx[:D]] if D else None,
@@ -434,8 +437,11 @@ def markov_decode(P_table, Q_table, start, D: int, temperature, steps: int, seed
             em_s.append([int(x) for x in out])
             tau_s.append(int(tau))
             dr_s.append(d)
+            mg_s.append((dmin, am, dm))
             last[r] = int(out[-1])
         emitted.append(em_s)
         taus.append(tau_s)
         drafts.append(dr_s)
-    return dict(emitted=emitted, tau=taus, drafts=drafts, margins=min_margin)
+        step_margins.append(mg_s)
+    return dict(emitted=emitted, tau=taus, drafts=drafts, margins=min_margin,
+                step_margins=step_margins)

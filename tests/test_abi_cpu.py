@@ -161,3 +161,25 @@ def test_ratio_validation_codes(sv):
     assert call(tl=(1.0, float("inf"))) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(choice=None) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(conf=None) == sv.SV_ERR_INVALID_ARGUMENT
+
+
+def test_sample_validation_codes(sv):
+    lib = sv.load()
+    fake = 1 << 20
+
+    def call(dtype=0, B=4, V=100, stride=100, logits=fake, base=0, idx=fake, istride=1, T=fake,
+             tok=fake, tstride=1):
+        return lib.sv_sample_rows(dtype, B, V, stride, logits, base, idx, istride, T, None, 0, 0,
+                                  0, tok, tstride, None)
+
+    assert call(dtype=3) == sv.SV_ERR_UNSUPPORTED
+    assert call(B=0) == sv.SV_OK
+    assert call(B=-1) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(V=0) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(stride=99) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(base=-1) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(istride=-1) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(tstride=0) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(logits=None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(idx=None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(tok=None) == sv.SV_ERR_INVALID_ARGUMENT
