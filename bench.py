@@ -195,6 +195,38 @@ def draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize):
     }
 
 
+def decode_loop_figure(sv, torch, dev, V=32768, B=64, D=8, steps=30):
+    """The multi-step decode loop on a synthetic Markov target (bf16 tables of
+    V x V, target P ~ 3 N(0, 1), drafter Q = P + N(0, 1), T = 1): time per
+    step (D sampler calls, row gather, verification, statistics), emitted
+    tokens per second, MAL and position-wise acceptance."""
+    from lossless_draft_verification_softmax_amd.decode_loop import MarkovDecodeLoop
+    g = torch.Generator(device=dev)
+    g.manual_seed(4000)
+    P = (3.0 * torch.randn((V, V), generator=g, device=dev)).to(torch.bfloat16)
+    Q = (P.float() + torch.randn((V, V), generator=g, device=dev)).to(torch.bfloat16)
+    start = torch.randint(0, V, (B,), generator=g, device=dev, dtype=torch.int64).to(torch.int32)
+    loop = MarkovDecodeLoop(P, Q, start, D, torch.ones(B, device=dev), seed=0)
+    for _ in range(3):
+        loop.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    emitted = torch.zeros((), dtype=torch.int64, device=dev)
+    e0.record()
+    for _ in range(steps):
+        out = loop.step()
+        emitted += out.accepted_len.sum() + B
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    summ = loop.summary()
+    del P, Q
+    return {"workload": f"Markov target V={V} bf16, B={B}, D={D}, T=1", "us_per_step": round(us, 1),
+            "emitted_tokens_per_s": round(float(emitted.item()) / (us * steps * 1e-6), 1),
+            "mal": round(summ["mal"], 4), "expected_mal": round(summ["expected_mal"], 4),
+            "position_acceptance": [round(x, 4) for x in summ["position_acceptance"]]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -350,6 +382,7 @@ def main():
     }
     if D > 0 and draft_rows > 0:
         res["draft_side"] = draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize)
+        res["decode_loop"] = decode_loop_figure(sv, torch, dev)
     if args.calib_copy_mb:
         # a plain device copy of known size: scales rocprofv3's byte counters
         # and gives the copy bandwidth for context (read + write bytes / time)
