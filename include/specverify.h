@@ -55,6 +55,8 @@ typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
 #define SV_MAX_DEPTH 64
 /* Largest B * D_max the single-workgroup budget sort accepts. */
 #define SV_MAX_BUDGET_POSITIONS 4096
+/* Most vocabulary shards of sv_verify_batch_sharded. */
+#define SV_MAX_SHARDS 16
 
 /* Number of stage events sv_verify_batch records when asked to. */
 #define SV_NUM_STAGE_EVENTS 5
@@ -195,6 +197,31 @@ typedef struct sv_verify_args {
    * An entry may be NULL (not recorded).  For timing only. */
   void* const* stage_events;
 } sv_verify_args;
+
+/* ---------------------------------------------------------------------------
+ * sv_verify_batch_sharded -- the same verification with the vocabulary split
+ * over n_shards buffers, as a tensor-parallel target leaves its logits (the
+ * pages' target runs with TP = 8: "AngelSpec: specialize the drafter...",
+ * section "The numbers"); here every shard sits on the one GPU.
+ *
+ * Shard s holds columns [s * shard_width, min(V, (s + 1) * shard_width)) of
+ * every target row in target_shards[s] and of every draft row in
+ * draft_shards[s] (NULL array: no draft logits, as draft_logits = NULL),
+ * all with row stride args->row_stride (>= shard_width).  n_shards must equal
+ * ceil(V / shard_width), 1 <= n_shards <= SV_MAX_SHARDS, shard_width a
+ * multiple of 8 elements, every shard pointer 16-byte aligned.
+ * args->target_logits and args->draft_logits are ignored; everything else,
+ * the outputs and the workspace are as for sv_verify_batch, and so are the
+ * results: the method is that of the concatenated rows.  The team row pass
+ * tiles each shard with its own members, so the row normalisers are the
+ * associative (max, sum) merge of per-shard states and sum min(p, q) a sum of
+ * per-shard sums; the draw scans tile masses in column order across shards.
+ * SV_ERR_UNSUPPORTED when a shard needs more team members than fit (no
+ * streaming fallback here) or for a shard width that is not a multiple of 8.
+ * ------------------------------------------------------------------------- */
+sv_status sv_verify_batch_sharded(const sv_verify_args* args, int32_t n_shards,
+                                  int64_t shard_width, const void* const* target_shards,
+                                  const void* const* draft_shards, void* stream);
 
 /* Device scratch needed by sv_verify_batch for these sizes (0 on bad sizes). */
 size_t sv_verify_workspace_bytes(int32_t B, int32_t D_max, int64_t V);

@@ -32,10 +32,11 @@ int device_cu_count() {
   return cus;
 }
 
-sv_status validate_verify(const sv_verify_args* a, size_t* need) {
+// row_width: the elements of a row held by one buffer (V, or the shard width).
+sv_status validate_verify(const sv_verify_args* a, int64_t row_width, size_t* need) {
   if (!a) return SV_ERR_INVALID_ARGUMENT;
   if (a->B < 0 || a->D_max < 0 || a->D_max > SV_MAX_DEPTH) return SV_ERR_INVALID_ARGUMENT;
-  if (a->V < 1 || a->V > INT32_MAX || a->row_stride < a->V) return SV_ERR_INVALID_ARGUMENT;
+  if (a->V < 1 || a->V > INT32_MAX || a->row_stride < row_width) return SV_ERR_INVALID_ARGUMENT;
   if (a->dtype != SV_DTYPE_BF16 && a->dtype != SV_DTYPE_FP32) return SV_ERR_UNSUPPORTED;
   if (a->flags & ~(SV_FLAG_FORCE_FP64_DRAW | SV_FLAG_STREAMING_ROW_PASS | SV_FLAG_EXACT_FP64_MASSES))
     return SV_ERR_UNSUPPORTED;
@@ -89,12 +90,19 @@ size_t sv_verify_workspace_bytes(int32_t B, int32_t D_max, int64_t V) {
   return sv::workspace_layout(B, D_max, V).total;
 }
 
-sv_status sv_verify_batch(const sv_verify_args* a, void* stream) {
-  size_t need = 0;
-  const sv_status st = validate_verify(a, &need);
-  if (st != SV_OK) return st;
-  if (a->B == 0) return SV_OK;
+}  // extern "C"
+
+namespace {
+
+sv_status run_verify(const sv_verify_args* a, int32_t nshard, int64_t shard_w,
+                     const void* const* tsh, const void* const* dsh, void* stream) {
   sv::VerifyParams p{};
+  p.nshard = nshard;
+  p.shard_w = shard_w;
+  for (int32_t s = 0; s < nshard && nshard > 1; ++s) {
+    p.tsh[s] = tsh[s];
+    p.dsh[s] = dsh ? dsh[s] : nullptr;
+  }
   p.dtype = a->dtype;
   p.B = a->B;
   p.D = a->D_max;
@@ -141,10 +149,54 @@ sv_status sv_verify_batch(const sv_verify_args* a, void* stream) {
   p.plan_counts = reinterpret_cast<int32_t*>(ws + L.plan_counts);
   p.team_xch = reinterpret_cast<uint64_t*>(ws + L.team_xch);
   p.sync_error = reinterpret_cast<int32_t*>(ws + L.sync_error);
+  p.shard_tab = reinterpret_cast<const void**>(ws + L.shard_tab);
   const int grid = device_cu_count();
   if (grid <= 0) return SV_ERR_DEVICE;
+  if (nshard > 1) {  // the sharded path has no streaming fallback
+    int32_t T, per, nv, slice;
+    if (grid > sv::kMaxTeamGrid ||
+        !sv::team_geometry_sharded(p.dtype, nshard, shard_w, grid, &T, &per, &nv, &slice))
+      return SV_ERR_UNSUPPORTED;
+  }
   const hipError_t e = sv::launch_verify(p, grid, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status sv_verify_batch(const sv_verify_args* a, void* stream) {
+  size_t need = 0;
+  const sv_status st = validate_verify(a, a ? a->V : 0, &need);
+  if (st != SV_OK) return st;
+  if (a->B == 0) return SV_OK;
+  return run_verify(a, 1, a->V, nullptr, nullptr, stream);
+}
+
+sv_status sv_verify_batch_sharded(const sv_verify_args* a, int32_t n_shards, int64_t shard_width,
+                                  const void* const* target_shards,
+                                  const void* const* draft_shards, void* stream) {
+  if (!a || !target_shards || n_shards < 1 || n_shards > SV_MAX_SHARDS)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (shard_width < 8 || shard_width % 8 != 0) return SV_ERR_UNSUPPORTED;
+  if (a->V < 1 || (a->V + shard_width - 1) / shard_width != n_shards)
+    return SV_ERR_INVALID_ARGUMENT;
+  for (int32_t s = 0; s < n_shards; ++s) {
+    if (!target_shards[s] || !aligned16(target_shards[s])) return SV_ERR_INVALID_ARGUMENT;
+    if (draft_shards && (!draft_shards[s] || !aligned16(draft_shards[s])))
+      return SV_ERR_INVALID_ARGUMENT;
+  }
+  sv_verify_args b = *a;
+  b.target_logits = target_shards[0];
+  b.draft_logits = draft_shards ? draft_shards[0] : nullptr;
+  if ((b.draft_logits == nullptr) != (b.draft_row0 == nullptr)) return SV_ERR_INVALID_ARGUMENT;
+  size_t need = 0;
+  const sv_status st = validate_verify(&b, n_shards > 1 ? shard_width : a->V, &need);
+  if (st != SV_OK) return st;
+  if (b.B == 0) return SV_OK;
+  if (n_shards == 1) return run_verify(&b, 1, b.V, nullptr, nullptr, stream);
+  return run_verify(&b, n_shards, shard_width, target_shards, draft_shards, stream);
 }
 
 sv_status sv_allocate_budget(const float* conf, int32_t B, int32_t D_max,

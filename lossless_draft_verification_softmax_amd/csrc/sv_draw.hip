@@ -27,6 +27,7 @@
 #include "specverify.h"
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
+#include "sv_shard.hpp"
 
 namespace sv {
 
@@ -35,18 +36,20 @@ constexpr int kPer = 8;  // elements per thread per tile
 constexpr float kDrawMargin32 = 1e-5f;
 constexpr int kQueueGrid = 2048;
 
-// Eight consecutive logits starting at i0 (< hi); entries at or past hi read
-// as -inf, which gives them weight 0.
-template <typename E>
-__device__ __forceinline__ void load8(const typename E::Storage* row, int64_t i0, int64_t hi,
+// Eight consecutive logits starting at i0 (< hi, a multiple of 8); entries at
+// or past hi read as -inf, which gives them weight 0.  The eight never cross a
+// vocabulary shard.
+template <typename E, bool SH>
+__device__ __forceinline__ void load8(const RowView<E, SH>& row, int64_t i0, int64_t hi,
                                       float (&x)[kPer]) {
   if (i0 + kPer <= hi) {
+    const typename E::Storage* g = row.at(i0);
     if constexpr (E::kPerVec == 8) {
-      E::unpack(load16(row + i0), x);
+      E::unpack(load16(g), x);
     } else {
       float a[4], b[4];
-      E::unpack(load16(row + i0), a);
-      E::unpack(load16(row + i0 + 4), b);
+      E::unpack(load16(g), a);
+      E::unpack(load16(g + 4), b);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         x[j] = a[j];
@@ -55,7 +58,7 @@ __device__ __forceinline__ void load8(const typename E::Storage* row, int64_t i0
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) x[j] = (i0 + j < hi) ? E::load1(row, i0 + j) : -INFINITY;
+    for (int j = 0; j < kPer; ++j) x[j] = (i0 + j < hi) ? E::load1(row.at(i0 + j), 0) : -INFINITY;
   }
 }
 
@@ -118,21 +121,21 @@ __device__ __forceinline__ T block_sum256(T v, T* lds) {
 
 // ---------------------------------------------------------------------------
 // Weights.
-template <typename E>
+template <typename E, bool SH>
 struct Weights32 {
-  const typename E::Storage* prow;
-  const typename E::Storage* qrow;  // null: bonus draw (w = p)
+  RowView<E, SH> prow, qrow;
+  bool has_q;  // false: bonus draw (w = p)
   float sl, mp, lzp, mq, lzq;
   __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, float (&w)[kPer]) const {
     float a[kPer];
-    load8<E>(prow, i0, hi, a);
-    if (!qrow) {
+    load8<E, SH>(prow, i0, hi, a);
+    if (!has_q) {
 #pragma unroll
       for (int j = 0; j < kPer; ++j) w[j] = exp2_fast(__builtin_fmaf(a[j] - mp, sl, -lzp));
       return;
     }
     float b[kPer];
-    load8<E>(qrow, i0, hi, b);
+    load8<E, SH>(qrow, i0, hi, b);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const float pv = exp2_fast(__builtin_fmaf(a[j] - mp, sl, -lzp));
@@ -142,13 +145,12 @@ struct Weights32 {
   }
 };
 
-template <typename E>
-__device__ __forceinline__ Weights32<E> weights32(const VerifyParams& p, const DrawState& st) {
-  Weights32<E> w;
-  w.prow = static_cast<const typename E::Storage*>(p.target) + st.prow * p.stride;
-  w.qrow = (st.mode == kDrawResidual)
-               ? static_cast<const typename E::Storage*>(p.draft) + st.qrow * p.stride
-               : nullptr;
+template <typename E, bool SH>
+__device__ __forceinline__ Weights32<E, SH> weights32(const VerifyParams& p, const DrawState& st) {
+  Weights32<E, SH> w;
+  w.has_q = st.mode == kDrawResidual;
+  w.prow = row_view<E, SH>(p, false, st.prow);
+  w.qrow = row_view<E, SH>(p, true, w.has_q ? st.qrow : 0);
   w.sl = st.sl;
   w.mp = st.mp;
   w.lzp = st.lzp;
@@ -161,23 +163,23 @@ __device__ __forceinline__ Weights32<E> weights32(const VerifyParams& p, const D
 // float64 reciprocal of T (one extra rounding, about 1e-16 relative, where a
 // division would cost ten float64 operations per element); the normalisers
 // are float64 sums of exp((x - max) / T).
-template <typename E>
+template <typename E, bool SH>
 struct Weights64 {
-  const typename E::Storage* prow;
-  const typename E::Storage* qrow;
+  RowView<E, SH> prow, qrow;
+  bool has_q;
   double invT, mp, mq, lnzp, lnzq;
   bool unnormalised;  // w = exp((x - mp) / T): residual mass was zero
   __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, double (&w)[kPer]) const {
     float a[kPer];
-    load8<E>(prow, i0, hi, a);
-    if (unnormalised || !qrow) {
+    load8<E, SH>(prow, i0, hi, a);
+    if (unnormalised || !has_q) {
       const double off = unnormalised ? 0.0 : lnzp;
 #pragma unroll
       for (int j = 0; j < kPer; ++j) w[j] = exp(((double)a[j] - mp) * invT - off);
       return;
     }
     float b[kPer];
-    load8<E>(qrow, i0, hi, b);
+    load8<E, SH>(qrow, i0, hi, b);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const double pv = exp(((double)a[j] - mp) * invT - lnzp);
@@ -338,26 +340,26 @@ __device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W&
 }
 
 // ---------------------------------------------------------------------------
-template <typename E>
+template <typename E, bool SH>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_mass32(VerifyParams p) {
   __shared__ float lds[kDrawThreads / kWave];
   const int r = blockIdx.y;
   const DrawState st = p.req[r];
   if (st.mode == kDrawNone) return;
-  const Weights32<E> w = weights32<E>(p, st);
+  const Weights32<E, SH> w = weights32<E, SH>(p, st);
   for (int64_t tile = blockIdx.x; tile < p.S2; tile += gridDim.x) {
     const float m = tile_mass<float>(w, tile, p.V, lds);
     if (threadIdx.x == 0) p.seg_w32[(int64_t)r * p.S2 + tile] = m;
   }
 }
 
-template <typename E>
+template <typename E, bool SH>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_pick32(VerifyParams p) {
   __shared__ PickLds<float> L;
   const int r = blockIdx.x;
   const DrawState st = p.req[r];
   if (st.mode == kDrawNone) return;
-  const Weights32<E> w = weights32<E>(p, st);
+  const Weights32<E, SH> w = weights32<E, SH>(p, st);
   PickResult res{-1, 0.0, 0.0, 0};
   const bool force64 = (p.flags & SV_FLAG_FORCE_FP64_DRAW) != 0u;
   if (!force64) res = pick<float>(p.seg_w32 + (int64_t)r * p.S2, p.S2, p.V, st.u, w, L);
@@ -373,14 +375,13 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick32(VerifyParams p) {
   }
 }
 
-template <typename E>
-__device__ __forceinline__ Weights64<E> weights64(const VerifyParams& p, const DrawState& st,
+template <typename E, bool SH>
+__device__ __forceinline__ Weights64<E, SH> weights64(const VerifyParams& p, const DrawState& st,
                                                   bool unnormalised) {
-  Weights64<E> w;
-  w.prow = static_cast<const typename E::Storage*>(p.target) + st.prow * p.stride;
-  w.qrow = (st.mode == kDrawResidual && !unnormalised)
-               ? static_cast<const typename E::Storage*>(p.draft) + st.qrow * p.stride
-               : nullptr;
+  Weights64<E, SH> w;
+  w.has_q = st.mode == kDrawResidual && !unnormalised;
+  w.prow = row_view<E, SH>(p, false, st.prow);
+  w.qrow = row_view<E, SH>(p, true, w.has_q ? st.qrow : 0);
   w.invT = 1.0 / (double)st.T;
   w.mp = st.mp;
   w.mq = st.mq;
@@ -408,7 +409,7 @@ __device__ __forceinline__ Weights64<E> weights64(const VerifyParams& p, const D
 // recomputed directly.
 constexpr double kTau64 = 1e-4;
 
-template <typename E>
+template <typename E, bool SH>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
   __shared__ double lds[kDrawThreads / kWave][5];
   __shared__ int32_t ldsu[kDrawThreads / kWave];
@@ -424,9 +425,8 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
     const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
     const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
     float a[kPer], b[kPer];
-    load8<E>(static_cast<const typename E::Storage*>(p.target) + st.prow * p.stride, i0, hi, a);
-    if (residual)
-      load8<E>(static_cast<const typename E::Storage*>(p.draft) + st.qrow * p.stride, i0, hi, b);
+    load8<E, SH>(row_view<E, SH>(p, false, st.prow), i0, hi, a);
+    if (residual) load8<E, SH>(row_view<E, SH>(p, true, st.qrow), i0, hi, b);
     double zp = 0.0, zq = 0.0, D = 0.0, A = 0.0, S = 0.0;
     double kep[kPer], keq[kPer];
     int32_t U = 0;
@@ -534,7 +534,7 @@ __device__ __forceinline__ void merge_z64(const double* pp, const double* pq, in
   __syncthreads();
 }
 
-template <typename E>
+template <typename E, bool SH>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   __shared__ PickLds<double> L;
   __shared__ double lds[kDrawThreads / kWave];
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   merge_z64(p.seg_zp64 + (int64_t)r * p.S2, residual ? p.seg_zq64 + (int64_t)r * p.S2 : nullptr,
             p.S2, lds2, Zp, Zq);
   if (!residual) Zq = 1.0;
-  Weights64<E> w = weights64<E>(p, st, false);
+  Weights64<E, SH> w = weights64<E, SH>(p, st, false);
   w.lnzp = log(Zp);
   w.lnzq = log(Zq);
   // Tile masses: from the one-pass split where it is certain, else directly.
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   PickResult res = pick<double>(masses, p.S2, p.V, (double)st.u, w, L);
   const bool unnorm = !(res.R > 0.0);
   if (unnorm) {
-    const Weights64<E> wu = weights64<E>(p, st, true);
+    const Weights64<E, SH> wu = weights64<E, SH>(p, st, true);
     res = pick<double>(p.seg_zp64 + (int64_t)r * p.S2, p.S2, p.V, (double)st.u, wu, L);
   }
   if (!res.found) {
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
     __shared__ unsigned long long s_last1;
     if (threadIdx.x == 0) s_last1 = 0ull;
     __syncthreads();
-    const Weights64<E> wl = unnorm ? weights64<E>(p, st, true) : w;
+    const Weights64<E, SH> wl = unnorm ? weights64<E, SH>(p, st, true) : w;
     for (int64_t tile = 0; tile < p.S2; ++tile) {
       const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
       const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
@@ -630,18 +630,24 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   }
 }
 
-template <typename E>
+template <typename E, bool SH>
 static void launch_draw_t(const VerifyParams& p, hipStream_t stream) {
   const unsigned gx = (unsigned)(p.S2 < 1024 ? p.S2 : 1024);
-  hipLaunchKernelGGL(k_draw_mass32<E>, dim3(gx, (unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
-  hipLaunchKernelGGL(k_draw_pick32<E>, dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
-  hipLaunchKernelGGL(k_draw_tile64<E>, dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
-  hipLaunchKernelGGL(k_draw_pick64<E>, dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL((k_draw_mass32<E, SH>), dim3(gx, (unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL((k_draw_pick32<E, SH>), dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL((k_draw_tile64<E, SH>), dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL((k_draw_pick64<E, SH>), dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
 }
 
 void launch_draw(const VerifyParams& p, hipStream_t stream) {
-  if (p.dtype == SV_DTYPE_BF16) launch_draw_t<Bf16>(p, stream);
-  else launch_draw_t<F32>(p, stream);
+  const bool sh = p.nshard > 1;
+  if (p.dtype == SV_DTYPE_BF16) {
+    if (sh) launch_draw_t<Bf16, true>(p, stream);
+    else launch_draw_t<Bf16, false>(p, stream);
+  } else {
+    if (sh) launch_draw_t<F32, true>(p, stream);
+    else launch_draw_t<F32, false>(p, stream);
+  }
 }
 
 }  // namespace sv

@@ -17,6 +17,7 @@ constexpr int kDrawTile = 2048;
 // float64 draw: uncertain-sign elements kept per tile (more: the tile is
 // recomputed directly)
 constexpr int kDrawKeep64 = 16;
+constexpr int kMaxShards = SV_MAX_SHARDS;
 // Largest grid of the team row pass, and most members per row.
 constexpr int kMaxTeamGrid = 1024;
 constexpr int kMaxTeam = 64;
@@ -66,6 +67,16 @@ struct VerifyParams {
   uint32_t seed_lo, seed_hi, step, flags;
   const void* target;
   const void* draft;
+  // Vocabulary shards (sv_verify_batch_sharded): nshard > 1 buffers, shard s
+  // holding columns [s W, min(V, (s + 1) W)) of every row at row stride
+  // `stride`; target / draft then hold shard 0 (null draft: no draft
+  // shards) and the kernels read the shard pointers from shard_tab (target
+  // shards, then draft shards), written by k_plan.
+  int32_t nshard;
+  int32_t team_per_shard;  // team row pass: members per shard
+  int64_t shard_w;
+  const void* tsh[kMaxShards];
+  const void* dsh[kMaxShards];
   const int64_t* target_row0;
   const int64_t* draft_row0;
   const int32_t* tokens;
@@ -98,6 +109,7 @@ struct VerifyParams {
   int32_t* plan_counts;    // [2]
   uint64_t* team_xch;      // [kMaxTeamGrid * 4][4] tagged slice states exchanged in a team
   int32_t* sync_error;     // set if a team wait expired
+  const void** shard_tab;  // [2 * kMaxShards] shard pointers (written by k_plan)
 };
 
 // ---- launch geometry (host) -------------------------------------------------
@@ -130,7 +142,7 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct WorkspaceLayout {
   size_t part_p, part_q, part_a, req, seg_w32, seg_zp64, seg_zq64, seg_w64, seg_a64, seg_t64, seg_u32, seg_e64,
       fb_count, fb_list,
-      plan_pairs, plan_singles, plan_counts, team_xch, sync_error, total;
+      plan_pairs, plan_singles, plan_counts, team_xch, shard_tab, sync_error, total;
   int32_t slots;
 };
 
@@ -161,6 +173,7 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
   L.plan_singles = off; off += align256(U * sizeof(PlanItem));
   L.plan_counts = off; off += align256(2 * sizeof(int32_t));
   L.team_xch = off; off += align256((size_t)kTeamXchWords * sizeof(uint64_t));
+  L.shard_tab = off; off += align256(2 * kMaxShards * sizeof(void*));
   L.sync_error = off; off += align256(sizeof(int32_t));
   L.total = off;
   return L;
@@ -169,6 +182,8 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
 hipError_t launch_verify(VerifyParams& p, int grid, hipStream_t stream);
 bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
                    int32_t* slice_len);
+bool team_geometry_sharded(sv_dtype dtype, int32_t nshard, int64_t W, int grid, int32_t* T,
+                           int32_t* per_shard, int32_t* NV, int32_t* slice_len);
 hipError_t launch_rowteam(VerifyParams& p, int grid, int nv, hipStream_t stream);
 void launch_plan(const VerifyParams& p, hipStream_t stream);
 void launch_rowpass(const VerifyParams& p, int grid, hipStream_t stream);

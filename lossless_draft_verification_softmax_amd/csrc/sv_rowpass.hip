@@ -94,6 +94,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
     p.plan_counts[1] = carry_singles;
     *p.sync_error = 0;
   }
+  if (p.nshard > 1 && threadIdx.x < 2 * kMaxShards) {
+    const int s = (int)threadIdx.x % kMaxShards;
+    p.shard_tab[threadIdx.x] = (int)threadIdx.x < kMaxShards ? p.tsh[s] : p.dsh[s];
+  }
   // The team row pass tells fresh exchange words from stale ones by their tag
   // (never 0 once written): clear them before every launch.
   uint4* xch = reinterpret_cast<uint4*>(p.team_xch);

@@ -81,18 +81,37 @@ struct UnitDesc {
   int32_t ordinal;  // pair ordinal within the team
 };
 
-// The workgroup's slice of every row it works on: elements [lo, hi), of
-// which [lo, vhi) are nvec whole 16-byte vectors.
+// The workgroup's slice of every row it works on: elements [lo, hi) of the
+// buffers tgt / dft, of which [lo, vhi) are nvec whole 16-byte vectors;
+// element i is column i + off of the full row.  Without vocabulary shards
+// the buffers are the row buffers and off = 0; with shards, member m works
+// in shard m / team_per_shard (the team's members tile each shard, so no
+// slice crosses one) and the buffers are that shard's.
 struct Slice {
-  int64_t lo, vhi, hi, nvec;
+  int64_t lo, vhi, hi, nvec, off;
+  const void* tgt;
+  const void* dft;
 };
 
-template <typename E>
+template <typename E, bool SH>
 __device__ __forceinline__ Slice make_slice(const VerifyParams& p, int member) {
   constexpr int VEC = E::kPerVec;
   Slice sc;
-  sc.lo = (int64_t)member * p.team_len;
-  sc.hi = min(p.V, sc.lo + (int64_t)p.team_len);
+  int64_t width = p.V;
+  int j = member;
+  sc.off = 0;
+  sc.tgt = p.target;
+  sc.dft = p.draft;
+  if constexpr (SH) {
+    const int s = member / p.team_per_shard;
+    j = member % p.team_per_shard;
+    sc.off = (int64_t)s * p.shard_w;
+    width = min(p.shard_w, p.V - sc.off);
+    sc.tgt = p.shard_tab[s];
+    sc.dft = p.shard_tab[kMaxShards + s];
+  }
+  sc.lo = (int64_t)j * p.team_len;
+  sc.hi = min(width, sc.lo + (int64_t)p.team_len);
   if (sc.hi < sc.lo) sc.hi = sc.lo;
   sc.nvec = (sc.hi - sc.lo) / VEC;
   sc.vhi = sc.lo + sc.nvec * VEC;
@@ -185,8 +204,8 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
   using S = typename E::Storage;
   constexpr int VEC = E::kPerVec;
   const int64_t nvec = u.kind == 0 ? 0 : sc.nvec;
-  const S* prow = row_ptr<E>(p.target, u.trow, p.stride) + sc.lo;
-  const S* qrow = row_ptr<E>(p.draft, u.drow, p.stride) + sc.lo;
+  const S* prow = row_ptr<E>(sc.tgt, u.trow, p.stride) + sc.lo;
+  const S* qrow = row_ptr<E>(sc.dft, u.drow, p.stride) + sc.lo;
   const bool pair = u.kind == 1;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -248,7 +267,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int64_t lo = sc.lo, vhi = sc.vhi, hi = sc.hi;
-  const auto* prow = row_ptr<E>(p.target, u.trow, p.stride);
+  const auto* prow = row_ptr<E>(sc.tgt, u.trow, p.stride);
   if (u.kind == 3) {
     // arg max of this thread's vectors: best vector in order, then its first
     // maximal element (NaN propagates through the maximum)
@@ -275,11 +294,11 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
         const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
 #pragma unroll
         for (int j = VEC - 1; j >= 0; --j)
-          if (x[j] == best) a.i = (int32_t)(lo + v * VEC + j);
+          if (x[j] == best) a.i = (int32_t)(sc.off + lo + v * VEC + j);
       }
     }
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads)
-      a = argmax_merge(a, ArgMax{E::load1(prow, i), (int32_t)i});
+      a = argmax_merge(a, ArgMax{E::load1(prow, i), (int32_t)(sc.off + i)});
     for (int m = 1; m < kWave; m <<= 1) {
       ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
       a = argmax_merge(a, o);
@@ -302,7 +321,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
     for (int i = 0; i < NV; ++i)
       E::unpack(R.q[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
     sq = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[VEC * NV]), mslq);
-    const auto* qrow = row_ptr<E>(p.draft, u.drow, p.stride);
+    const auto* qrow = row_ptr<E>(sc.dft, u.drow, p.stride);
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
       float x1[1] = {E::load1(qrow, i)};
       softmax_group<1>(sq, x1, sl);
@@ -361,8 +380,8 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
       sum += m[0];
     }
     acc = sum * kp;
-    const auto* prow = row_ptr<E>(p.target, u.trow, p.stride);
-    const auto* qrow = row_ptr<E>(p.draft, u.drow, p.stride);
+    const auto* prow = row_ptr<E>(sc.tgt, u.trow, p.stride);
+    const auto* qrow = row_ptr<E>(sc.dft, u.drow, p.stride);
     for (int64_t i = sc.vhi + threadIdx.x; i < sc.hi; i += kDataThreads)
       acc += exp2_fast(fminf(__builtin_fmaf(E::load1(prow, i), sl, -cp),
                              __builtin_fmaf(E::load1(qrow, i), sl, -cq)));
@@ -504,7 +523,7 @@ __device__ __forceinline__ void second_pass_comm(const VerifyParams& p, const Un
 
 // ---------------------------------------------------------------------------
 
-template <typename E, int NV>
+template <typename E, int NV, bool SH>
 __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
   __shared__ TeamLds L;
   const int nt = p.team;
@@ -519,7 +538,7 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
   const int64_t my_singles =
       (in_team && n_singles > team) ? (n_singles - 1 - team) / p.nteams + 1 : 0;
   const int64_t n = my_pairs + my_singles;
-  const Slice sc = make_slice<E>(p, member);
+  const Slice sc = make_slice<E, SH>(p, member);
 
   // Both roles run steps s = 0 .. n with one barrier each, then a last one.
   // Data step s: loads of unit s + 2, first pass of unit s, the
@@ -639,6 +658,27 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
 // exponentials of one more row pair are parked in LDS), T members per row.
 // Returns false if a row needs more than 64 members (the caller then uses
 // the streaming row pass).
+// With nshard > 1 vocabulary shards of width W, every shard is tiled by the
+// same number of members (T = nshard * per_shard) and no slice crosses a
+// shard.
+bool team_geometry_sharded(sv_dtype dtype, int32_t nshard, int64_t W, int grid, int32_t* T,
+                           int32_t* per_shard, int32_t* NV, int32_t* slice_len) {
+  const int64_t vec = (dtype == SV_DTYPE_BF16) ? 8 : 4;
+  const int64_t wvec = (W + vec - 1) / vec;
+  int64_t nv = (wvec + kDataThreads - 1) / kDataThreads;
+  if (nv > 2) nv = 2;
+  if (nv < 1) nv = 1;
+  const int64_t per = (wvec + kDataThreads * nv - 1) / (kDataThreads * nv);
+  const int64_t t = per * nshard;
+  if (t > 64 || t > grid) return false;
+  const int64_t svec = (wvec + per - 1) / per;
+  *T = (int32_t)t;
+  *per_shard = (int32_t)per;
+  *NV = (int32_t)((svec + kDataThreads - 1) / kDataThreads);
+  *slice_len = (int32_t)(svec * vec);
+  return true;
+}
+
 bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
                    int32_t* slice_len) {
   const int64_t vec = (dtype == SV_DTYPE_BF16) ? 8 : 4;
@@ -661,27 +701,36 @@ bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
 // running other work every workgroup is resident from the start.  (A plain
 // launch: the cooperative launch path costs more than ten microseconds of
 // launch latency here.)  On a shared device the team wait is still bounded.
-template <typename E, int NV>
+template <typename E, int NV, bool SH>
 static hipError_t launch_team_t(VerifyParams& p, int grid, hipStream_t stream) {
   static std::atomic<int> per_cu{-1};
   int fit = per_cu.load(std::memory_order_relaxed);
   if (fit < 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_rowteam<E, NV>, kTeamThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_rowteam<E, NV, SH>, kTeamThreads, 0) !=
         hipSuccess)
       nb = 0;
     fit = nb;
     per_cu.store(fit, std::memory_order_relaxed);
   }
   if (fit < 1) return hipErrorLaunchOutOfResources;
-  hipLaunchKernelGGL((k_rowteam<E, NV>), dim3((unsigned)grid), dim3(kTeamThreads), 0, stream, p);
+  hipLaunchKernelGGL((k_rowteam<E, NV, SH>), dim3((unsigned)grid), dim3(kTeamThreads), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
-hipError_t launch_rowteam(VerifyParams& p, int grid, int nv, hipStream_t stream) {
+template <bool SH>
+static hipError_t launch_rowteam_sh(VerifyParams& p, int grid, int nv, hipStream_t stream) {
   if (p.dtype == SV_DTYPE_BF16)
-    return nv == 1 ? launch_team_t<Bf16, 1>(p, grid, stream) : launch_team_t<Bf16, 2>(p, grid, stream);
-  return nv == 1 ? launch_team_t<F32, 1>(p, grid, stream) : launch_team_t<F32, 2>(p, grid, stream);
+    return nv == 1 ? launch_team_t<Bf16, 1, SH>(p, grid, stream)
+                   : launch_team_t<Bf16, 2, SH>(p, grid, stream);
+  return nv == 1 ? launch_team_t<F32, 1, SH>(p, grid, stream)
+                 : launch_team_t<F32, 2, SH>(p, grid, stream);
+}
+
+hipError_t launch_rowteam(VerifyParams& p, int grid, int nv, hipStream_t stream) {
+  return p.nshard > 1 ? launch_rowteam_sh<true>(p, grid, nv, stream)
+                      : launch_rowteam_sh<false>(p, grid, nv, stream);
 }
 
 }  // namespace sv

@@ -23,6 +23,7 @@
 #include "sv_block.hpp"
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
+#include "sv_shard.hpp"
 
 namespace sv {
 
@@ -67,7 +68,7 @@ __device__ __forceinline__ bool finite_f(float x) { return x == x && x != INFINI
 // ---------------------------------------------------------------------------
 // k_accept: one workgroup (2 wavefronts) per request.  Thread k handles
 // target row k (k <= n) and, for k < n, draft row k and the accept test.
-template <typename E>
+template <typename E, bool SH>
 __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
   using S = typename E::Storage;
   __shared__ uint32_t s_bits;
@@ -118,9 +119,8 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
         }
       }
       if (k < n && bits == 0u) {
-        const S* prow = row_ptr<E>(p.target, p.target_row0[r] + k, p.stride);
-        const S* qrow = row_ptr<E>(p.draft, p.draft_row0[r] + k, p.stride);
-        const float pd = E::load1(prow, d), qd = E::load1(qrow, d);
+        const float pd = E::load1(row_view<E, SH>(p, false, p.target_row0[r] + k).at(d), 0);
+        const float qd = E::load1(row_view<E, SH>(p, true, p.draft_row0[r] + k).at(d), 0);
         // log2 p(d) - log2 q(d), each as (x - m) sl - log2 z.
         const float lp = __builtin_fmaf(pd - sp.m, sl, -__log2f(sp.z));
         const float lq = __builtin_fmaf(qd - sq.m, sl, -__log2f(sq.z));
@@ -226,9 +226,16 @@ template <typename E>
 static hipError_t launch_all(VerifyParams& p, int grid, hipStream_t stream) {
   // Team row pass when a row fits a team of at most 64 members and the team
   // kernel fits one workgroup per CU; otherwise the streaming row pass.
-  int32_t T = 0, nv = 0, slice = 0;
-  const bool team = (p.flags & SV_FLAG_STREAMING_ROW_PASS) == 0u && grid <= kMaxTeamGrid &&
-                    team_geometry(p.dtype, p.V, grid, &T, &nv, &slice);
+  // Vocabulary shards need the team pass (its members tile the shards).
+  int32_t T = 0, nv = 0, slice = 0, per_shard = 0;
+  const bool sharded = p.nshard > 1;
+  const bool team =
+      (p.flags & SV_FLAG_STREAMING_ROW_PASS) == 0u && grid <= kMaxTeamGrid &&
+      (sharded ? team_geometry_sharded(p.dtype, p.nshard, p.shard_w, grid, &T, &per_shard, &nv,
+                                       &slice)
+               : team_geometry(p.dtype, p.V, grid, &T, &nv, &slice));
+  if (sharded && !team) return hipErrorInvalidValue;
+  p.team_per_shard = sharded ? per_shard : T;
   if (team) {
     p.S1 = T;
     // with acceptance rates the team pass stores a pair's row states in slot 0
@@ -248,6 +255,7 @@ static hipError_t launch_all(VerifyParams& p, int grid, hipStream_t stream) {
   mark(p, 1, stream);
   bool done = false;
   if (team) done = launch_rowteam(p, grid, nv, stream) == hipSuccess;
+  if (!done && sharded) return hipErrorInvalidValue;
   if (!done) {
     (void)hipGetLastError();
     if (team) {  // fall back: streaming pass with its own slot layout
@@ -258,7 +266,10 @@ static hipError_t launch_all(VerifyParams& p, int grid, hipStream_t stream) {
     launch_rowpass(p, grid, stream);
   }
   mark(p, 2, stream);
-  hipLaunchKernelGGL(k_accept<E>, dim3((unsigned)p.B), dim3(128), 0, stream, p);
+  if (sharded)
+    hipLaunchKernelGGL((k_accept<E, true>), dim3((unsigned)p.B), dim3(128), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_accept<E, false>), dim3((unsigned)p.B), dim3(128), 0, stream, p);
   mark(p, 3, stream);
   launch_draw(p, stream);
   mark(p, 4, stream);

@@ -42,7 +42,8 @@ BIT_SYNC_TIMEOUT = 64
 EXPORTS = ["sv_status_string", "sv_version", "sv_k_rho", "sv_allocate_budget",
            "sv_verify_workspace_bytes", "sv_verify_batch", "sv_accept_stats",
            "sv_draft_confidence_workspace_bytes", "sv_draft_confidence", "sv_select_budget_ratio",
-           "sv_sample_rows"]
+           "sv_sample_rows", "sv_verify_batch_sharded"]
+MAX_SHARDS = 16
 MAX_RATIOS = 8
 DCUT_RATIOS = (0.25, 0.5, 0.75, 1.0)
 
@@ -118,6 +119,10 @@ def load() -> ctypes.CDLL:
                                  ctypes.c_int64, vp, ctypes.c_int64, vp, vp, ctypes.c_uint64,
                                  ctypes.c_uint32, ctypes.c_uint32, vp, ctypes.c_int64, vp]
     L.sv_sample_rows.restype = ctypes.c_int
+    L.sv_verify_batch_sharded.argtypes = [ctypes.POINTER(SvVerifyArgs), ctypes.c_int32,
+                                          ctypes.c_int64, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                          vp]
+    L.sv_verify_batch_sharded.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -314,13 +319,16 @@ class Verifier:
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.args = SvVerifyArgs()
         self._keep = []
+        self._shards = None
 
     def prepare(self, target, draft, target_row0, draft_row0, draft_tokens, depth, temperature,
-                *, seed: int = 0, step: int = 0, request_id=None, flags: int = 0):
+                *, seed: int = 0, step: int = 0, request_id=None, flags: int = 0,
+                _shard: bool = False):
         """Fill the argument block; the tensors must stay alive while used."""
         tgt, stride = _rows_view(target)
-        if tgt.shape[1] < self.V:
+        if tgt.shape[1] < self.V and not _shard:
             raise ValueError("row width below V")
+        self._shards = None
         a = self.args
         a.dtype = _dtype_code(tgt.dtype)
         a.B, a.D_max, a.V, a.row_stride = self.B, self.D_max, self.V, stride
@@ -352,6 +360,34 @@ class Verifier:
                       request_id]
         return self
 
+    def prepare_sharded(self, target_shards, draft_shards, shard_width: int, target_row0,
+                        draft_row0, draft_tokens, depth, temperature, *, seed: int = 0,
+                        step: int = 0, request_id=None, flags: int = 0):
+        """Like prepare, for logits split over vocabulary shards: shard s of a
+        row holds columns [s W, min(V, (s + 1) W)); every shard a (rows, width)
+        tensor with the same contiguous-row stride (sv_verify_batch_sharded)."""
+        views = [_rows_view(t) for t in target_shards]
+        stride = views[0][1]
+        if any(st != stride for _, st in views):
+            raise ValueError("every shard needs the same row stride")
+        self.prepare(views[0][0], None if draft_shards is None else _rows_view(draft_shards[0])[0],
+                     target_row0, draft_row0, draft_tokens, depth, temperature, seed=seed,
+                     step=step, request_id=request_id, flags=flags, _shard=True)
+        self.args.row_stride = stride
+        self.args.target_logits = None
+        self.args.draft_logits = None
+        n = len(target_shards)
+        self._tsh = (ctypes.c_void_p * n)(*[t.data_ptr() for t, _ in views])
+        self._dsh = None
+        if draft_shards is not None:
+            dv = [_rows_view(t) for t in draft_shards]
+            if any(st != stride for _, st in dv) or len(dv) != n:
+                raise ValueError("draft shards must match the target shards")
+            self._dsh = (ctypes.c_void_p * n)(*[t.data_ptr() for t, _ in dv])
+        self._shards = (n, int(shard_width))
+        self._keep.append((target_shards, draft_shards))
+        return self
+
     def set_stage_events(self, events):
         """Ask for SV_NUM_STAGE_EVENTS torch.cuda.Event objects (timing
         enabled; an entry may be None) to be recorded at the stage
@@ -369,6 +405,12 @@ class Verifier:
         self.args.stage_events = ctypes.cast(self._events, ctypes.c_void_p)
 
     def run(self) -> VerifyOutputs:
+        if self._shards is not None:
+            n, w = self._shards
+            st = load().sv_verify_batch_sharded(ctypes.byref(self.args), n, w, self._tsh,
+                                                self._dsh, _stream(self.device))
+            _check(st, "sv_verify_batch_sharded")
+            return self.out
         st = load().sv_verify_batch(ctypes.byref(self.args), _stream(self.device))
         _check(st, "sv_verify_batch")
         return self.out

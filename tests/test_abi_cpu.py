@@ -183,3 +183,31 @@ def test_sample_validation_codes(sv):
     assert call(logits=None) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(idx=None) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(tok=None) == sv.SV_ERR_INVALID_ARGUMENT
+
+
+def test_sharded_verify_validation_codes(sv):
+    lib = sv.load()
+    fake = 1 << 20
+    P = ctypes.c_void_p
+
+    def call(n=2, w=64, V=120, shards=(fake, fake + 4096), dshards=None, stride=64, B=1,
+             draft_row0=None):
+        a = sv.SvVerifyArgs()
+        a.dtype, a.B, a.D_max, a.V, a.row_stride = 0, B, 3, V, stride
+        a.target_row0, a.depth, a.temperature = fake, fake, fake
+        a.accepted_len, a.out_tokens, a.num_out, a.draft_tokens = fake, fake, fake, fake
+        a.draft_row0 = draft_row0
+        a.workspace, a.workspace_bytes = fake, 1 << 30
+        t = (P * len(shards))(*shards) if shards is not None else None
+        d = (P * len(dshards))(*dshards) if dshards is not None else None
+        return lib.sv_verify_batch_sharded(ctypes.byref(a), n, w, t, d, None)
+
+    assert call(shards=None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(n=0) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(n=17) == sv.SV_ERR_INVALID_ARGUMENT
+    assert call(w=60) == sv.SV_ERR_UNSUPPORTED             # not a multiple of 8
+    assert call(n=3, shards=(fake, fake, fake)) == sv.SV_ERR_INVALID_ARGUMENT  # ceil(120/64) = 2
+    assert call(shards=(fake, fake + 8)) == sv.SV_ERR_INVALID_ARGUMENT         # misaligned shard
+    assert call(stride=60) == sv.SV_ERR_INVALID_ARGUMENT   # stride below the shard width
+    assert call(dshards=(fake, fake)) == sv.SV_ERR_INVALID_ARGUMENT            # no draft_row0
+    assert call(B=0) == sv.SV_OK
