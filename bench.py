@@ -195,6 +195,43 @@ def draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize):
     }
 
 
+def sharded_figure(sv, torch, w, tgt, dft, bud, dr0, n_shards, rowpass_bytes, step_us):
+    """The same verification with the vocabulary split over n_shards buffers
+    (a tensor-parallel target's layout, all on this GPU): time per call."""
+    B, D, V = w.B, w.D, w.V
+    W = -(-V // n_shards)
+    W = -(-W // 8) * 8
+
+    def split(rows):
+        out = []
+        for s in range(0, V, W):
+            buf = torch.empty((rows.shape[0], W), dtype=rows.dtype, device=rows.device)
+            part = rows[:, s:s + W]
+            buf[:, : part.shape[1]] = part
+            out.append(buf)
+        return out
+
+    ts, ds = split(tgt), split(dft.reshape(B * D, V))
+    v = sv.Verifier(B, D, V, tgt.device, alpha=True, diag=True)
+    v.prepare_sharded(ts, ds, W, bud["target_row0"], dr0, w.draft_tokens, bud["depth"],
+                      w.temperature, seed=0, step=0)
+    for _ in range(5):
+        v.run()
+    torch.cuda.synchronize()
+    n = 30
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        v.run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    del ts, ds
+    return {"shards": len(range(0, V, W)), "shard_width": W, "verify_us": round(us, 1),
+            "unsharded_verify_us": round(step_us, 1),
+            "algorithmic_GBps": round(rowpass_bytes / (us * 1e-6) / 1e9, 1)}
+
+
 def decode_loop_figure(sv, torch, dev, V=32768, B=64, D=8, steps=30):
     """The multi-step decode loop on a synthetic Markov target (bf16 tables of
     V x V, target P ~ 3 N(0, 1), drafter Q = P + N(0, 1), T = 1): time per
@@ -383,6 +420,9 @@ def main():
     if D > 0 and draft_rows > 0:
         res["draft_side"] = draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize)
         res["decode_loop"] = decode_loop_figure(sv, torch, dev)
+        verify_us = sum(stage_ms) * 1e3  # the stage events cover the whole verification
+        res["sharded_tp8"] = sharded_figure(sv, torch, w, copies[0][0], copies[0][1], bud, dr0, 8,
+                                            rowpass_bytes, verify_us)
     if args.calib_copy_mb:
         # a plain device copy of known size: scales rocprofv3's byte counters
         # and gives the copy bandwidth for context (read + write bytes / time)
