@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the draft-side, decode-loop and sharded figures (profiling runs)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(a reference dispatch for scaling rocprofv3 byte counters)")
@@ -417,7 +419,7 @@ def main():
         "expected_mean_accepted_length": round(float(stats_out["summary"][1]), 4),
         "source_digest": digest,
     }
-    if D > 0 and draft_rows > 0:
+    if D > 0 and draft_rows > 0 and not args.no_extras:
         res["draft_side"] = draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize)
         res["decode_loop"] = decode_loop_figure(sv, torch, dev)
         verify_us = sum(stage_ms) * 1e3  # the stage events cover the whole verification
