@@ -125,6 +125,7 @@ __device__ uint64_t select_threshold(const uint64_t (&key)[kKeySlots], int N, in
     S.s_whole = 0;
   }
   if (Keff <= 0) return ~0ull;
+  if (Keff >= S.s_valid) return 1ull;  // every valid position is kept (their keys are >= 1)
   for (int d = 0; d < 8; ++d) {
     const int shift = 56 - 8 * d;
     if (tid < 256) S.hist[tid] = 0;

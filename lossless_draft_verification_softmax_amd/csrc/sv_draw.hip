@@ -585,11 +585,13 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
       }
     }
     s_redo[threadIdx.x] = redo;
-    __syncthreads();
-    for (int k = 0; k < kDrawThreads && base + k < p.S2; ++k) {
-      if (!s_redo[k]) continue;  // uniform: every thread reads the same flag
-      const double m = tile_mass<double>(w, base + k, p.V, lds);
-      if (threadIdx.x == 0) masses[base + k] = m;
+    // usually no tile needs a direct recompute: skip the walk over the flags
+    if (__syncthreads_or(redo)) {
+      for (int k = 0; k < kDrawThreads && base + k < p.S2; ++k) {
+        if (!s_redo[k]) continue;  // uniform: every thread reads the same flag
+        const double m = tile_mass<double>(w, base + k, p.V, lds);
+        if (threadIdx.x == 0) masses[base + k] = m;
+      }
     }
     __syncthreads();
   }
