@@ -213,11 +213,13 @@ typedef struct sv_verify_args {
  * args->target_logits and args->draft_logits are ignored; everything else,
  * the outputs and the workspace are as for sv_verify_batch, and so are the
  * results: the method is that of the concatenated rows.  The team row pass
- * tiles each shard with its own members, so the row normalisers are the
- * associative (max, sum) merge of per-shard states and sum min(p, q) a sum of
- * per-shard sums; the draw scans tile masses in column order across shards.
- * SV_ERR_UNSUPPORTED when a shard needs more team members than fit (no
- * streaming fallback here) or for a shard width that is not a multiple of 8.
+ * tiles the concatenated row exactly as an unsharded one (a member's slice
+ * may span two shards; each 16-byte vector lies in one, its address resolved
+ * once per thread), so the row normalisers are the associative (max, sum)
+ * merge of slice states and sum min(p, q) a sum of slice sums; the draw scans
+ * tile masses in column order across shards.  SV_ERR_UNSUPPORTED when a row
+ * needs more team members than fit (no streaming fallback here) or for a
+ * shard width that is not a multiple of 8.
  * ------------------------------------------------------------------------- */
 sv_status sv_verify_batch_sharded(const sv_verify_args* args, int32_t n_shards,
                                   int64_t shard_width, const void* const* target_shards,

@@ -153,9 +153,8 @@ sv_status run_verify(const sv_verify_args* a, int32_t nshard, int64_t shard_w,
   const int grid = device_cu_count();
   if (grid <= 0) return SV_ERR_DEVICE;
   if (nshard > 1) {  // the sharded path has no streaming fallback
-    int32_t T, per, nv, slice;
-    if (grid > sv::kMaxTeamGrid ||
-        !sv::team_geometry_sharded(p.dtype, nshard, shard_w, grid, &T, &per, &nv, &slice))
+    int32_t T, nv, slice;
+    if (grid > sv::kMaxTeamGrid || !sv::team_geometry(p.dtype, p.V, grid, &T, &nv, &slice))
       return SV_ERR_UNSUPPORTED;
   }
   const hipError_t e = sv::launch_verify(p, grid, static_cast<hipStream_t>(stream));

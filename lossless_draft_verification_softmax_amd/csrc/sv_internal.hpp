@@ -73,7 +73,6 @@ struct VerifyParams {
   // shards) and the kernels read the shard pointers from shard_tab (target
   // shards, then draft shards), written by k_plan.
   int32_t nshard;
-  int32_t team_per_shard;  // team row pass: members per shard
   int64_t shard_w;
   const void* tsh[kMaxShards];
   const void* dsh[kMaxShards];
@@ -182,8 +181,6 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
 hipError_t launch_verify(VerifyParams& p, int grid, hipStream_t stream);
 bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
                    int32_t* slice_len);
-bool team_geometry_sharded(sv_dtype dtype, int32_t nshard, int64_t W, int grid, int32_t* T,
-                           int32_t* per_shard, int32_t* NV, int32_t* slice_len);
 hipError_t launch_rowteam(VerifyParams& p, int grid, int nv, hipStream_t stream);
 void launch_plan(const VerifyParams& p, hipStream_t stream);
 void launch_rowpass(const VerifyParams& p, int grid, hipStream_t stream);

@@ -81,14 +81,17 @@ struct UnitDesc {
   int32_t ordinal;  // pair ordinal within the team
 };
 
-// The workgroup's slice of every row it works on: elements [lo, hi) of the
-// buffers tgt / dft, of which [lo, vhi) are nvec whole 16-byte vectors;
-// element i is column i + off of the full row.  Without vocabulary shards
-// the buffers are the row buffers and off = 0; with shards, member m works
-// in shard m / team_per_shard (the team's members tile each shard, so no
-// slice crosses one) and the buffers are that shard's.
+// The workgroup's slice of every row it works on: columns [lo, hi) of the
+// full row, of which [lo, vhi) are nvec whole 16-byte vectors.  Column i
+// lies at element i - toff of the buffers tgt / dft.  Without vocabulary
+// shards these are the row buffers and toff = 0.  With shards the slices
+// tile the concatenated row as they do an unsharded one and may cross a
+// shard boundary; the shard width is a whole number of vectors, so each
+// vector lies in one shard and each thread resolves its vectors' shard
+// addresses once (LanePtrs).  tgt / dft are then the last shard's buffers,
+// which hold the ragged tail (the columns past the last whole vector).
 struct Slice {
-  int64_t lo, vhi, hi, nvec, off;
+  int64_t lo, vhi, hi, nvec, toff;
   const void* tgt;
   const void* dft;
 };
@@ -97,25 +100,47 @@ template <typename E, bool SH>
 __device__ __forceinline__ Slice make_slice(const VerifyParams& p, int member) {
   constexpr int VEC = E::kPerVec;
   Slice sc;
-  int64_t width = p.V;
-  int j = member;
-  sc.off = 0;
+  sc.toff = 0;
   sc.tgt = p.target;
   sc.dft = p.draft;
   if constexpr (SH) {
-    const int s = member / p.team_per_shard;
-    j = member % p.team_per_shard;
-    sc.off = (int64_t)s * p.shard_w;
-    width = min(p.shard_w, p.V - sc.off);
-    sc.tgt = p.shard_tab[s];
-    sc.dft = p.shard_tab[kMaxShards + s];
+    const int last = p.nshard - 1;
+    sc.toff = (int64_t)last * p.shard_w;
+    sc.tgt = p.shard_tab[last];
+    sc.dft = p.shard_tab[kMaxShards + last];
   }
-  sc.lo = (int64_t)j * p.team_len;
-  sc.hi = min(width, sc.lo + (int64_t)p.team_len);
+  sc.lo = (int64_t)member * p.team_len;
+  sc.hi = min(p.V, sc.lo + (int64_t)p.team_len);
   if (sc.hi < sc.lo) sc.hi = sc.lo;
   sc.nvec = (sc.hi - sc.lo) / VEC;
   sc.vhi = sc.lo + sc.nvec * VEC;
   return sc;
+}
+
+// Sharded rows: the address in row 0 of each of this thread's NV vectors,
+// in the target and in the draft shards.  Vectors past the slice get any
+// address inside the table's range; they are never read.
+template <int NV>
+struct LanePtrs {
+  const char* t[NV];
+  const char* d[NV];
+};
+
+template <typename E, int NV>
+__device__ __forceinline__ LanePtrs<NV> lane_ptrs(const VerifyParams& p, const Slice& sc) {
+  using S = typename E::Storage;
+  constexpr int VEC = E::kPerVec;
+  const int64_t wv = p.shard_w / VEC;  // vectors per shard
+  LanePtrs<NV> lp;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t g = sc.lo / VEC + (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+    const int s = (int)min(g / wv, (int64_t)(p.nshard - 1));
+    const int64_t o = (g - (int64_t)s * wv) * VEC * (int64_t)sizeof(S);
+    lp.t[i] = static_cast<const char*>(p.shard_tab[s]) + o;
+    lp.d[i] = static_cast<const char*>(p.shard_tab[kMaxShards + s]) + o;
+  }
+  return lp;
 }
 
 // Shared state, double-buffered by unit parity (see the step order above).
@@ -198,23 +223,38 @@ __device__ __forceinline__ const uint4* neg_inf_line() {
 // Issues the 2 * NV loads of a unit.  Vectors outside the slice, the draft
 // row of a single row and every vector of an empty unit read the -inf line
 // instead.
-template <typename E, int NV>
+template <typename E, int NV, bool SH>
 __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc& u,
-                                          const Slice& sc, Regs<NV>& R, const uint4* dummy) {
+                                          const Slice& sc, const LanePtrs<NV>& lp, Regs<NV>& R,
+                                          const uint4* dummy) {
   using S = typename E::Storage;
   constexpr int VEC = E::kPerVec;
   const int64_t nvec = u.kind == 0 ? 0 : sc.nvec;
-  const S* prow = row_ptr<E>(sc.tgt, u.trow, p.stride) + sc.lo;
-  const S* qrow = row_ptr<E>(sc.dft, u.drow, p.stride) + sc.lo;
   const bool pair = u.kind == 1;
+  if constexpr (SH) {
+    const int64_t tb = u.trow * p.stride * (int64_t)sizeof(S);
+    const int64_t db = u.drow * p.stride * (int64_t)sizeof(S);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
-    const bool in = v < nvec;
-    const void* pa = in ? (const void*)(prow + v * VEC) : (const void*)dummy;
-    const void* qa = (in && pair) ? (const void*)(qrow + v * VEC) : (const void*)dummy;
-    R.p[i] = load16(pa);
-    R.q[i] = load16(qa);
+    for (int i = 0; i < NV; ++i) {
+      const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+      const bool in = v < nvec;
+      const void* pa = in ? (const void*)(lp.t[i] + tb) : (const void*)dummy;
+      const void* qa = (in && pair) ? (const void*)(lp.d[i] + db) : (const void*)dummy;
+      R.p[i] = load16(pa);
+      R.q[i] = load16(qa);
+    }
+  } else {
+    const S* prow = row_ptr<E>(sc.tgt, u.trow, p.stride) + sc.lo;
+    const S* qrow = row_ptr<E>(sc.dft, u.drow, p.stride) + sc.lo;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+      const bool in = v < nvec;
+      const void* pa = in ? (const void*)(prow + v * VEC) : (const void*)dummy;
+      const void* qa = (in && pair) ? (const void*)(qrow + v * VEC) : (const void*)dummy;
+      R.p[i] = load16(pa);
+      R.q[i] = load16(qa);
+    }
   }
 }
 
@@ -294,11 +334,11 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
         const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
 #pragma unroll
         for (int j = VEC - 1; j >= 0; --j)
-          if (x[j] == best) a.i = (int32_t)(sc.off + lo + v * VEC + j);
+          if (x[j] == best) a.i = (int32_t)(lo + v * VEC + j);
       }
     }
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads)
-      a = argmax_merge(a, ArgMax{E::load1(prow, i), (int32_t)(sc.off + i)});
+      a = argmax_merge(a, ArgMax{E::load1(prow, i - sc.toff), (int32_t)i});
     for (int m = 1; m < kWave; m <<= 1) {
       ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
       a = argmax_merge(a, o);
@@ -313,7 +353,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
   SoftmaxPart sq{-INFINITY, 0.0f};
   SoftmaxPart sp = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[0]), mslp);
   for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
-    float x1[1] = {E::load1(prow, i)};
+    float x1[1] = {E::load1(prow, i - sc.toff)};
     softmax_group<1>(sp, x1, sl);
   }
   if (u.kind == 1) {
@@ -323,7 +363,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
     sq = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[VEC * NV]), mslq);
     const auto* qrow = row_ptr<E>(sc.dft, u.drow, p.stride);
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
-      float x1[1] = {E::load1(qrow, i)};
+      float x1[1] = {E::load1(qrow, i - sc.toff)};
       softmax_group<1>(sq, x1, sl);
     }
   }
@@ -383,8 +423,8 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
     const auto* prow = row_ptr<E>(sc.tgt, u.trow, p.stride);
     const auto* qrow = row_ptr<E>(sc.dft, u.drow, p.stride);
     for (int64_t i = sc.vhi + threadIdx.x; i < sc.hi; i += kDataThreads)
-      acc += exp2_fast(fminf(__builtin_fmaf(E::load1(prow, i), sl, -cp),
-                             __builtin_fmaf(E::load1(qrow, i), sl, -cq)));
+      acc += exp2_fast(fminf(__builtin_fmaf(E::load1(prow, i - sc.toff), sl, -cp),
+                             __builtin_fmaf(E::load1(qrow, i - sc.toff), sl, -cq)));
   }
   acc = wave_sum(acc);
   if (lane == 0) L.acc[b][wave] = acc;
@@ -551,6 +591,8 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
   __shared__ uint4 park[kPark][kDataThreads];
   if (threadIdx.x < kDataThreads) {
     const uint4* dummy = neg_inf_line<E>();
+    LanePtrs<NV> lp{};
+    if constexpr (SH) lp = lane_ptrs<E, NV>(p, sc);
     Regs<NV> R0, R1, R2;
     UnitDesc U0 = unit_at(p, 0, n, team, my_pairs);
     UnitDesc U1 = unit_at(p, 1, n, team, my_pairs);
@@ -558,13 +600,13 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     UnitDesc un = unit_at(p, 2, n, team, my_pairs);
     UnitDesc up = no_unit();  // unit s - 1 (parked)
     float mslp1 = 0.0f, mslq1 = 0.0f;
-    load_unit<E, NV>(p, U0, sc, R0, dummy);
-    load_unit<E, NV>(p, U1, sc, R1, dummy);
+    load_unit<E, NV, SH>(p, U0, sc, lp, R0, dummy);
+    load_unit<E, NV, SH>(p, U1, sc, lp, R1, dummy);
     // Step s: first pass on buffer s mod 3, loads into buffer s + 2 mod 3.
     auto step = [&](int64_t s, const Regs<NV>& Rf, const UnitDesc& Uf, Regs<NV>& Rl,
                     UnitDesc& Ul) {
       Ul = un;
-      load_unit<E, NV>(p, Ul, sc, Rl, dummy);
+      load_unit<E, NV, SH>(p, Ul, sc, lp, Rl, dummy);
       un = unit_at(p, s + 3, n, team, my_pairs);
       float e[2 * NV * E::kPerVec];
       float mslp = 0.0f, mslq = 0.0f;
@@ -657,28 +699,8 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
 // thread per row (three buffers of two rows stay in registers, the
 // exponentials of one more row pair are parked in LDS), T members per row.
 // Returns false if a row needs more than 64 members (the caller then uses
-// the streaming row pass).
-// With nshard > 1 vocabulary shards of width W, every shard is tiled by the
-// same number of members (T = nshard * per_shard) and no slice crosses a
-// shard.
-bool team_geometry_sharded(sv_dtype dtype, int32_t nshard, int64_t W, int grid, int32_t* T,
-                           int32_t* per_shard, int32_t* NV, int32_t* slice_len) {
-  const int64_t vec = (dtype == SV_DTYPE_BF16) ? 8 : 4;
-  const int64_t wvec = (W + vec - 1) / vec;
-  int64_t nv = (wvec + kDataThreads - 1) / kDataThreads;
-  if (nv > 2) nv = 2;
-  if (nv < 1) nv = 1;
-  const int64_t per = (wvec + kDataThreads * nv - 1) / (kDataThreads * nv);
-  const int64_t t = per * nshard;
-  if (t > 64 || t > grid) return false;
-  const int64_t svec = (wvec + per - 1) / per;
-  *T = (int32_t)t;
-  *per_shard = (int32_t)per;
-  *NV = (int32_t)((svec + kDataThreads - 1) / kDataThreads);
-  *slice_len = (int32_t)(svec * vec);
-  return true;
-}
-
+// the streaming row pass).  Vocabulary shards do not change it: the members
+// tile the concatenated row.
 bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
                    int32_t* slice_len) {
   const int64_t vec = (dtype == SV_DTYPE_BF16) ? 8 : 4;

@@ -226,16 +226,13 @@ template <typename E>
 static hipError_t launch_all(VerifyParams& p, int grid, hipStream_t stream) {
   // Team row pass when a row fits a team of at most 64 members and the team
   // kernel fits one workgroup per CU; otherwise the streaming row pass.
-  // Vocabulary shards need the team pass (its members tile the shards).
-  int32_t T = 0, nv = 0, slice = 0, per_shard = 0;
+  // Vocabulary shards need the team pass (its members resolve the shard of
+  // each vector).
+  int32_t T = 0, nv = 0, slice = 0;
   const bool sharded = p.nshard > 1;
-  const bool team =
-      (p.flags & SV_FLAG_STREAMING_ROW_PASS) == 0u && grid <= kMaxTeamGrid &&
-      (sharded ? team_geometry_sharded(p.dtype, p.nshard, p.shard_w, grid, &T, &per_shard, &nv,
-                                       &slice)
-               : team_geometry(p.dtype, p.V, grid, &T, &nv, &slice));
+  const bool team = (p.flags & SV_FLAG_STREAMING_ROW_PASS) == 0u && grid <= kMaxTeamGrid &&
+                    team_geometry(p.dtype, p.V, grid, &T, &nv, &slice);
   if (sharded && !team) return hipErrorInvalidValue;
-  p.team_per_shard = sharded ? per_shard : T;
   if (team) {
     p.S1 = T;
     // with acceptance rates the team pass stores a pair's row states in slot 0
