@@ -126,22 +126,26 @@ struct Weights32 {
   RowView<E, SH> prow, qrow;
   bool has_q;  // false: bonus draw (w = p)
   float sl, mp, lzp, mq, lzq;
-  __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, float (&w)[kPer]) const {
-    float a[kPer];
-    load8<E, SH>(prow, i0, hi, a);
+  // weights of eight logits a (target) and b (draft; unused for a bonus draw)
+  __device__ __forceinline__ void from(const float (&a)[kPer], const float (&b)[kPer],
+                                       float (&w)[kPer]) const {
     if (!has_q) {
 #pragma unroll
       for (int j = 0; j < kPer; ++j) w[j] = exp2_fast(__builtin_fmaf(a[j] - mp, sl, -lzp));
       return;
     }
-    float b[kPer];
-    load8<E, SH>(qrow, i0, hi, b);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const float pv = exp2_fast(__builtin_fmaf(a[j] - mp, sl, -lzp));
       const float qv = exp2_fast(__builtin_fmaf(b[j] - mq, sl, -lzq));
       w[j] = fmaxf(pv - qv, 0.0f);
     }
+  }
+  __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, float (&w)[kPer]) const {
+    float a[kPer], b[kPer];
+    load8<E, SH>(prow, i0, hi, a);
+    if (has_q) load8<E, SH>(qrow, i0, hi, b);
+    from(a, b, w);
   }
 };
 
@@ -428,8 +432,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
     load8<E, SH>(row_view<E, SH>(p, false, st.prow), i0, hi, a);
     if (residual) load8<E, SH>(row_view<E, SH>(p, true, st.qrow), i0, hi, b);
     double zp = 0.0, zq = 0.0, D = 0.0, A = 0.0, S = 0.0;
-    double kep[kPer], keq[kPer];
-    int32_t U = 0;
+    uint32_t kmask = 0u;  // elements kept for the pick (their ep, eq recomputed below)
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const double ep = exp(((double)a[j] - (double)st.mp) * invT);
@@ -445,14 +448,13 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
           D += d;
           A += ep;
         } else if (d >= -tol && (ep > 0.0 || eq > 0.0)) {
-          kep[U] = ep;
-          keq[U] = eq;
-          ++U;
+          kmask |= 1u << j;
         }
       }
     }
     // kept elements: positions by an exclusive scan of the counts in thread
     // order, so the list is in element order
+    const int32_t U = __builtin_popcount(kmask);
     int32_t incl = U;
     for (int d = 1; d < kWave; d <<= 1) {
       const int32_t o = __shfl_up(incl, d);
@@ -467,11 +469,16 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
     }
     base += incl - U;
     const int64_t o = (int64_t)r * p.S2 + tile;
-    if (total <= kDrawKeep64) {
+    if (total <= kDrawKeep64 && kmask != 0u) {
       double* keep = p.seg_e64 + o * (kDrawKeep64 * 2);
-      for (int k = 0; k < U; ++k) {
-        keep[2 * (base + k)] = kep[k];
-        keep[2 * (base + k) + 1] = keq[k];
+      int32_t pos = base;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        if ((kmask >> j) & 1u) {
+          keep[2 * pos] = exp(((double)a[j] - (double)st.mp) * invT);
+          keep[2 * pos + 1] = exp(((double)b[j] - (double)st.mq) * invT);
+          ++pos;
+        }
       }
     }
     // block sums in a fixed order
@@ -540,14 +547,32 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   __shared__ double lds[kDrawThreads / kWave];
   __shared__ double lds2[kDrawThreads / kWave][2];
   __shared__ int s_redo[kDrawThreads];
+  __shared__ double s_mass[kDrawThreads];
   const int r = blockIdx.x;
   const DrawState st = p.req[r];
   if (st.mode == kDrawNone || !st.need64) return;
   const bool residual = st.mode == kDrawResidual;
-  double* masses = p.seg_w64 + (int64_t)r * p.S2;
+  const int64_t ro = (int64_t)r * p.S2;
+  // Tile masses stay in LDS when the row has at most one round of tiles.
+  double* masses = p.S2 <= kDrawThreads ? s_mass : p.seg_w64 + ro;
+  // The first round's split results are loaded together with the
+  // normaliser partials: one memory round trip before the masses.
+  const int64_t t0 = threadIdx.x;
+  const bool have0 = residual && t0 < p.S2;
+  int32_t nk0 = 0;
+  double d0 = 0.0, a0 = 0.0, s0 = 0.0;
+  double2 kv0[kDrawKeep64];
+  if (have0) {
+    nk0 = p.seg_u32[ro + t0];
+    d0 = p.seg_w64[ro + t0];
+    a0 = p.seg_a64[ro + t0];
+    s0 = p.seg_t64[ro + t0];
+    const double2* keep = reinterpret_cast<const double2*>(p.seg_e64 + (ro + t0) * (kDrawKeep64 * 2));
+#pragma unroll
+    for (int k = 0; k < kDrawKeep64; ++k) kv0[k] = keep[k];
+  }
   double Zp, Zq;
-  merge_z64(p.seg_zp64 + (int64_t)r * p.S2, residual ? p.seg_zq64 + (int64_t)r * p.S2 : nullptr,
-            p.S2, lds2, Zp, Zq);
+  merge_z64(p.seg_zp64 + ro, residual ? p.seg_zq64 + ro : nullptr, p.S2, lds2, Zp, Zq);
   if (!residual) Zq = 1.0;
   Weights64<E, SH> w = weights64<E, SH>(p, st, false);
   w.lnzp = log(Zp);
@@ -565,21 +590,35 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
     const int64_t t = base + threadIdx.x;
     int redo = 0;
     if (t < p.S2) {
-      const int64_t o = (int64_t)r * p.S2 + t;
+      const int64_t o = ro + t;
       if (!residual) {
         masses[t] = p.seg_zp64[o] / Zp;
-      } else if (split_ok && p.seg_u32[o] <= kDrawKeep64) {
-        const int32_t nk = p.seg_u32[o];
-        double m = (masses[t] + (rho - rho_e) * p.seg_a64[o]) * izq + p.seg_t64[o] * g_tie;
-        // the whole list is loaded at once (entries past nk are unused)
-        const double2* keep = reinterpret_cast<const double2*>(p.seg_e64 + o * (kDrawKeep64 * 2));
+      } else if (split_ok) {
+        int32_t nk = nk0;
+        double d = d0, a = a0, sv = s0;
         double2 kv[kDrawKeep64];
+        if (base == 0) {
 #pragma unroll
-        for (int k = 0; k < kDrawKeep64; ++k) kv[k] = keep[k];
+          for (int k = 0; k < kDrawKeep64; ++k) kv[k] = kv0[k];
+        } else {
+          nk = p.seg_u32[o];
+          d = p.seg_w64[o];
+          a = p.seg_a64[o];
+          sv = p.seg_t64[o];
+          // the whole list is loaded at once (entries past nk are unused)
+          const double2* keep = reinterpret_cast<const double2*>(p.seg_e64 + o * (kDrawKeep64 * 2));
 #pragma unroll
-        for (int k = 0; k < kDrawKeep64; ++k)
-          if (k < nk) m += fmax(0.0, kv[k].x * izp - kv[k].y * izq);
-        masses[t] = m;
+          for (int k = 0; k < kDrawKeep64; ++k) kv[k] = keep[k];
+        }
+        if (nk <= kDrawKeep64) {
+          double m = (d + (rho - rho_e) * a) * izq + sv * g_tie;
+#pragma unroll
+          for (int k = 0; k < kDrawKeep64; ++k)
+            if (k < nk) m += fmax(0.0, kv[k].x * izp - kv[k].y * izq);
+          masses[t] = m;
+        } else {
+          redo = 1;
+        }
       } else {
         redo = 1;
       }

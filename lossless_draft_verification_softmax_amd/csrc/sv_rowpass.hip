@@ -33,38 +33,50 @@ constexpr int kPassUnroll = 4;
 constexpr int kPlanThreads = 1024;
 
 // ---------------------------------------------------------------------------
-// Exclusive prefix sum of an int over the block (fixed order); *total gets
-// the block total.
-__device__ __forceinline__ int32_t block_excl_scan_i(int32_t v, int32_t* lds, int32_t* total) {
+// Exclusive prefix sums of two ints over the block (fixed order, one pair of
+// barriers for both); tot gets the block totals.
+__device__ __forceinline__ int2 block_excl_scan_i2(int2 v, int2* lds, int2* tot) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  int32_t x = v;
+  int2 x = v;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    const int32_t o = __shfl_up(x, d);
-    if (lane >= d) x += o;
+    const int ox = __shfl_up(x.x, d), oy = __shfl_up(x.y, d);
+    if (lane >= d) {
+      x.x += ox;
+      x.y += oy;
+    }
   }
   if (lane == kWave - 1) lds[wave] = x;
   lds_barrier();
-  int32_t base = 0, tot = 0;
+  int2 base = make_int2(0, 0), t = make_int2(0, 0);
   for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
-    if (w < wave) base += lds[w];
-    tot += lds[w];
+    const int2 o = lds[w];
+    if (w < wave) {
+      base.x += o.x;
+      base.y += o.y;
+    }
+    t.x += o.x;
+    t.y += o.y;
   }
   lds_barrier();
-  *total = tot;
-  return base + x - v;
+  *tot = t;
+  return make_int2(base.x + x.x - v.x, base.y + x.y - v.y);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
-  __shared__ int32_t lds[kPlanThreads / kWave];
+  __shared__ int2 lds[kPlanThreads / kWave];
   int32_t carry_pairs = 0, carry_singles = 0;
   for (int base = 0; base < p.B; base += kPlanThreads) {
     const int r = base + (int)threadIdx.x;
     int32_t np = 0, ns = 0, n = 0;
     float T = 0.0f;
+    int64_t t0 = 0, d0 = 0;
     if (r < p.B) {
+      // every load of the request at once
       n = p.depth[r];
       T = p.temperature[r];
+      t0 = p.target_row0[r];
+      if (p.draft_row0) d0 = p.draft_row0[r];
       const bool valid = n >= 0 && n <= p.D && temperature_ok(T) &&
                          !(T > 0.0f && n > 0 && p.draft == nullptr);
       if (valid) {
@@ -72,13 +84,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
         ns = (T > 0.0f) ? 1 : n + 1;
       }
     }
-    int32_t tp, ts;
-    const int32_t op = carry_pairs + block_excl_scan_i(np, lds, &tp);
-    const int32_t os = carry_singles + block_excl_scan_i(ns, lds, &ts);
+    int2 tot;
+    const int2 off = block_excl_scan_i2(make_int2(np, ns), lds, &tot);
+    const int32_t op = carry_pairs + off.x;
+    const int32_t os = carry_singles + off.y;
     if (np > 0 || ns > 0) {
       const float sl = (T > 0.0f) ? kLog2e / T : 0.0f;
-      const int64_t t0 = p.target_row0[r];
-      const int64_t d0 = (np > 0) ? p.draft_row0[r] : 0;
       for (int k = 0; k < np; ++k)
         p.plan_pairs[op + k] = PlanItem{t0 + k, d0 + k, ((uint32_t)r << 7) | (uint32_t)k, T, sl, 0u};
       for (int j = 0; j < ns; ++j) {
@@ -86,8 +97,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
         p.plan_singles[os + j] = PlanItem{t0 + k, 0, ((uint32_t)r << 7) | (uint32_t)k, T, sl, 0u};
       }
     }
-    carry_pairs += tp;
-    carry_singles += ts;
+    carry_pairs += tot.x;
+    carry_singles += tot.y;
   }
   if (threadIdx.x == 0) {
     p.plan_counts[0] = carry_pairs;
@@ -99,9 +110,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
     p.shard_tab[threadIdx.x] = (int)threadIdx.x < kMaxShards ? p.tsh[s] : p.dsh[s];
   }
   // The team row pass tells fresh exchange words from stale ones by their tag
-  // (never 0 once written): clear them before every launch.
+  // (never 0 once written): clear the words this launch reads (4 records of
+  // 4 words per team member) before every launch.
+  const int64_t used = p.team > 0 ? (int64_t)p.nteams * p.team * 16 : 0;
   uint4* xch = reinterpret_cast<uint4*>(p.team_xch);
-  for (int i = threadIdx.x; i < kTeamXchWords / 2; i += kPlanThreads) xch[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int64_t i = threadIdx.x; i < used / 2; i += kPlanThreads) xch[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ---------------------------------------------------------------------------

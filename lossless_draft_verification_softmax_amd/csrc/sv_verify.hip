@@ -33,11 +33,16 @@ namespace sv {
 // chunk rather than one per slot.
 constexpr int kMergeChunk = 16;
 
-__device__ __forceinline__ SoftmaxPart merge_row(const float2* parts, int64_t unit, int S1,
+// v holds the first chunk of slots, loaded by the caller (entries past nseg
+// set to the empty state); later chunks are loaded here.
+__device__ __forceinline__ SoftmaxPart merge_row(const float2 (&v0)[kMergeChunk],
+                                                 const float2* parts, int64_t unit, int S1,
                                                  int nseg, float sl) {
   SoftmaxPart s{-INFINITY, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kMergeChunk; ++i) s = merge_parts(s, SoftmaxPart{v0[i].x, v0[i].y}, sl);
   const float2* row = parts + unit * S1;
-  for (int j0 = 0; j0 < nseg; j0 += kMergeChunk) {
+  for (int j0 = kMergeChunk; j0 < nseg; j0 += kMergeChunk) {
     float2 v[kMergeChunk];
 #pragma unroll
     for (int i = 0; i < kMergeChunk; ++i)
@@ -48,10 +53,13 @@ __device__ __forceinline__ SoftmaxPart merge_row(const float2* parts, int64_t un
   return s;
 }
 
-__device__ __forceinline__ ArgMax merge_row_argmax(const float2* parts, int64_t unit, int S1) {
+__device__ __forceinline__ ArgMax merge_row_argmax(const float2 (&v0)[kMergeChunk],
+                                                   const float2* parts, int64_t unit, int S1) {
   ArgMax a{-INFINITY, INT32_MAX};
+#pragma unroll
+  for (int i = 0; i < kMergeChunk; ++i) a = argmax_merge(a, ArgMax{v0[i].x, __float_as_int(v0[i].y)});
   const float2* row = parts + unit * S1;
-  for (int j0 = 0; j0 < S1; j0 += kMergeChunk) {
+  for (int j0 = kMergeChunk; j0 < S1; j0 += kMergeChunk) {
     float2 v[kMergeChunk];
 #pragma unroll
     for (int i = 0; i < kMergeChunk; ++i)
@@ -77,50 +85,80 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
   const int r = blockIdx.x;
   const int k = threadIdx.x;
   const int D = p.D;
+  // Loads in three rounds: the request's scalars; then, independent of each
+  // other, thread k's token and the first chunk of its row states and alpha
+  // partials; then p(d) and q(d).
   const int n = p.depth[r];
   const float T = p.temperature[r];
   const uint32_t rid = p.request_id ? p.request_id[r] : (uint32_t)r;
+  const int64_t trow0 = p.target_row0[r];
+  const int64_t drow0 = p.draft_row0 ? p.draft_row0[r] : 0;
+  const int sync_err = *p.sync_error;
   if (k == 0) s_bits = 0u;
   if (r == 0 && k == 0) *p.fb_count = 0;  // float64 draw queue, filled by k_draw_pick32
-  __syncthreads();
 
   uint32_t bits = 0u;
-  if (*p.sync_error) bits |= SV_BIT_SYNC_TIMEOUT;
+  if (sync_err) bits |= SV_BIT_SYNC_TIMEOUT;
   if (n < 0 || n > D) bits |= SV_BIT_BAD_DEPTH;
   if (!temperature_ok(T)) bits |= SV_BIT_BAD_TEMPERATURE;
   const bool live = (bits == 0u) && k <= n;
   const int64_t unit = (int64_t)r * (D + 1) + k;
+  const bool pair = live && k < n;
+  const bool greedy = T == 0.0f;
+  // slots merged per row: every slot at T = 0 and for a single row, the
+  // pair's slots for a row pair; q only for a T > 0 pair with draft logits
+  const int np_ = live ? ((greedy || !pair) ? p.S1 : p.pair_slots) : 0;
+  const int nq_ = (pair && !greedy && p.draft != nullptr) ? p.pair_slots : 0;
+  const int na_ = (k < D && k < n && !greedy && bits == 0u && p.alpha) ? p.alpha_slots : 0;
+  const int32_t tok_k = (k < D) ? p.tokens[(int64_t)r * D + k] : 0;
+  float2 pv[kMergeChunk], qv[kMergeChunk];
+  float av[kMergeChunk];
+  {
+    const float2* prow_s = p.part_p + unit * p.S1;
+    const float2* qrow_s = p.part_q + unit * p.S1;
+    const float* arow_s = p.part_a + unit * p.S1;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+      pv[i] = (i < np_) ? prow_s[i] : make_float2(-INFINITY, greedy ? __int_as_float(INT32_MAX) : 0.0f);
+      qv[i] = (i < nq_) ? qrow_s[i] : make_float2(-INFINITY, 0.0f);
+      av[i] = (i < na_) ? arow_s[i] : 0.0f;
+    }
+  }
+  int32_t d = 0;
+  if (pair) {
+    d = tok_k;
+    if (d < 0 || (int64_t)d >= p.V) bits |= SV_BIT_BAD_TOKEN;
+  }
+  // p(d), q(d) for the accept test, issued before the merges
+  float pd = 0.0f, qd = 0.0f;
+  if (pair && !greedy && bits == 0u && p.draft != nullptr) {
+    pd = E::load1(row_view<E, SH>(p, false, trow0 + k).at(d), 0);
+    qd = E::load1(row_view<E, SH>(p, true, drow0 + k).at(d), 0);
+  }
 
   bool keep = true;
   float margin = INFINITY;
   float sl = 0.0f;
   SoftmaxPart sp{0.0f, 1.0f}, sq{0.0f, 1.0f};
   ArgMax am{0.0f, 0};
-  int32_t d = 0;
   if (live) {
-    if (k < n) {
-      d = p.tokens[(int64_t)r * D + k];
-      if (d < 0 || (int64_t)d >= p.V) bits |= SV_BIT_BAD_TOKEN;
-    }
-    if (T == 0.0f) {
-      am = merge_row_argmax(p.part_p, unit, p.S1);
+    if (greedy) {
+      am = merge_row_argmax(pv, p.part_p, unit, p.S1);
       if (!finite_f(am.v)) bits |= SV_BIT_BAD_ROW;
       if (k < n) keep = (d == am.i);
     } else {
       sl = kLog2e / T;
-      sp = merge_row(p.part_p, unit, p.S1, (k < n) ? p.pair_slots : p.S1, sl);
+      sp = merge_row(pv, p.part_p, unit, p.S1, np_, sl);
       if (!finite_f(sp.m)) bits |= SV_BIT_BAD_ROW;
       if (k < n) {
         if (p.draft == nullptr) {
           bits |= SV_BIT_BAD_ROW;
         } else {
-          sq = merge_row(p.part_q, unit, p.S1, p.pair_slots, sl);
+          sq = merge_row(qv, p.part_q, unit, p.S1, nq_, sl);
           if (!finite_f(sq.m)) bits |= SV_BIT_BAD_ROW;
         }
       }
       if (k < n && bits == 0u) {
-        const float pd = E::load1(row_view<E, SH>(p, false, p.target_row0[r] + k).at(d), 0);
-        const float qd = E::load1(row_view<E, SH>(p, true, p.draft_row0[r] + k).at(d), 0);
         // log2 p(d) - log2 q(d), each as (x - m) sl - log2 z.
         const float lp = __builtin_fmaf(pd - sp.m, sl, -__log2f(sp.z));
         const float lq = __builtin_fmaf(qd - sq.m, sl, -__log2f(sq.z));
@@ -132,6 +170,7 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       }
     }
   }
+  __syncthreads();  // s_bits cleared
   if (bits) atomicOr(&s_bits, bits);
   __syncthreads();
   const uint32_t all_bits = s_bits;
@@ -159,7 +198,7 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
 
   if (k <= D) {
     int32_t tok = -1;
-    if (k < tau) tok = p.tokens[(int64_t)r * D + k];
+    if (k < tau) tok = tok_k;
     else if (k == tau && T == 0.0f) tok = am.i;
     p.out_tokens[(int64_t)r * (D + 1) + k] = tok;
   }
@@ -169,8 +208,10 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       if (T == 0.0f) {
         a = keep ? 1.0f : 0.0f;
       } else {
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) a += av[i];
         const float* pa = p.part_a + unit * p.S1;
-        for (int j0 = 0; j0 < p.alpha_slots; j0 += kMergeChunk) {
+        for (int j0 = kMergeChunk; j0 < p.alpha_slots; j0 += kMergeChunk) {
           float v[kMergeChunk];
 #pragma unroll
           for (int i = 0; i < kMergeChunk; ++i) v[i] = (j0 + i < p.alpha_slots) ? pa[j0 + i] : 0.0f;
@@ -191,8 +232,8 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       st.mode = kDrawNone;
     } else {
       st.mode = (tau < n) ? kDrawResidual : kDrawBonus;
-      st.prow = p.target_row0[r] + tau;
-      st.qrow = (tau < n) ? p.draft_row0[r] + tau : -1;
+      st.prow = trow0 + tau;
+      st.qrow = (tau < n) ? drow0 + tau : -1;
       st.sl = sl;
       st.T = T;
       st.mp = sp.m;
