@@ -397,7 +397,8 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
   float acc = 0.0f;
   if (ok) {
     const float kp = exp2_fast(mslp - cp), kq = exp2_fast(mslq - cq);
-    const float r = kp > 0x1p-60f ? kq / kp : 0.0f;
+    // kp in (2^-60, 1]: the hardware reciprocal (1 ulp) instead of a division
+    const float r = kp > 0x1p-60f ? kq * __builtin_amdgcn_rcpf(kp) : 0.0f;
     // chunks of G 16-byte vectors of each row
     constexpr int G = H >= 2 ? 2 : 1;
     float sum = 0.0f;
@@ -406,11 +407,14 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
       float m[4 * G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
+        // ep and eq r are non-negative floats, which order as their bit
+        // patterns do: an integer minimum, with no canonicalisation of the
+        // values read back from LDS
         const uint4 a = ex[c + h], q = ex[H + c + h];
-        m[4 * h + 0] = fminf(__uint_as_float(a.x), __uint_as_float(q.x) * r);
-        m[4 * h + 1] = fminf(__uint_as_float(a.y), __uint_as_float(q.y) * r);
-        m[4 * h + 2] = fminf(__uint_as_float(a.z), __uint_as_float(q.z) * r);
-        m[4 * h + 3] = fminf(__uint_as_float(a.w), __uint_as_float(q.w) * r);
+        m[4 * h + 0] = __uint_as_float(min(a.x, __float_as_uint(__uint_as_float(q.x) * r)));
+        m[4 * h + 1] = __uint_as_float(min(a.y, __float_as_uint(__uint_as_float(q.y) * r)));
+        m[4 * h + 2] = __uint_as_float(min(a.z, __float_as_uint(__uint_as_float(q.z) * r)));
+        m[4 * h + 3] = __uint_as_float(min(a.w, __float_as_uint(__uint_as_float(q.w) * r)));
       }
 #pragma unroll
       for (int w = 1; w < 4 * G; w <<= 1) {
