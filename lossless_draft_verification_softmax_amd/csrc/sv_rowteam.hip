@@ -13,8 +13,10 @@
 // registers.  Nothing is read twice from memory.
 //
 // Each member walks a sequence of units: its team's row pairs, then its
-// team's single rows (bonus rows at T > 0 and all target rows at T = 0),
-// always its own slice of the row.
+// team's single rows (bonus rows at T > 0 and all target rows at T = 0) two
+// at a time, always its own slice of the row.  A unit of two single rows
+// holds the second one in the draft buffer; each row keeps its own
+// temperature and kind (arg max at T = 0) and its own partial slot.
 //
 // Workgroup layout: waves 0..14 are data waves, wave 15 is the communication
 // wave.  The data waves only load rows and reduce them to per-wave states
@@ -74,7 +76,7 @@ struct Regs {
 // A unit of work, held in scalar registers.
 struct UnitDesc {
   int64_t trow;     // target row index
-  int64_t drow;     // draft row index (row pairs)
+  int64_t drow;     // draft row index (row pairs); second target row of a single unit, or -1
   uint32_t code;    // request << 7 | position
   float sl;         // log2(e) / T
   int32_t kind;     // 0 none, 1 row pair, 2 single row, 3 single row at T = 0
@@ -146,7 +148,7 @@ __device__ __forceinline__ LanePtrs<NV> lane_ptrs(const VerifyParams& p, const S
 // Shared state, double-buffered by unit parity (see the step order above).
 struct TeamLds {
   SoftmaxPart sm[2][kDataWaves][2];  // per-wave (max, sum) of p and q
-  ArgMax am[2][kDataWaves];          // per-wave arg max at T = 0
+  ArgMax am[2][kDataWaves][2];       // per-wave arg max at T = 0, per single row
   float acc[2][kDataWaves];          // per-wave sum of min(p, q)
   float c[2][2];                     // team log2 normalisers of p and q
   int ok[2];
@@ -176,11 +178,21 @@ __device__ __forceinline__ UnitDesc no_unit() {
   return u;
 }
 
+// Single rows per team member: the team's singles are items team,
+// team + nteams, ...; single unit j holds the team's singles 2j and 2j + 1.
+__device__ __forceinline__ int64_t single_units(int64_t my_singles) {
+  return (my_singles + 1) / 2;
+}
+
+__device__ __forceinline__ int64_t team_single(const VerifyParams& p, int team, int64_t m) {
+  return (int64_t)team + (int64_t)p.nteams * m;
+}
+
 // Unit j of this workgroup: its team's row pairs (items team, team + nteams,
-// ...) and then its team's single rows (dealt the same way); the workgroup
-// always takes slice `member` of the row.
+// ...) and then its team's single rows (dealt the same way), two per unit;
+// the workgroup always takes slice `member` of the row.
 __device__ __forceinline__ UnitDesc unit_at(const VerifyParams& p, int64_t j, int64_t n,
-                                            int team, int64_t my_pairs) {
+                                            int team, int64_t my_pairs, int64_t my_singles) {
   if (j >= n) return no_unit();
   UnitDesc u;
   if (j < my_pairs) {
@@ -188,11 +200,13 @@ __device__ __forceinline__ UnitDesc unit_at(const VerifyParams& p, int64_t j, in
     u.kind = 1;
     u.ordinal = (int32_t)j;
   } else {
-    const int64_t it = (int64_t)team + (int64_t)p.nteams * (j - my_pairs);
+    const int64_t m = 2 * (j - my_pairs);
+    const int64_t it = team_single(p, team, m);
     load_item(u, p.plan_singles, it);
     const __attribute__((address_space(4))) PlanItem* c =
         (const __attribute__((address_space(4))) PlanItem*)p.plan_singles;
     u.kind = (c[it].T == 0.0f) ? 3 : 2;
+    u.drow = (m + 1 < my_singles) ? c[it + p.nteams].trow : -1;
     u.ordinal = 0;
   }
   return u;
@@ -220,9 +234,10 @@ __device__ __forceinline__ const uint4* neg_inf_line() {
   return &kNegInfLine[E::kPerVec == 8 ? 0 : 1];
 }
 
-// Issues the 2 * NV loads of a unit.  Vectors outside the slice, the draft
-// row of a single row and every vector of an empty unit read the -inf line
-// instead.
+// Issues the 2 * NV loads of a unit: the target and draft rows of a pair,
+// or the two target rows of a single unit.  Vectors outside the slice, the
+// absent second row of a single unit and every vector of an empty unit read
+// the -inf line instead.
 template <typename E, int NV, bool SH>
 __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc& u,
                                           const Slice& sc, const LanePtrs<NV>& lp, Regs<NV>& R,
@@ -231,6 +246,7 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
   constexpr int VEC = E::kPerVec;
   const int64_t nvec = u.kind == 0 ? 0 : sc.nvec;
   const bool pair = u.kind == 1;
+  const bool second = pair || u.drow >= 0;
   if constexpr (SH) {
     const int64_t tb = u.trow * p.stride * (int64_t)sizeof(S);
     const int64_t db = u.drow * p.stride * (int64_t)sizeof(S);
@@ -239,19 +255,20 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
       const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
       const bool in = v < nvec;
       const void* pa = in ? (const void*)(lp.t[i] + tb) : (const void*)dummy;
-      const void* qa = (in && pair) ? (const void*)(lp.d[i] + db) : (const void*)dummy;
+      const char* qbase = pair ? lp.d[i] : lp.t[i];
+      const void* qa = (in && second) ? (const void*)(qbase + db) : (const void*)dummy;
       R.p[i] = load16(pa);
       R.q[i] = load16(qa);
     }
   } else {
     const S* prow = row_ptr<E>(sc.tgt, u.trow, p.stride) + sc.lo;
-    const S* qrow = row_ptr<E>(sc.dft, u.drow, p.stride) + sc.lo;
+    const S* qrow = row_ptr<E>(pair ? sc.dft : sc.tgt, u.drow, p.stride) + sc.lo;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
       const bool in = v < nvec;
       const void* pa = in ? (const void*)(prow + v * VEC) : (const void*)dummy;
-      const void* qa = (in && pair) ? (const void*)(qrow + v * VEC) : (const void*)dummy;
+      const void* qa = (in && second) ? (const void*)(qrow + v * VEC) : (const void*)dummy;
       R.p[i] = load16(pa);
       R.q[i] = load16(qa);
     }
@@ -294,21 +311,20 @@ __device__ __forceinline__ SoftmaxPart softmax_keep(const float (&x)[N], float s
   return {cm, acc};
 }
 
-// First pass of a unit over this thread's vectors: (max, sum) of the slice
-// for p (and q for a pair), or the slice arg max at T = 0; one state per
-// wave into LDS.
+// First pass of one single row (a target row) held in V: the slice arg max
+// at T = 0 (kind 3), else the slice (max, sum) with log2(e)/T = sl; one
+// state per wave into LDS entry `slot` (0 or 1) of the unit's states.
 template <typename E, int NV>
-__device__ __forceinline__ void first_pass_data(const VerifyParams& p, const UnitDesc& u,
-                                                const Slice& sc, const Regs<NV>& R, TeamLds& L,
-                                                int b, float (&e)[2 * NV * E::kPerVec],
-                                                float& mslp, float& mslq) {
+__device__ __forceinline__ void single_first(const VerifyParams& p, const Slice& sc,
+                                             const uint4 (&V)[NV], int64_t trow, int kind,
+                                             float sl, TeamLds& L, int b, int slot,
+                                             float (&e)[2 * NV * E::kPerVec]) {
   constexpr int VEC = E::kPerVec;
-  if (u.kind == 0) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int64_t lo = sc.lo, vhi = sc.vhi, hi = sc.hi;
-  const auto* prow = row_ptr<E>(sc.tgt, u.trow, p.stride);
-  if (u.kind == 3) {
+  const auto* prow = row_ptr<E>(sc.tgt, trow, p.stride);
+  if (kind == 3) {
     // arg max of this thread's vectors: best vector in order, then its first
     // maximal element (NaN propagates through the maximum)
     float best = -INFINITY;
@@ -316,7 +332,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       float x[VEC];
-      E::unpack(R.p[i], x);
+      E::unpack(V[i], x);
       float cm = x[0];
 #pragma unroll
       for (int j = 1; j < VEC; ++j) cm = vmax(cm, x[j]);
@@ -330,7 +346,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
       for (int i = 0; i < NV; ++i) {
         if (i != bi) continue;
         float x[VEC];
-        E::unpack(R.p[i], x);
+        E::unpack(V[i], x);
         const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
 #pragma unroll
         for (int j = VEC - 1; j >= 0; --j)
@@ -343,29 +359,63 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
       ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
       a = argmax_merge(a, o);
     }
-    if (lane == 0) L.am[b][wave] = a;
+    if (lane == 0) L.am[b][wave][slot] = a;
     return;
   }
+  float x[VEC * NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) E::unpack(V[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
+  float msl;
+  SoftmaxPart sp = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[0]), msl);
+  for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
+    float x1[1] = {E::load1(prow, i - sc.toff)};
+    softmax_group<1>(sp, x1, sl);
+  }
+  sp = wave_merge_ref(sp, sl);
+  if (lane == 0) L.sm[b][wave][slot] = sp;
+}
+
+// First pass of a unit over this thread's vectors: for a row pair the slice
+// (max, sum) of p and q, keeping the exponentials; for a single unit each of
+// its rows by single_first (the second row's temperature is read from its
+// work item, item2).  One state per wave and row into LDS.
+template <typename E, int NV>
+__device__ __forceinline__ void first_pass_data(const VerifyParams& p, const UnitDesc& u,
+                                                const Slice& sc, const Regs<NV>& R, TeamLds& L,
+                                                int b, float (&e)[2 * NV * E::kPerVec],
+                                                float& mslp, float& mslq, int64_t item2) {
+  constexpr int VEC = E::kPerVec;
+  if (u.kind == 0) return;
+  if (u.kind != 1) {
+    single_first<E, NV>(p, sc, R.p, u.trow, u.kind, u.sl, L, b, 0, e);
+    if (u.drow >= 0) {
+      const __attribute__((address_space(4))) PlanItem* c =
+          (const __attribute__((address_space(4))) PlanItem*)p.plan_singles;
+      const float T2 = c[item2].T, sl2 = c[item2].sl;
+      single_first<E, NV>(p, sc, R.q, u.drow, T2 == 0.0f ? 3 : 2, sl2, L, b, 1, e);
+    }
+    return;
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t vhi = sc.vhi, hi = sc.hi;
+  const auto* prow = row_ptr<E>(sc.tgt, u.trow, p.stride);
   const float sl = u.sl;
   float x[VEC * NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) E::unpack(R.p[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
-  SoftmaxPart sq{-INFINITY, 0.0f};
   SoftmaxPart sp = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[0]), mslp);
   for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
     float x1[1] = {E::load1(prow, i - sc.toff)};
     softmax_group<1>(sp, x1, sl);
   }
-  if (u.kind == 1) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      E::unpack(R.q[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
-    sq = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[VEC * NV]), mslq);
-    const auto* qrow = row_ptr<E>(sc.dft, u.drow, p.stride);
-    for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
-      float x1[1] = {E::load1(qrow, i - sc.toff)};
-      softmax_group<1>(sq, x1, sl);
-    }
+  for (int i = 0; i < NV; ++i) E::unpack(R.q[i], *reinterpret_cast<float(*)[VEC]>(&x[i * VEC]));
+  SoftmaxPart sq = softmax_keep<VEC * NV>(x, sl, *reinterpret_cast<float(*)[VEC * NV]>(&e[VEC * NV]), mslq);
+  const auto* qrow = row_ptr<E>(sc.dft, u.drow, p.stride);
+  for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads) {
+    float x1[1] = {E::load1(qrow, i - sc.toff)};
+    softmax_group<1>(sq, x1, sl);
   }
   sp = wave_merge_ref(sp, sl);
   sq = wave_merge_ref(sq, sl);
@@ -437,43 +487,79 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
 // ---------------------------------------------------------------------------
 // Communication wave.
 
+// The second row of a single unit, as the communication wave holds it.
+struct SecondRow {
+  uint32_t code;  // request << 7 | position
+  float sl;       // log2(e) / T
+  int32_t kind;   // 0 none, 2 single row, 3 single row at T = 0
+};
+
+__device__ __forceinline__ int64_t code_slot(const VerifyParams& p, uint32_t code, int member) {
+  const int64_t unit = (int64_t)(code >> 7) * (p.D + 1) + (code & 127u);
+  return unit * p.S1 + member;
+}
+
+// A single row's slice state from the data waves' states (entry `slot` of
+// the unit's), into its partial slot; `sum` is reduced alongside.
+__device__ __forceinline__ void comm_single_softmax(const VerifyParams& p, const TeamLds& L, int b,
+                                                    int slot, float sl, int64_t dst, float& sum) {
+  const int lane = threadIdx.x & (kWave - 1);
+  SoftmaxPart sp{-INFINITY, 0.0f}, none{-INFINITY, 0.0f};
+  if (lane < kDataWaves) sp = L.sm[b][lane][slot];
+  wave_merge_ref2(sp, none, false, sum, sl);
+  if (lane == 0) p.part_p[dst] = make_float2(sp.m, sp.z);
+}
+
+__device__ __forceinline__ void comm_single_argmax(const VerifyParams& p, const TeamLds& L, int b,
+                                                   int slot, int64_t dst) {
+  const int lane = threadIdx.x & (kWave - 1);
+  ArgMax a = (lane < kDataWaves) ? L.am[b][lane][slot] : ArgMax{-INFINITY, INT32_MAX};
+  for (int m = 1; m < kWave; m <<= 1) {
+    ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
+    a = argmax_merge(a, o);
+  }
+  if (lane == 0) p.part_p[dst] = make_float2(a.v, __int_as_float(a.i));
+}
+
 // Combines the data waves' first-pass states of a unit (a fixed reduction
 // tree over the lanes), writes the partial slots and publishes a pair.
 __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const UnitDesc& u,
-                                                const TeamLds& L, int b, int team, int member,
-                                                const UnitDesc& ua, int ba) {
+                                                const SecondRow& u2, const TeamLds& L, int b,
+                                                int team, int member, const UnitDesc& ua, int ba) {
   const int lane = threadIdx.x & (kWave - 1);
   // the second-pass sums of unit ua are reduced alongside (same tree as
   // a lone wave sum)
   const bool fin = wants_alpha(p, ua);
   float acc = (fin && lane < kDataWaves) ? L.acc[ba][lane] : 0.0f;
-  if (u.kind == 0 || u.kind == 3) {
-    if (fin) {
-      acc = wave_sum(acc);
-      if (lane == 0) p.part_a[unit_slot(p, ua, member)] = acc;
+  if (u.kind != 1) {
+    // single unit (or none): its first row, with the second-pass sum of unit
+    // ua reduced alongside a softmax row or alone, then its second row
+    if (u.kind == 2) {
+      comm_single_softmax(p, L, b, 0, u.sl, code_slot(p, u.code, member), acc);
+    } else {
+      if (fin) acc = wave_sum(acc);
+      if (u.kind == 3) comm_single_argmax(p, L, b, 0, code_slot(p, u.code, member));
     }
-    if (u.kind == 0) return;
-  }
-  const int64_t slot = unit_slot(p, u, member);
-  if (u.kind == 3) {
-    ArgMax a = (lane < kDataWaves) ? L.am[b][lane] : ArgMax{-INFINITY, INT32_MAX};
-    for (int m = 1; m < kWave; m <<= 1) {
-      ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
-      a = argmax_merge(a, o);
+    if (fin && lane == 0) p.part_a[unit_slot(p, ua, member)] = acc;
+    if (u2.kind == 2) {
+      float none = 0.0f;
+      comm_single_softmax(p, L, b, 1, u2.sl, code_slot(p, u2.code, member), none);
+    } else if (u2.kind == 3) {
+      comm_single_argmax(p, L, b, 1, code_slot(p, u2.code, member));
     }
-    if (lane == 0) p.part_p[slot] = make_float2(a.v, __int_as_float(a.i));
     return;
   }
+  const int64_t slot = unit_slot(p, u, member);
   const float sl = u.sl;
   SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
   if (lane < kDataWaves) {
     sp = L.sm[b][lane][0];
     sq = L.sm[b][lane][1];
   }
-  wave_merge_ref2(sp, sq, u.kind == 1, acc, sl);
+  wave_merge_ref2(sp, sq, true, acc, sl);
   if (lane == 0) {
     p.part_p[slot] = make_float2(sp.m, sp.z);
-    if (u.kind == 1) p.part_q[slot] = make_float2(sq.m, sq.z);
+    p.part_q[slot] = make_float2(sq.m, sq.z);
     if (fin) p.part_a[unit_slot(p, ua, member)] = acc;
   }
   if (wants_alpha(p, u) && lane < 4) {
@@ -581,7 +667,7 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
       (in_team && n_pairs > team) ? (n_pairs - 1 - team) / p.nteams + 1 : 0;
   const int64_t my_singles =
       (in_team && n_singles > team) ? (n_singles - 1 - team) / p.nteams + 1 : 0;
-  const int64_t n = my_pairs + my_singles;
+  const int64_t n = my_pairs + single_units(my_singles);
   const Slice sc = make_slice<E, SH>(p, member);
 
   // Both roles run steps s = 0 .. n with one barrier each, then a last one.
@@ -598,10 +684,10 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     LanePtrs<NV> lp{};
     if constexpr (SH) lp = lane_ptrs<E, NV>(p, sc);
     Regs<NV> R0, R1, R2;
-    UnitDesc U0 = unit_at(p, 0, n, team, my_pairs);
-    UnitDesc U1 = unit_at(p, 1, n, team, my_pairs);
+    UnitDesc U0 = unit_at(p, 0, n, team, my_pairs, my_singles);
+    UnitDesc U1 = unit_at(p, 1, n, team, my_pairs, my_singles);
     UnitDesc U2 = no_unit();
-    UnitDesc un = unit_at(p, 2, n, team, my_pairs);
+    UnitDesc un = unit_at(p, 2, n, team, my_pairs, my_singles);
     UnitDesc up = no_unit();  // unit s - 1 (parked)
     float mslp1 = 0.0f, mslq1 = 0.0f;
     load_unit<E, NV, SH>(p, U0, sc, lp, R0, dummy);
@@ -611,10 +697,11 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
                     UnitDesc& Ul) {
       Ul = un;
       load_unit<E, NV, SH>(p, Ul, sc, lp, Rl, dummy);
-      un = unit_at(p, s + 3, n, team, my_pairs);
+      un = unit_at(p, s + 3, n, team, my_pairs, my_singles);
       float e[2 * NV * E::kPerVec];
       float mslp = 0.0f, mslq = 0.0f;
-      first_pass_data<E, NV>(p, Uf, sc, Rf, L, (int)(s & 1), e, mslp, mslq);
+      first_pass_data<E, NV>(p, Uf, sc, Rf, L, (int)(s & 1), e, mslp, mslq,
+                             team_single(p, team, 2 * (s - my_pairs) + 1));
       // Swap: unit s - 1 out of the parking slot, unit s in (each thread
       // overwrites only the entries it has just read), before the barrier so
       // that the LDS traffic overlaps the other waves' first passes.
@@ -651,18 +738,25 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     // issues ahead of the data waves that share its SIMD.
     __builtin_amdgcn_s_setprio(3);
     const int lane = threadIdx.x & (kWave - 1);
-    // Work items of units base .. base + 63, one per lane (code, T, log2(e)/T),
-    // loaded with one vector load per lane for 64 steps: a scalar load per
-    // step would be waited for at every barrier.
-    uint4 blk = make_uint4(0u, 0u, 0u, 0u);
+    // Work items of units base .. base + 63, one per lane (code, T, log2(e)/T;
+    // blk2 the second row of a single unit), loaded with vector loads per lane
+    // for 64 steps: a scalar load per step would be waited for at every
+    // barrier.
+    uint4 blk = make_uint4(0u, 0u, 0u, 0u), blk2 = make_uint4(0u, 0u, 0u, 0u);
     auto load_block = [&](int64_t base) {
       const int64_t j = base + lane;
       blk = make_uint4(0u, 0u, 0u, 0u);
+      blk2 = make_uint4(0u, 0u, 0u, 0u);
       if (j < n) {
-        const PlanItem* it = (j < my_pairs)
-                                 ? p.plan_pairs + ((int64_t)team + (int64_t)p.nteams * j)
-                                 : p.plan_singles + ((int64_t)team + (int64_t)p.nteams * (j - my_pairs));
-        blk = *reinterpret_cast<const uint4*>(&it->code);
+        if (j < my_pairs) {
+          const PlanItem* it = p.plan_pairs + ((int64_t)team + (int64_t)p.nteams * j);
+          blk = *reinterpret_cast<const uint4*>(&it->code);
+        } else {
+          const int64_t m = 2 * (j - my_pairs);
+          blk = *reinterpret_cast<const uint4*>(&p.plan_singles[team_single(p, team, m)].code);
+          if (m + 1 < my_singles)
+            blk2 = *reinterpret_cast<const uint4*>(&p.plan_singles[team_single(p, team, m + 1)].code);
+        }
       }
       // Wait for the block here, once per 64 steps: the compiler cannot
       // track this conditional load across iterations and would otherwise
@@ -682,13 +776,25 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
       u.ordinal = (s < my_pairs) ? (int32_t)s : 0;
       return u;
     };
+    auto comm_second = [&](int64_t s) {
+      SecondRow r{0u, 0.0f, 0};
+      if (s < n && s >= my_pairs && 2 * (s - my_pairs) + 1 < my_singles) {
+        const int l = (int)(s & 63);
+        r.code = (uint32_t)__builtin_amdgcn_readlane((int)blk2.x, l);
+        const float T2 = __int_as_float(__builtin_amdgcn_readlane((int)blk2.y, l));
+        r.sl = __int_as_float(__builtin_amdgcn_readlane((int)blk2.z, l));
+        r.kind = (T2 == 0.0f) ? 3 : 2;
+      }
+      return r;
+    };
     bool failed = false;
     UnitDesc um2 = no_unit(), um1 = no_unit();
     for (int64_t s = 0; s <= n; ++s) {
       lds_barrier();
       if ((s & 63) == 0) load_block(s);
       const UnitDesc u = comm_unit(s);
-      first_pass_comm(p, u, L, (int)(s & 1), team, member, um2, (int)((s - 2) & 1));
+      first_pass_comm(p, u, comm_second(s), L, (int)(s & 1), team, member, um2,
+                      (int)((s - 2) & 1));
       if (wants_alpha(p, u)) team_wait_comm(p, u, L, (int)(s & 1), team, member, failed);
       um2 = um1;
       um1 = u;
