@@ -311,6 +311,63 @@ __device__ __forceinline__ SoftmaxPart softmax_keep(const float (&x)[N], float s
   return {cm, acc};
 }
 
+// Arg max of a wave's share of a bf16 row slice held in V, by integer keys:
+// an element's key is its 16 bits mapped to unsigned order (the sign bit
+// flipped for a positive value, every bit for a negative one) above 15 minus
+// its position among the thread's 8 NV elements, so that the unsigned
+// maximum of a thread's keys is its largest value at its first position;
+// the lane and the vector index then join the position, and one 32-bit
+// maximum over the wave gives the wave's first maximal column.  Returns
+// false when the float path must decide: a maximum of zero (-0 and +0 tie
+// as values) or a slice with a ragged tail.  A NaN anywhere in the wave's
+// share gives the state (NaN, none), an all -inf share (-inf, none).
+template <int NV>
+__device__ __forceinline__ bool bf16_argmax_keys(const uint4 (&V)[NV], const Slice& sc, ArgMax& out) {
+  typedef short short2v __attribute__((ext_vector_type(2)));
+  static_assert(NV <= 2, "positions must fit 4 key bits");
+  if (sc.vhi < sc.hi) return false;
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint32_t d[4] = {V[i].x, V[i].y, V[i].z, V[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // 0xffff in each half holding a negative value
+      const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(short2v, d[k]) >> (short)15);
+      const uint32_t o = d[k] ^ (neg | 0x80008000u);
+      const uint32_t klo = (o << 16) | (uint32_t)(15 - (8 * i + 2 * k));
+      const uint32_t khi = (o & 0xFFFF0000u) | (uint32_t)(14 - (8 * i + 2 * k));
+      kmax = max(max(kmax, klo), khi);
+      kmin = min(min(kmin, klo), khi);
+    }
+  }
+  // NaN: above +inf (0xff80 maps to 0xff80) or below -inf (0x007f)
+  const bool nan = __ballot(kmax >= 0xFF810000u || kmin < 0x007F0000u) != 0ull;
+  const uint32_t local = 15u - (kmax & 15u);  // vector * 8 + element
+  // the lane, taken here rather than kept live across the row loop
+  const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const uint32_t rank = ((local >> 3) << 9) | (lane << 3) | (local & 7u);
+  const uint32_t wk = (uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(wave_allreduce(
+      __uint_as_float((kmax & 0xFFFF0000u) | (0xFFFFu - rank)),
+      [](float a, float b) { return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b))); })));
+  const uint32_t ord = wk >> 16;
+  if (nan) {
+    out = ArgMax{__int_as_float(0x7fc00000), INT32_MAX};
+    return true;
+  }
+  if (ord == 0x8000u) return false;  // +0
+  if (ord == 0x007Fu) {  // -inf
+    out = ArgMax{-INFINITY, INT32_MAX};
+    return true;
+  }
+  const uint32_t bits = ord >= 0x8000u ? (ord ^ 0x8000u) : (ord ^ 0xFFFFu);
+  const uint32_t r = 0xFFFFu - (wk & 0xFFFFu);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t v = (int64_t)(wave * kWave + (int)((r >> 3) & 63u)) + (int64_t)kDataThreads * (r >> 9);
+  out = ArgMax{__uint_as_float(bits << 16), (int32_t)(sc.lo + v * 8 + (r & 7u))};
+  return true;
+}
+
 // First pass of one single row (a target row) held in V: the slice arg max
 // at T = 0 (kind 3), else the slice (max, sum) with log2(e)/T = sl; one
 // state per wave into LDS entry `slot` (0 or 1) of the unit's states.
@@ -325,6 +382,13 @@ __device__ __forceinline__ void single_first(const VerifyParams& p, const Slice&
   const int64_t lo = sc.lo, vhi = sc.vhi, hi = sc.hi;
   const auto* prow = row_ptr<E>(sc.tgt, trow, p.stride);
   if (kind == 3) {
+    if constexpr (E::kPerVec == 8) {
+      ArgMax w;
+      if (bf16_argmax_keys<NV>(V, sc, w)) {
+        if (lane == 0) L.am[b][wave][slot] = w;
+        return;
+      }
+    }
     // arg max of this thread's vectors: best vector in order, then its first
     // maximal element (NaN propagates through the maximum)
     float best = -INFINITY;
