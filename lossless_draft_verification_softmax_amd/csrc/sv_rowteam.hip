@@ -389,40 +389,38 @@ __device__ __forceinline__ void single_first(const VerifyParams& p, const Slice&
         return;
       }
     }
-    // arg max of this thread's vectors: best vector in order, then its first
-    // maximal element (NaN propagates through the maximum)
-    float best = -INFINITY;
-    int bi = -1;
+    // arg max of this thread's vectors: the maximum (NaN propagates), then
+    // its first position by a compare-select walk from the last element; a
+    // maximum of -inf or NaN has no position
+    float xs[NV][VEC];
+    float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      float x[VEC];
-      E::unpack(V[i], x);
-      float cm = x[0];
+      E::unpack(V[i], xs[i]);
 #pragma unroll
-      for (int j = 1; j < VEC; ++j) cm = vmax(cm, x[j]);
-      const bool up = cm > best;
-      best = vmax(best, cm);
-      bi = up ? i : bi;
+      for (int j = 0; j < VEC; ++j) mx = vmax(mx, xs[i][j]);
     }
-    ArgMax a{best, INT32_MAX};
-    if (best == best && bi >= 0) {
+    ArgMax a{mx, INT32_MAX};
+    if (mx > -INFINITY) {
+      const int32_t base = (int32_t)(lo + (int64_t)threadIdx.x * VEC);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        if (i != bi) continue;
-        float x[VEC];
-        E::unpack(V[i], x);
-        const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
+      for (int i = NV - 1; i >= 0; --i)
 #pragma unroll
         for (int j = VEC - 1; j >= 0; --j)
-          if (x[j] == best) a.i = (int32_t)(lo + v * VEC + j);
-      }
+          if (xs[i][j] == mx) a.i = base + (kDataThreads * i * VEC + j);
     }
     for (int64_t i = vhi + threadIdx.x; i < hi; i += kDataThreads)
       a = argmax_merge(a, ArgMax{E::load1(prow, i - sc.toff), (int32_t)i});
-    for (int m = 1; m < kWave; m <<= 1) {
-      ArgMax o{__shfl_xor(a.v, m), __shfl_xor(a.i, m)};
-      a = argmax_merge(a, o);
-    }
+    // wave merge: the largest value (a NaN in any lane wins, by ballot), then
+    // the smallest position among the lanes holding it (-0 and +0 compare
+    // equal, as in the per-element walk)
+    const bool nan = __ballot(a.v != a.v) != 0ull;
+    const float wm = wave_allreduce(a.v, [](float x, float y) { return fmaxf(x, y); });
+    const int32_t wi = __float_as_int(wave_allreduce(
+        __int_as_float(a.v == wm ? a.i : INT32_MAX),
+        [](float x, float y) { return __int_as_float(min(__float_as_int(x), __float_as_int(y))); }));
+    a = nan ? ArgMax{__int_as_float(0x7fc00000), INT32_MAX}
+            : ArgMax{wm, wm == -INFINITY ? INT32_MAX : wi};
     if (lane == 0) L.am[b][wave][slot] = a;
     return;
   }
