@@ -179,9 +179,11 @@ __device__ __forceinline__ UnitDesc no_unit() {
 }
 
 // Single rows per team member: the team's singles are items team,
-// team + nteams, ...; single unit j holds the team's singles 2j and 2j + 1.
-__device__ __forceinline__ int64_t single_units(int64_t my_singles) {
-  return (my_singles + 1) / 2;
+// team + nteams, ...; single unit j holds the team's singles PS j .. PS j +
+// PS - 1 (PS = 2, or 1 where the pairing's registers do not fit: the
+// vocabulary-sharded instantiation).
+__device__ __forceinline__ int64_t single_units(int64_t my_singles, int PS) {
+  return (my_singles + PS - 1) / PS;
 }
 
 __device__ __forceinline__ int64_t team_single(const VerifyParams& p, int team, int64_t m) {
@@ -192,7 +194,8 @@ __device__ __forceinline__ int64_t team_single(const VerifyParams& p, int team, 
 // ...) and then its team's single rows (dealt the same way), two per unit;
 // the workgroup always takes slice `member` of the row.
 __device__ __forceinline__ UnitDesc unit_at(const VerifyParams& p, int64_t j, int64_t n,
-                                            int team, int64_t my_pairs, int64_t my_singles) {
+                                            int team, int64_t my_pairs, int64_t my_singles,
+                                            int PS) {
   if (j >= n) return no_unit();
   UnitDesc u;
   if (j < my_pairs) {
@@ -200,13 +203,13 @@ __device__ __forceinline__ UnitDesc unit_at(const VerifyParams& p, int64_t j, in
     u.kind = 1;
     u.ordinal = (int32_t)j;
   } else {
-    const int64_t m = 2 * (j - my_pairs);
+    const int64_t m = PS * (j - my_pairs);
     const int64_t it = team_single(p, team, m);
     load_item(u, p.plan_singles, it);
     const __attribute__((address_space(4))) PlanItem* c =
         (const __attribute__((address_space(4))) PlanItem*)p.plan_singles;
     u.kind = (c[it].T == 0.0f) ? 3 : 2;
-    u.drow = (m + 1 < my_singles) ? c[it + p.nteams].trow : -1;
+    u.drow = (PS == 2 && m + 1 < my_singles) ? c[it + p.nteams].trow : -1;
     u.ordinal = 0;
   }
   return u;
@@ -238,7 +241,7 @@ __device__ __forceinline__ const uint4* neg_inf_line() {
 // or the two target rows of a single unit.  Vectors outside the slice, the
 // absent second row of a single unit and every vector of an empty unit read
 // the -inf line instead.
-template <typename E, int NV, bool SH>
+template <typename E, int NV, bool SH, int PS>
 __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc& u,
                                           const Slice& sc, const LanePtrs<NV>& lp, Regs<NV>& R,
                                           const uint4* dummy) {
@@ -246,7 +249,7 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
   constexpr int VEC = E::kPerVec;
   const int64_t nvec = u.kind == 0 ? 0 : sc.nvec;
   const bool pair = u.kind == 1;
-  const bool second = pair || u.drow >= 0;
+  const bool second = pair || (PS == 2 && u.drow >= 0);
   if constexpr (SH) {
     const int64_t tb = u.trow * p.stride * (int64_t)sizeof(S);
     const int64_t db = u.drow * p.stride * (int64_t)sizeof(S);
@@ -255,14 +258,14 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
       const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
       const bool in = v < nvec;
       const void* pa = in ? (const void*)(lp.t[i] + tb) : (const void*)dummy;
-      const char* qbase = pair ? lp.d[i] : lp.t[i];
+      const char* qbase = (PS == 2 && !pair) ? lp.t[i] : lp.d[i];
       const void* qa = (in && second) ? (const void*)(qbase + db) : (const void*)dummy;
       R.p[i] = load16(pa);
       R.q[i] = load16(qa);
     }
   } else {
     const S* prow = row_ptr<E>(sc.tgt, u.trow, p.stride) + sc.lo;
-    const S* qrow = row_ptr<E>(pair ? sc.dft : sc.tgt, u.drow, p.stride) + sc.lo;
+    const S* qrow = row_ptr<E>((PS == 2 && !pair) ? sc.tgt : sc.dft, u.drow, p.stride) + sc.lo;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t v = (int64_t)threadIdx.x + (int64_t)kDataThreads * i;
@@ -441,7 +444,7 @@ __device__ __forceinline__ void single_first(const VerifyParams& p, const Slice&
 // (max, sum) of p and q, keeping the exponentials; for a single unit each of
 // its rows by single_first (the second row's temperature is read from its
 // work item, item2).  One state per wave and row into LDS.
-template <typename E, int NV>
+template <typename E, int NV, int PS>
 __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const UnitDesc& u,
                                                 const Slice& sc, const Regs<NV>& R, TeamLds& L,
                                                 int b, float (&e)[2 * NV * E::kPerVec],
@@ -450,7 +453,7 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
   if (u.kind == 0) return;
   if (u.kind != 1) {
     single_first<E, NV>(p, sc, R.p, u.trow, u.kind, u.sl, L, b, 0, e);
-    if (u.drow >= 0) {
+    if (PS == 2 && u.drow >= 0) {
       const __attribute__((address_space(4))) PlanItem* c =
           (const __attribute__((address_space(4))) PlanItem*)p.plan_singles;
       const float T2 = c[item2].T, sl2 = c[item2].sl;
@@ -729,7 +732,8 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
       (in_team && n_pairs > team) ? (n_pairs - 1 - team) / p.nteams + 1 : 0;
   const int64_t my_singles =
       (in_team && n_singles > team) ? (n_singles - 1 - team) / p.nteams + 1 : 0;
-  const int64_t n = my_pairs + single_units(my_singles);
+  constexpr int PS = SH ? 1 : 2;  // single rows per unit
+  const int64_t n = my_pairs + single_units(my_singles, PS);
   const Slice sc = make_slice<E, SH>(p, member);
 
   // Both roles run steps s = 0 .. n with one barrier each, then a last one.
@@ -746,24 +750,24 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     LanePtrs<NV> lp{};
     if constexpr (SH) lp = lane_ptrs<E, NV>(p, sc);
     Regs<NV> R0, R1, R2;
-    UnitDesc U0 = unit_at(p, 0, n, team, my_pairs, my_singles);
-    UnitDesc U1 = unit_at(p, 1, n, team, my_pairs, my_singles);
+    UnitDesc U0 = unit_at(p, 0, n, team, my_pairs, my_singles, PS);
+    UnitDesc U1 = unit_at(p, 1, n, team, my_pairs, my_singles, PS);
     UnitDesc U2 = no_unit();
-    UnitDesc un = unit_at(p, 2, n, team, my_pairs, my_singles);
+    UnitDesc un = unit_at(p, 2, n, team, my_pairs, my_singles, PS);
     UnitDesc up = no_unit();  // unit s - 1 (parked)
     float mslp1 = 0.0f, mslq1 = 0.0f;
-    load_unit<E, NV, SH>(p, U0, sc, lp, R0, dummy);
-    load_unit<E, NV, SH>(p, U1, sc, lp, R1, dummy);
+    load_unit<E, NV, SH, PS>(p, U0, sc, lp, R0, dummy);
+    load_unit<E, NV, SH, PS>(p, U1, sc, lp, R1, dummy);
     // Step s: first pass on buffer s mod 3, loads into buffer s + 2 mod 3.
     auto step = [&](int64_t s, const Regs<NV>& Rf, const UnitDesc& Uf, Regs<NV>& Rl,
                     UnitDesc& Ul) {
       Ul = un;
-      load_unit<E, NV, SH>(p, Ul, sc, lp, Rl, dummy);
-      un = unit_at(p, s + 3, n, team, my_pairs, my_singles);
+      load_unit<E, NV, SH, PS>(p, Ul, sc, lp, Rl, dummy);
+      un = unit_at(p, s + 3, n, team, my_pairs, my_singles, PS);
       float e[2 * NV * E::kPerVec];
       float mslp = 0.0f, mslq = 0.0f;
-      first_pass_data<E, NV>(p, Uf, sc, Rf, L, (int)(s & 1), e, mslp, mslq,
-                             team_single(p, team, 2 * (s - my_pairs) + 1));
+      first_pass_data<E, NV, PS>(p, Uf, sc, Rf, L, (int)(s & 1), e, mslp, mslq,
+                                 team_single(p, team, PS * (s - my_pairs) + 1));
       // Swap: unit s - 1 out of the parking slot, unit s in (each thread
       // overwrites only the entries it has just read), before the barrier so
       // that the LDS traffic overlaps the other waves' first passes.
@@ -814,9 +818,9 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
           const PlanItem* it = p.plan_pairs + ((int64_t)team + (int64_t)p.nteams * j);
           blk = *reinterpret_cast<const uint4*>(&it->code);
         } else {
-          const int64_t m = 2 * (j - my_pairs);
+          const int64_t m = PS * (j - my_pairs);
           blk = *reinterpret_cast<const uint4*>(&p.plan_singles[team_single(p, team, m)].code);
-          if (m + 1 < my_singles)
+          if (PS == 2 && m + 1 < my_singles)
             blk2 = *reinterpret_cast<const uint4*>(&p.plan_singles[team_single(p, team, m + 1)].code);
         }
       }
@@ -840,7 +844,7 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     };
     auto comm_second = [&](int64_t s) {
       SecondRow r{0u, 0.0f, 0};
-      if (s < n && s >= my_pairs && 2 * (s - my_pairs) + 1 < my_singles) {
+      if (PS == 2 && s < n && s >= my_pairs && 2 * (s - my_pairs) + 1 < my_singles) {
         const int l = (int)(s & 63);
         r.code = (uint32_t)__builtin_amdgcn_readlane((int)blk2.x, l);
         const float T2 = __int_as_float(__builtin_amdgcn_readlane((int)blk2.y, l));
