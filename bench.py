@@ -269,8 +269,9 @@ def decode_loop_figure(sv, torch, dev, V=32768, B=64, D=8, steps=30):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(every step fits one MI355X, see the sharding note in DESIGN.md)",
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(every step of this workload fits one MI355X; the path shards by request or by "
+              "vocabulary, but no multi-GPU run is made here)",
               file=sys.stderr)
         sys.exit(2)
     import torch

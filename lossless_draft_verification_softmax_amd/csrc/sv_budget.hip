@@ -134,7 +134,7 @@ __device__ uint64_t select_threshold(const uint64_t (&key)[kKeySlots], int N, in
     const int32_t need = S.s_need;
 #pragma unroll
     for (int j = 0; j < kKeySlots; ++j) {
-      // keys sharing the selected top bits (all keys in round 0)
+      // keys sharing the selected top bits (all keys for the first digit)
       const bool match = d == 0 || (key[j] >> (shift + 8)) == (prefix >> (shift + 8));
       if (match && j * kBudgetThreads + tid < N)
         atomicAdd(&S.hist[(int)((key[j] >> shift) & 255u)], 1);
