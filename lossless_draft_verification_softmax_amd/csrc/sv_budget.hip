@@ -350,12 +350,29 @@ __global__ __launch_bounds__(kStatsThreads) void k_accept_stats(
   float tested = 0.0f, kept = 0.0f, asum = 0.0f;
   int32_t with_k = 0;
   float st = 0.0f, sn = 0.0f, se = 0.0f;  // lane 0 only
+  // A request's depth, accepted length and acceptance rates are loaded one
+  // request ahead (the rates of all D positions, whatever the depth).
+  auto load_req = [&](int r, int& n, int& tau, float& a) {
+    n = 0;
+    tau = 0;
+    a = 1.0f;
+    if (r < B) {
+      n = depth[r];
+      tau = accepted_len[r];
+      if (alpha && lane < D) a = alpha[(int64_t)r * D + lane];
+    }
+  };
+  int n_next, tau_next;
+  float a_next;
+  load_req(wave, n_next, tau_next, a_next);
   for (int r = wave; r < B; r += kStatsWaves) {
-    int n = depth[r];
+    int n = n_next;
+    const int tau = tau_next;
+    const float a_raw = a_next;
+    load_req(r + kStatsWaves, n_next, tau_next, a_next);
     n = n < 0 ? 0 : (n > D ? D : n);
-    const int tau = accepted_len[r];
     const bool in = lane < n;
-    const float a = (in && alpha) ? alpha[(int64_t)r * D + lane] : 1.0f;
+    const float a = (in && alpha) ? a_raw : 1.0f;
     // inclusive prefix product over lanes (fixed Hillis-Steele order)
     float pref = a;
 #pragma unroll

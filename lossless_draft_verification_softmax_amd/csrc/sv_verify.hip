@@ -85,9 +85,10 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
   const int r = blockIdx.x;
   const int k = threadIdx.x;
   const int D = p.D;
-  // Loads in three rounds: the request's scalars; then, independent of each
-  // other, thread k's token and the first chunk of its row states and alpha
-  // partials; then p(d) and q(d).
+  // Loads in two rounds: the request's scalars, thread k's token and the
+  // first chunk of its row states and alpha partials (read whatever the depth
+  // and temperature turn out to be: the slots lie inside the workspace, and
+  // those past a row's count are discarded below); then p(d) and q(d).
   const int n = p.depth[r];
   const float T = p.temperature[r];
   const uint32_t rid = p.request_id ? p.request_id[r] : (uint32_t)r;
@@ -119,9 +120,15 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
     const float* arow_s = p.part_a + unit * p.S1;
 #pragma unroll
     for (int i = 0; i < kMergeChunk; ++i) {
-      pv[i] = (i < np_) ? prow_s[i] : make_float2(-INFINITY, greedy ? __int_as_float(INT32_MAX) : 0.0f);
-      qv[i] = (i < nq_) ? qrow_s[i] : make_float2(-INFINITY, 0.0f);
-      av[i] = (i < na_) ? arow_s[i] : 0.0f;
+      pv[i] = prow_s[i];
+      qv[i] = qrow_s[i];
+      av[i] = arow_s[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+      if (i >= np_) pv[i] = make_float2(-INFINITY, greedy ? __int_as_float(INT32_MAX) : 0.0f);
+      if (i >= nq_) qv[i] = make_float2(-INFINITY, 0.0f);
+      if (i >= na_) av[i] = 0.0f;
     }
   }
   int32_t d = 0;
