@@ -14,9 +14,11 @@
 //
 // Each member walks a sequence of units: its team's row pairs, then its
 // team's single rows (bonus rows at T > 0 and all target rows at T = 0) two
-// at a time, always its own slice of the row.  A unit of two single rows
-// holds the second one in the draft buffer; each row keeps its own
-// temperature and kind (arg max at T = 0) and its own partial slot.
+// at a time (one at a time in the vocabulary-sharded instantiation, whose
+// registers are taken by per-thread shard addresses), always its own slice
+// of the row.  A unit of two single rows holds the second one in the draft
+// buffer; each row keeps its own temperature and kind (arg max at T = 0) and
+// its own partial slot.
 //
 // Workgroup layout: waves 0..14 are data waves, wave 15 is the communication
 // wave.  The data waves only load rows and reduce them to per-wave states
