@@ -1,0 +1,84 @@
+"""Randomised parity sweep against the oracle: random batch shapes up to the
+full vocabularies (151936 bf16, 262144 fp32), ragged depths, temperatures
+mixed over {0, 0.6, 1}, logits rounded to halves in some cases (many tied
+maxima), rows whose maximum is a signed zero, rows masked to a few columns,
+and both row passes on the same inputs.  Every request must meet the parity
+bar (bit-exact at T = 0, tokens outside the oracle's flag bands and alpha
+within 1e-5 at T > 0)."""
+import numpy as np
+import pytest
+import torch
+
+from lossless_draft_verification_softmax_amd import specverify as sv
+from tests.parity import compare, gpu_verify, oracle_verify, padded_offsets
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+CASES_PER_SEED = 10
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sv.load()
+
+
+def random_case(rng, case):
+    dtype = (torch.bfloat16, torch.float32)[case % 2]
+    B = int(rng.integers(1, 20))
+    D = int(rng.integers(0, 9))
+    V = int(rng.choice([33, 1001, 4099, 20000, 70001, 151931, 151936]
+                       + ([262144] if dtype == torch.float32 else [])))
+    vec = 8 if dtype == torch.bfloat16 else 4
+    stride = (V + vec - 1) // vec * vec + vec * int(rng.integers(0, 2))
+    temps = rng.choice(np.array([0.0, 0.0, 0.6, 1.0], np.float32), size=B).astype(np.float32)
+    P = (3.0 * rng.standard_normal((B * (D + 1), stride))).astype(np.float32)
+    if rng.random() < 0.5:
+        P = np.round(P * 2) / 2
+    Q = np.empty((max(B * D, 1), stride), np.float32)
+    for r in range(B):
+        for k in range(D):
+            Q[r * D + k] = P[r * (D + 1) + k] + rng.standard_normal(stride)
+    for i in range(P.shape[0]):
+        u = rng.random()
+        if u < 0.1:  # the maximum is zero, present with both signs
+            P[i] = -np.abs(P[i]) - 0.5
+            P[i, int(rng.integers(0, V))] = -0.0
+            P[i, int(rng.integers(0, V))] = 0.0
+        elif u < 0.2:  # masked vocabulary
+            P[i, rng.random(stride) < 0.9] = -np.inf
+            P[i, int(rng.integers(0, V))] = 1.0
+    P[:, V:] = np.nan  # padding: never read
+    Q[:, V:] = np.nan
+    Pd = torch.from_numpy(P).to(DEV).to(dtype)
+    Qd = torch.from_numpy(Q).to(DEV).to(dtype)
+    Ph = np.ascontiguousarray(Pd.float().cpu().numpy()[:, :V])
+    Qh = np.ascontiguousarray(Qd.float().cpu().numpy()[:, :V])
+    tokens = rng.integers(0, V, size=(B, max(D, 1))).astype(np.int32)[:, :D].copy()
+    for r in range(B):  # greedy drafts that often match
+        if temps[r] == 0.0:
+            for k in range(D):
+                if rng.random() < 0.8:
+                    tokens[r, k] = int(np.argmax(Ph[r * (D + 1) + k]))
+    depth = rng.integers(0, D + 1, size=B).astype(np.int32)
+    return dict(B=B, D=D, V=V, temps=temps, Pd=Pd, Qd=Qd, Ph=Ph, Qh=Qh, tokens=tokens,
+                depth=depth, seed=int(rng.integers(0, 1 << 30)))
+
+
+@pytest.mark.parametrize("sweep_seed", [11, 12, 13, 14])
+def test_random_sweep(sweep_seed):
+    rng = np.random.default_rng(sweep_seed)
+    for case in range(CASES_PER_SEED):
+        c = random_case(rng, case)
+        B, D = c["B"], c["D"]
+        tr0, dr0 = padded_offsets(B, D, DEV)
+        o = oracle_verify(c["Ph"], c["Qh"], tr0.cpu().numpy(), dr0.cpu().numpy(), c["tokens"],
+                          c["depth"], c["temps"], np.arange(B), seed=c["seed"])
+        for flags in (0, sv.SV_FLAG_STREAMING_ROW_PASS):
+            g = gpu_verify(c["Pd"], c["Qd"], tr0, dr0, torch.from_numpy(c["tokens"]).to(DEV),
+                           torch.from_numpy(c["depth"]).to(DEV),
+                           torch.from_numpy(c["temps"]).to(DEV), seed=c["seed"], flags=flags,
+                           V=c["V"])
+            rep = compare(g, o, np.arange(B), c["temps"], c["depth"])
+            assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"], (case, flags)
