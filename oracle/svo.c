@@ -326,7 +326,11 @@ int svo_verify_batch(const float* target, const float* draft, int64_t V, int64_t
         P_rows[k] = target + (target_row0[r] + k) * row_stride;
         if (!svo_row_valid(P_rows[k], V)) b |= SVO_BIT_BAD_ROW;
       }
-      if (T != 0.0f) {
+      if (T != 0.0f && n > 0 && !draft) {
+        /* a sampling request with drafted positions needs draft rows: without
+           any (allowed only for greedy batches) it is an invalid request */
+        b |= SVO_BIT_BAD_ROW;
+      } else if (T != 0.0f) {
         for (int32_t k = 0; k < n; ++k) {
           Q_rows[k] = draft + (draft_row0[r] + k) * row_stride;
           if (!svo_row_valid(Q_rows[k], V)) b |= SVO_BIT_BAD_ROW;

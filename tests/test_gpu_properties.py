@@ -157,13 +157,18 @@ def test_degenerate_shapes():
 
 
 def test_draft_logits_absent_with_sampling_request():
-    B, D, V = 2, 2, 64
+    B, D, V = 3, 2, 64
     P = torch.randn((B * (D + 1), V), device=DEV)
     tr0, _ = padded_offsets(B, D, DEV)
-    g = gpu_verify(P, None, tr0, None, torch.zeros((B, D), dtype=torch.int32, device=DEV),
-                   torch.full((B,), D, dtype=torch.int32, device=DEV),
-                   torch.tensor([0.0, 1.0], device=DEV))
-    assert g["bits"][0] == 0 and g["bits"][1] == sv.BIT_BAD_ROW
+    tokens = np.zeros((B, D), np.int32)
+    depth = np.array([D, D, 0], np.int32)
+    temps = np.array([0.0, 1.0, 1.0], np.float32)
+    g = gpu_verify(P, None, tr0, None, torch.from_numpy(tokens).to(DEV),
+                   torch.from_numpy(depth).to(DEV), torch.from_numpy(temps).to(DEV))
+    assert g["bits"][0] == 0 and g["bits"][1] == sv.BIT_BAD_ROW and g["bits"][2] == 0
+    o = oracle_verify(P.cpu().numpy(), None, tr0.cpu().numpy(), None, tokens, depth, temps,
+                      np.arange(B))
+    compare(g, o, np.arange(B), temps, depth, check_alpha=False)
 
 
 def test_identical_draft_accepts_all_on_gpu():

@@ -64,6 +64,26 @@ def test_t0_draft_rows_not_needed(svo):
     assert np.all(res["accepted_len"] == D)
 
 
+def test_sampling_request_without_draft_rows_is_invalid(svo):
+    """Draft rows may be absent only when no request samples: a T > 0 request
+    with drafted positions is then reported as an invalid row (nothing
+    emitted), while greedy requests and bonus-only requests (depth 0, which
+    read no draft row) are verified as usual."""
+    rng = np.random.default_rng(9)
+    B, D, V = 3, 2, 10
+    P = rng.standard_normal((B * (D + 1), V)).astype(np.float32)
+    tr0 = np.arange(B, dtype=np.int64) * (D + 1)
+    tokens = np.argmax(P.reshape(B, D + 1, V)[:, :D], -1).astype(np.int32)
+    depth = np.array([D, D, 0], np.int32)
+    res = svo.verify_batch(P, None, tr0, None, tokens, depth,
+                           np.array([0.0, 1.0, 1.0], np.float32), D_max=D)
+    assert res["bits"].tolist() == [0, svo.BIT_BAD_ROW, 0]
+    assert res["accepted_len"][0] == D and res["num_out"][0] == D + 1
+    assert res["num_out"][1] == 0 and np.all(res["out_tokens"][1] == -1)
+    assert res["accepted_len"][2] == 0 and res["num_out"][2] == 1
+    assert 0 <= res["out_tokens"][2, 0] < V
+
+
 # ---- closed-form special cases --------------------------------------------
 
 def test_identical_draft_accepts_everything(svo):
