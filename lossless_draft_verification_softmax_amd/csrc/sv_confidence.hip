@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kConfThreads) void k_conf_final(ConfParams c) {
     return;
   }
   const float xd = E::load1(base, d);
-  c.conf[idx] = exp2_fast((xd - s.m) * sl) / s.z;
+  c.conf[idx] = exp2_fast(__builtin_fmaf(xd, sl, -ref_of(s.m, sl))) / s.z;
 }
 
 template <typename E>

@@ -120,25 +120,45 @@ __device__ __forceinline__ double shfl_xor_d(double v, int mask) {
 
 // ---------------------------------------------------------------------------
 // Online softmax state over a row slice, in the log2 domain: the slice's
-// maximum m (raw logit units) and z = sum 2^((x - m) * sl), sl = log2(e) / T.
+// maximum m (raw logit units) and z = sum 2^(x sl - fl(m sl)), sl = log2(e) / T,
+// where fl(m sl) is the rounded float32 product.  Every exponential of a row
+// is taken against such a rounded reference (one fused x sl - ref, rounded
+// once), and every rescale and every normaliser uses the same rounded
+// products, so the reference's own rounding cancels exactly: the value of a
+// state is z 2^fl(m sl) at any magnitude of m sl.  (Mixing in the exact
+// product m sl instead would bias p by 2^(m sl - fl(m sl)), up to 1e-5
+// relative once |m sl| passes 128, as at T = 0.3 with logits near 30.)
 struct SoftmaxPart {
   float m;
   float z;
 };
+
+// The rounded product fl(m sl): the reference of a state with maximum m.
+__device__ __forceinline__ float ref_of(float m, float sl) {
+#pragma clang fp contract(off)
+  return m * sl;
+}
+
+// 2^(fl(a sl) - fl(m sl)): the factor that takes a sum relative to a's
+// reference to m's reference (exactly 1 for a = m).
+__device__ __forceinline__ float rescale(float a, float m, float sl) {
+#pragma clang fp contract(off)
+  return exp2_fast(a * sl - m * sl);
+}
 
 // Merge of two partial states (the associative (max, rescaled sum) rule).
 __device__ __forceinline__ SoftmaxPart merge_parts(SoftmaxPart a, SoftmaxPart b, float sl) {
   float m = vmax(a.m, b.m);
   if (m == -INFINITY) return {m, 0.0f};
   // A part whose max is -inf holds only masked entries: it adds nothing.
-  float za = (a.m == -INFINITY) ? 0.0f : a.z * exp2_fast((a.m - m) * sl);
-  float zb = (b.m == -INFINITY) ? 0.0f : b.z * exp2_fast((b.m - m) * sl);
+  float za = (a.m == -INFINITY) ? 0.0f : a.z * rescale(a.m, m, sl);
+  float zb = (b.m == -INFINITY) ? 0.0f : b.z * rescale(b.m, m, sl);
   return {m, za + zb};
 }
 
 __device__ __forceinline__ SoftmaxPart wave_merge(SoftmaxPart p, float sl) {
   float m = wave_max(p.m);
-  float z = (p.m == -INFINITY || m == -INFINITY) ? 0.0f : p.z * exp2_fast((p.m - m) * sl);
+  float z = (p.m == -INFINITY || m == -INFINITY) ? 0.0f : p.z * rescale(p.m, m, sl);
   // NaN maxima propagate through vmax; keep the NaN so the row reads invalid.
   if (m != m) z = m;
   return {m, wave_sum(z)};
@@ -150,7 +170,7 @@ __device__ __forceinline__ SoftmaxPart wave_merge(SoftmaxPart p, float sl) {
 __device__ __forceinline__ SoftmaxPart wave_merge_fast(SoftmaxPart p, float sl) {
   const bool nan = __ballot(p.m != p.m) != 0ull;
   float m = wave_allreduce(p.m, [](float a, float b) { return fmaxf(a, b); });
-  float z = (p.m == -INFINITY || m == -INFINITY) ? 0.0f : p.z * exp2_fast((p.m - m) * sl);
+  float z = (p.m == -INFINITY || m == -INFINITY) ? 0.0f : p.z * rescale(p.m, m, sl);
   z = wave_sum(z);
   if (nan) {
     m = __int_as_float(0x7fc00000);
@@ -160,19 +180,61 @@ __device__ __forceinline__ SoftmaxPart wave_merge_fast(SoftmaxPart p, float sl) 
 }
 
 // Wave merge against lane 0's maximum instead of the wave maximum: each sum
-// is rescaled to 2^(m_0 sl), which needs no max reduction.  The result
+// is rescaled to 2^fl(m_0 sl), which needs no max reduction.  The result
 // (m_0, z) is a valid state whether or not m_0 is the largest element: its
-// value is z 2^(m_0 sl).  A rescaled sum above 2^100 (or NaN), a non-finite
+// value is z 2^fl(m_0 sl).  A rescaled sum above 2^100 (or NaN), a non-finite
 // m_0 or an empty lane 0 takes the exact merge instead.  So every element x
 // under a merged state satisfies (x - m) sl <= 106, through any number of
 // such merges, and sums stay far from float32 overflow.
 __device__ __forceinline__ SoftmaxPart wave_merge_ref(SoftmaxPart p, float sl) {
   const float m0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.m)));
   const bool empty = p.m == -INFINITY;
-  const float zs = empty ? 0.0f : p.z * exp2_fast((p.m - m0) * sl);
+  const float zs = empty ? 0.0f : p.z * rescale(p.m, m0, sl);
   if (__ballot(!(zs <= 0x1p100f)) != 0ull || !(fabsf(m0) < INFINITY))
     return wave_merge_fast(p, sl);
   return {m0, wave_sum(zs)};
+}
+
+// The same state against a reference near its log2 normaliser: (m', z') with
+// z' 2^fl(m' sl) = z 2^fl(m sl) and z' in about [0.5, 1), so that log2 z' is
+// small and exact to about 1e-7, whatever reference the merges used (merges
+// against lane 0's maximum leave sums up to 2^100, and one float32 ulp of a
+// log2 near 100 is 8e-6: up to 1e-5 relative in every p taken from it).  With z = mant 2^k (exact), c = fl(fl(m sl) + k)
+// and its rounding error e (two-sum, exact): z 2^fl(m sl) = mant 2^(c + e);
+// m' = c / sl (to within an ulp or two: any m' with fl(m' sl) near c will
+// do) and z' = mant 2^((c - fl(m' sl)) + e), the difference being exact (two
+// nearby floats).  Empty, zero-sum or non-finite states, and
+// products out of range, are returned unchanged.
+__device__ __forceinline__ SoftmaxPart renormalise(SoftmaxPart s, float sl) {
+#pragma clang fp contract(off)
+  const float r0 = s.m * sl;
+  if (!(s.z > 0.0f) || !(s.z < INFINITY) || !(fabsf(r0) < 0x1p100f)) return s;
+  int k;
+  const float mant = frexpf(s.z, &k);
+  const float kf = (float)k;
+  const float c = r0 + kf;
+  const float bb = c - r0;
+  const float e = (r0 - (c - bb)) + (kf - bb);
+  const float m1 = c * __builtin_amdgcn_rcpf(sl);
+  if (!(fabsf(m1) < INFINITY)) return s;
+  const float c1 = m1 * sl;
+  return {m1, mant * exp2_fast((c - c1) + e)};
+}
+
+// A state's log2 value fl(m sl) + log2 z as a reference c near it plus a
+// small remainder lz, exact to about 1e-7 whatever reference the merges used:
+// with z = mant 2^k (exact), c = fl(fl(m sl) + k), e its rounding error
+// (two-sum, exact) and lz = log2(mant) + e.  For a state with z > 0 and a
+// finite product m sl.
+__device__ __forceinline__ void log2_value(SoftmaxPart s, float sl, float& c, float& lz) {
+#pragma clang fp contract(off)
+  int k;
+  const float mant = frexpf(s.z, &k);
+  const float r0 = s.m * sl;
+  const float kf = (float)k;
+  c = r0 + kf;
+  const float bb = c - r0;
+  lz = __log2f(mant) + ((r0 - (c - bb)) + (kf - bb));
 }
 
 // Three wave sums over the same fixed tree, interleaved so that their
@@ -202,8 +264,8 @@ __device__ __forceinline__ void wave_merge_ref2(SoftmaxPart& p, SoftmaxPart& q, 
                                                 float& sum, float sl) {
   const float m0p = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.m)));
   const float m0q = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(q.m)));
-  float zp = (p.m == -INFINITY) ? 0.0f : p.z * exp2_fast((p.m - m0p) * sl);
-  float zq = (!has_q || q.m == -INFINITY) ? 0.0f : q.z * exp2_fast((q.m - m0q) * sl);
+  float zp = (p.m == -INFINITY) ? 0.0f : p.z * rescale(p.m, m0p, sl);
+  float zq = (!has_q || q.m == -INFINITY) ? 0.0f : q.z * rescale(q.m, m0q, sl);
   const bool bad_lane = !(zp <= 0x1p100f) || !(zq <= 0x1p100f);
   if (__ballot(bad_lane) != 0ull || !(fabsf(m0p) < INFINITY) ||
       (has_q && !(fabsf(m0q) < INFINITY))) {

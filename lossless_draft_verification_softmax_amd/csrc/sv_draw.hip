@@ -125,19 +125,19 @@ template <typename E, bool SH>
 struct Weights32 {
   RowView<E, SH> prow, qrow;
   bool has_q;  // false: bonus draw (w = p)
-  float sl, mp, lzp, mq, lzq;
+  float sl, cp, lzp, cq, lzq;  // references fl(m sl) and log2 sums of the rows
   // weights of eight logits a (target) and b (draft; unused for a bonus draw)
   __device__ __forceinline__ void from(const float (&a)[kPer], const float (&b)[kPer],
                                        float (&w)[kPer]) const {
     if (!has_q) {
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) w[j] = exp2_fast(__builtin_fmaf(a[j] - mp, sl, -lzp));
+      for (int j = 0; j < kPer; ++j) w[j] = exp2_fast(__builtin_fmaf(a[j], sl, -cp) - lzp);
       return;
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const float pv = exp2_fast(__builtin_fmaf(a[j] - mp, sl, -lzp));
-      const float qv = exp2_fast(__builtin_fmaf(b[j] - mq, sl, -lzq));
+      const float pv = exp2_fast(__builtin_fmaf(a[j], sl, -cp) - lzp);
+      const float qv = exp2_fast(__builtin_fmaf(b[j], sl, -cq) - lzq);
       w[j] = fmaxf(pv - qv, 0.0f);
     }
   }
@@ -156,9 +156,9 @@ __device__ __forceinline__ Weights32<E, SH> weights32(const VerifyParams& p, con
   w.prow = row_view<E, SH>(p, false, st.prow);
   w.qrow = row_view<E, SH>(p, true, w.has_q ? st.qrow : 0);
   w.sl = st.sl;
-  w.mp = st.mp;
+  w.cp = ref_of(st.mp, st.sl);
   w.lzp = st.lzp;
-  w.mq = st.mq;
+  w.cq = ref_of(st.mq, st.sl);
   w.lzq = st.lzq;
   return w;
 }
@@ -413,6 +413,15 @@ __device__ __forceinline__ Weights64<E, SH> weights64(const VerifyParams& p, con
 // recomputed directly.
 constexpr double kTau64 = 1e-4;
 
+// log2(Zq / Zp) from the float32 row states, with Z = sum 2^((x - m) sl): each
+// log2 sum lz is taken against the rounded reference fl(m sl), so each adds
+// its offset fl(m sl) - m sl (exact in float64, a product of two floats).
+__device__ __forceinline__ double log2_ratio_exact(const DrawState& st) {
+  const double op = (double)ref_of(st.mp, st.sl) - (double)st.mp * (double)st.sl;
+  const double oq = (double)ref_of(st.mq, st.sl) - (double)st.mq * (double)st.sl;
+  return ((double)st.lzq + oq) - ((double)st.lzp + op);
+}
+
 template <typename E, bool SH>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
   __shared__ double lds[kDrawThreads / kWave][5];
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
     const DrawState st = p.req[r];
     const bool residual = st.mode == kDrawResidual;
     const double invT = 1.0 / (double)st.T;
-    const double rho_e = residual ? exp2((double)st.lzq - (double)st.lzp) : 0.0;
+    const double rho_e = residual ? exp2(log2_ratio_exact(st)) : 0.0;
     const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
     const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
     float a[kPer], b[kPer];
@@ -579,7 +588,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   w.lnzq = log(Zq);
   // Tile masses: from the one-pass split where it is certain, else directly.
   const double rho = Zq / Zp;
-  const double rho_e = residual ? exp2((double)st.lzq - (double)st.lzp) : 0.0;
+  const double rho_e = residual ? exp2(log2_ratio_exact(st)) : 0.0;
   const bool split_ok = residual && (p.flags & SV_FLAG_EXACT_FP64_MASSES) == 0u &&
                         fabs(rho / rho_e - 1.0) <= 0.5 * kTau64;
   // residual weight per unit of ep of an equal-logit pair

@@ -193,7 +193,7 @@ __device__ __forceinline__ void stream_softmax(const typename E::Storage* prow,
 
 template <typename E>
 __device__ __forceinline__ float overlap_batch(const Batch<E, true>& b, float sl, float cp,
-                                               float cq) {
+                                               float cq, float dlz) {
   constexpr int VEC = E::kPerVec;
   float acc = 0.0f;
 #pragma unroll
@@ -203,7 +203,7 @@ __device__ __forceinline__ float overlap_batch(const Batch<E, true>& b, float sl
     E::unpack(b.q[u], c);
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
-      e[j] = exp2_fast(fminf(__builtin_fmaf(a[j], sl, -cp), __builtin_fmaf(c[j], sl, -cq)));
+      e[j] = exp2_fast(fminf(__builtin_fmaf(a[j], sl, -cp), __builtin_fmaf(c[j], sl, -cq) - dlz));
 #pragma unroll
     for (int w = 1; w < VEC; w <<= 1) {
 #pragma unroll
@@ -214,12 +214,14 @@ __device__ __forceinline__ float overlap_batch(const Batch<E, true>& b, float sl
   return acc;
 }
 
-// Pass 2: this thread's share of sum_y 2^min(x_p(y) sl - cp, x_q(y) sl - cq)
-// (padding vectors are -inf and add 0).
+// Pass 2: this thread's share of sum_y 2^min(x_p(y) sl - cp, x_q(y) sl - cq - dlz)
+// with the rows' references cp = fl(m_p sl), cq = fl(m_q sl) and dlz = lz_q -
+// lz_p, the difference of the log2 sums against them: 2^lz_p times the sum
+// of min(p, q) (padding vectors are -inf and add 0).
 template <typename E>
 __device__ __forceinline__ float stream_overlap(const typename E::Storage* prow,
                                                 const typename E::Storage* qrow, int64_t V,
-                                                float sl, float cp, float cq) {
+                                                float sl, float cp, float cq, float dlz) {
   constexpr int VEC = E::kPerVec;
   const int64_t vhi = (V / VEC) * VEC;
   const int64_t step = (int64_t)blockDim.x * VEC;
@@ -230,14 +232,14 @@ __device__ __forceinline__ float stream_overlap(const typename E::Storage* prow,
   if (base < vhi) load_batch<E, true>(b0, prow, qrow, base, step, vhi);
   for (; base < vhi; base += 2 * batch) {
     if (base + batch < vhi) load_batch<E, true>(b1, prow, qrow, base + batch, step, vhi);
-    acc += overlap_batch<E>(b0, sl, cp, cq);
+    acc += overlap_batch<E>(b0, sl, cp, cq, dlz);
     if (base + batch >= vhi) break;
     if (base + 2 * batch < vhi) load_batch<E, true>(b0, prow, qrow, base + 2 * batch, step, vhi);
-    acc += overlap_batch<E>(b1, sl, cp, cq);
+    acc += overlap_batch<E>(b1, sl, cp, cq, dlz);
   }
   for (int64_t i = vhi + threadIdx.x; i < V; i += blockDim.x) {
     const float a = E::load1(prow, i), c = E::load1(qrow, i);
-    acc += exp2_fast(fminf(__builtin_fmaf(a, sl, -cp), __builtin_fmaf(c, sl, -cq)));
+    acc += exp2_fast(fminf(__builtin_fmaf(a, sl, -cp), __builtin_fmaf(c, sl, -cq) - dlz));
   }
   return acc;
 }
@@ -263,9 +265,12 @@ __device__ void pair_item(const VerifyParams& p, const PlanItem& it, SoftmaxPart
   const bool finite = sp.m == sp.m && sq.m == sq.m && fabsf(sp.m) < INFINITY &&
                       fabsf(sq.m) < INFINITY;
   if (finite) {  // block-uniform
-    const float cp = __builtin_fmaf(sp.m, sl, __log2f(sp.z));
-    const float cq = __builtin_fmaf(sq.m, sl, __log2f(sq.z));
-    a = block_sum_f(stream_overlap<E>(prow, qrow, p.V, sl, cp, cq), lds_f);
+    const float lzp = __log2f(sp.z);
+    const float dlz = __log2f(sq.z) - lzp;
+    a = block_sum_f(stream_overlap<E>(prow, qrow, p.V, sl, ref_of(sp.m, sl), ref_of(sq.m, sl),
+                                      dlz),
+                    lds_f) *
+        exp2_fast(-lzp);
   }
   if (threadIdx.x == 0) p.part_a[slot] = a;
 }

@@ -33,11 +33,12 @@
 //
 // Software pipeline, step s: the data waves issue the loads of unit s + 2,
 // take the first pass of unit s and then the second pass of unit s - 1.  The
-// first pass of a row pair keeps its exponentials 2^((x - m_t) sl) (m_t the
-// thread's maximum over its vectors) and parks them in LDS (one slot of
+// first pass of a row pair keeps its exponentials 2^(x sl - fl(m_t sl)) (m_t
+// the thread's maximum over its vectors) and parks them in LDS (one slot of
 // 2 * NV * VEC float32 values per data thread, VEC elements per 16-byte
 // vector; each thread reads back only what it wrote), so the second pass
-// sums min(ep Kp, eq Kq) with one Kp = 2^(m_t sl - c_p) per thread and row
+// sums min(ep Kp, eq Kq) with one Kp = 2^(fl(m_t sl) - c_p - lz_p) per thread
+// and row (c_p + lz_p the log2 of the row's sum of 2^(x sl), lz_p small)
 // instead of an exponential per element.  The communication wave gathers the
 // team normalisers of unit s in the same step.  Three register buffers
 // rotate (unit s and two units in flight).
@@ -152,7 +153,8 @@ struct TeamLds {
   SoftmaxPart sm[2][kDataWaves][2];  // per-wave (max, sum) of p and q
   ArgMax am[2][kDataWaves][2];       // per-wave arg max at T = 0, per single row
   float acc[2][kDataWaves];          // per-wave sum of min(p, q)
-  float c[2][2];                     // team log2 normalisers of p and q
+  float c[2][2];                     // team row values of p and q in log2:
+  float lz[2][2];                    // a reference c and a small remainder lz
   int ok[2];
 };
 
@@ -285,7 +287,7 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
 // Data waves.
 
 // (max, sum) of N values with their exponentials kept: e[i] = 2^(x[i] sl -
-// msl), msl = m sl (m = 0 if every value is -inf), summed in the order of
+// msl), msl = fl(m sl) (m = 0 if every value is -inf), summed in the order of
 // softmax_group from an empty state.
 template <int N>
 __device__ __forceinline__ SoftmaxPart softmax_keep(const float (&x)[N], float sl, float (&e)[N],
@@ -295,7 +297,7 @@ __device__ __forceinline__ SoftmaxPart softmax_keep(const float (&x)[N], float s
   for (int i = 1; i + 1 < N; i += 2) cm = vmax3(cm, x[i], x[i + 1]);
   if constexpr ((N % 2) == 0) cm = vmax(cm, x[N - 1]);
   const float ms = (cm == -INFINITY) ? 0.0f : cm;
-  msl = ms * sl;
+  msl = ref_of(ms, sl);
 #pragma unroll
   for (int i = 0; i < N; ++i) e[i] = exp2_fast(__builtin_fmaf(x[i], sl, -msl));
   constexpr int C = N < 8 ? N : 8;
@@ -493,8 +495,10 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
 }
 
 // Second pass of a row pair: this thread's share of sum min(p, q) with the
-// team's log2 normalisers c, from the exponentials kept by the first pass:
-// p = ep Kp and q = eq Kq with Kp = 2^(mslp - c_p), Kq = 2^(mslq - c_q), and
+// team's row values c + lz (log2 of each row's sum of 2^(x sl)), from the
+// exponentials kept by the first pass: p = ep Kp and q = eq Kq with
+// Kp = 2^((mslp - c_p) - lz_p), Kq = 2^((mslq - c_q) - lz_q) (mslp - c_p is
+// a difference of two nearby floats, exact while it matters), and
 // min(p, q) = Kp min(ep, eq Kq / Kp).  Kp <= 1 (the thread maximum is at most
 // the row maximum); a thread with Kp under 2^-60 holds p values that small
 // and adds nothing.  One sum per wave into LDS.
@@ -510,10 +514,11 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const float sl = u.sl;
   const float cp = L.c[b][0], cq = L.c[b][1];
+  const float lzp = L.lz[b][0], lzq = L.lz[b][1];
   const bool ok = L.ok[b] != 0;
   float acc = 0.0f;
   if (ok) {
-    const float kp = exp2_fast(mslp - cp), kq = exp2_fast(mslq - cq);
+    const float kp = exp2_fast((mslp - cp) - lzp), kq = exp2_fast((mslq - cq) - lzq);
     // kp in (2^-60, 1]: the hardware reciprocal (1 ulp) instead of a division
     const float r = kp > 0x1p-60f ? kq * __builtin_amdgcn_rcpf(kp) : 0.0f;
     // chunks of G 16-byte vectors of each row
@@ -544,8 +549,8 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
     const auto* prow = row_ptr<E>(sc.tgt, u.trow, p.stride);
     const auto* qrow = row_ptr<E>(sc.dft, u.drow, p.stride);
     for (int64_t i = sc.vhi + threadIdx.x; i < sc.hi; i += kDataThreads)
-      acc += exp2_fast(fminf(__builtin_fmaf(E::load1(prow, i - sc.toff), sl, -cp),
-                             __builtin_fmaf(E::load1(qrow, i - sc.toff), sl, -cq)));
+      acc += exp2_fast(fminf(__builtin_fmaf(E::load1(prow, i - sc.toff), sl, -cp) - lzp,
+                             __builtin_fmaf(E::load1(qrow, i - sc.toff), sl, -cq) - lzq));
   }
   acc = wave_sum(acc);
   if (lane == 0) L.acc[b][wave] = acc;
@@ -704,8 +709,19 @@ __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const Unit
     }
     const bool ok = a.m == a.m && c.m == c.m && fabsf(a.m) < INFINITY && fabsf(c.m) < INFINITY;
     L.ok[b] = ok;
-    L.c[b][0] = ok ? __builtin_fmaf(a.m, sl, __log2f(a.z)) : 0.0f;
-    L.c[b][1] = ok ? __builtin_fmaf(c.m, sl, __log2f(c.z)) : 0.0f;
+    // The references the merges leave (lane maxima, not the row's) can sit
+    // far below the row's peak, with sums up to 2^100, whose log2 would
+    // carry an ulp of up to 8e-6: the row values are split instead into a
+    // reference c near them and a small remainder lz.
+    float cp = 0.0f, lzp = 0.0f, cq = 0.0f, lzq = 0.0f;
+    if (ok) {
+      log2_value(a, sl, cp, lzp);
+      log2_value(c, sl, cq, lzq);
+    }
+    L.c[b][0] = cp;
+    L.c[b][1] = cq;
+    L.lz[b][0] = lzp;
+    L.lz[b][1] = lzq;
   }
 }
 

@@ -155,20 +155,21 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       if (k < n) keep = (d == am.i);
     } else {
       sl = kLog2e / T;
-      sp = merge_row(pv, p.part_p, unit, p.S1, np_, sl);
+      sp = renormalise(merge_row(pv, p.part_p, unit, p.S1, np_, sl), sl);
       if (!finite_f(sp.m)) bits |= SV_BIT_BAD_ROW;
       if (k < n) {
         if (p.draft == nullptr) {
           bits |= SV_BIT_BAD_ROW;
         } else {
-          sq = merge_row(qv, p.part_q, unit, p.S1, nq_, sl);
+          sq = renormalise(merge_row(qv, p.part_q, unit, p.S1, nq_, sl), sl);
           if (!finite_f(sq.m)) bits |= SV_BIT_BAD_ROW;
         }
       }
       if (k < n && bits == 0u) {
-        // log2 p(d) - log2 q(d), each as (x - m) sl - log2 z.
-        const float lp = __builtin_fmaf(pd - sp.m, sl, -__log2f(sp.z));
-        const float lq = __builtin_fmaf(qd - sq.m, sl, -__log2f(sq.z));
+        // log2 p(d) - log2 q(d), each as (x sl - fl(m sl)) - log2 z: against
+        // the same rounded reference as the row's sum z
+        const float lp = __builtin_fmaf(pd, sl, -ref_of(sp.m, sl)) - __log2f(sp.z);
+        const float lq = __builtin_fmaf(qd, sl, -ref_of(sq.m, sl)) - __log2f(sq.z);
         const float ratio = exp2_fast(lp - lq);
         const Philox4 w = philox4x32_10((uint32_t)k, rid, p.step, 0u, p.seed_lo, p.seed_hi);
         const float u = u24(w.w[0]);

@@ -316,3 +316,44 @@ def test_long_fp32_rows_low_temperature(row_pass):
                       np.arange(B), seed=5)
     rep = compare(g, o, np.arange(B), temps, depth)
     assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"]
+
+
+@pytest.mark.parametrize("row_pass", ["team", "stream"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_large_references_low_temperature(dtype, row_pass):
+    """Peaked rows at T = 0.1 .. 0.6 whose peak (about 40 above the bulk) the
+    draft rows share, so p / q and alpha are near 1 and the references
+    m log2(e)/T reach 230 .. 750, where one float32 ulp is 1.5e-5 .. 6e-5.
+    Every normaliser, rescale and exponential must use the same rounded
+    reference fl(m sl) (its rounding then cancels): mixing in the exact
+    product once gave alpha errors of 1e-5 and more here.  alpha within 1e-5
+    relative, tokens outside the oracle's flag bands, and draft confidences
+    within 1e-5 relative."""
+    rng = np.random.default_rng(43)
+    B, D, V = 4, 3, 151936
+    temps = np.array([0.3, 0.2, 0.1, 0.6], np.float32)
+    P = (3.0 * rng.standard_normal((B * (D + 1), V))).astype(np.float32)
+    peaks = rng.integers(0, V, size=P.shape[0])
+    for i in range(P.shape[0]):
+        P[i, peaks[i]] = 40.0 + 12.0 * rng.random()
+    Q = np.empty((B * D, V), np.float32)
+    for r in range(B):
+        for k in range(D):
+            Q[r * D + k] = P[r * (D + 1) + k] + 0.02 * rng.standard_normal(V).astype(np.float32)
+    Pd, Qd = to_dev(P, dtype), to_dev(Q, dtype)
+    Ph, Qh = Pd.float().cpu().numpy(), Qd.float().cpu().numpy()
+    tokens = np.array([[peaks[r * (D + 1) + k] for k in range(D)] for r in range(B)], np.int32)
+    tokens[1, 2] = (tokens[1, 2] + 1) % V  # one draft off the peak
+    depth = np.full(B, D, np.int32)
+    tr0, dr0 = padded_offsets(B, D, DEV)
+    tok_d, temps_d = torch.from_numpy(tokens).to(DEV), torch.from_numpy(temps).to(DEV)
+    g = gpu_verify(Pd, Qd, tr0, dr0, tok_d, torch.from_numpy(depth).to(DEV), temps_d, seed=9,
+                   flags=sv.SV_FLAG_STREAMING_ROW_PASS if row_pass == "stream" else 0)
+    o = oracle_verify(Ph, Qh, tr0.cpu().numpy(), dr0.cpu().numpy(), tokens, depth, temps,
+                      np.arange(B), seed=9)
+    rep = compare(g, o, np.arange(B), temps, depth)
+    assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"]
+    conf = sv.draft_confidence(Qd, dr0, tok_d, temps_d).cpu().numpy().astype(np.float64)
+    ref = oracle.draft_confidence(Qh, dr0.cpu().numpy(), tokens, temps)
+    assert np.all(np.abs(conf - ref) <= 1e-5 * ref + 1e-30), (conf, ref)
+    assert ref[0, 0] > 0.5  # the peaks decide: confidences near 1 are checked
