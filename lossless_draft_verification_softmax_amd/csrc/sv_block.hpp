@@ -106,13 +106,9 @@ __device__ __forceinline__ void softmax_group(SoftmaxPart& s, const float (&x)[N
   if constexpr ((N % 2) == 0) cm = vmax(cm, x[N - 1]);
   const float mn = vmax(s.m, cm);
   const float ms = (mn == -INFINITY) ? 0.0f : mn;
-  // The state's sum is relative to 2^fl(m sl), the rounded product its
-  // exponentials were taken against; the rescale below uses the same rounded
-  // products, so it is exactly 1 while the maximum does not change.  (With
-  // the exact product m sl it would multiply the sum by 2^(m sl - fl(m sl))
-  // at every group: a bias of up to 1e-6 per group, about 1e-5 over a
-  // 262144-column fp32 row at T = 0.6.)
-  const float msl = ms * sl;
+  // The state's sum is relative to 2^R(s.m), R the integer reference: the
+  // rescale 2^(R(s.m) - R(mn)) is exact, and 1 while the maximum holds.
+  const float msl = ref_of(ms, sl);
   // exponentials in chunks of at most 8 (pairwise inside a chunk, chunks in
   // order), so that only 8 of them are live at a time
   constexpr int C = N < 8 ? N : 8;
@@ -130,7 +126,7 @@ __device__ __forceinline__ void softmax_group(SoftmaxPart& s, const float (&x)[N
     }
     acc = (c == 0) ? e[0] : acc + e[0];
   }
-  const float scale = exp2_fast(s.m * sl - msl);
+  const float scale = exp2_fast(ref_of(s.m, sl) - msl);
   s.z = __builtin_fmaf(s.z, scale, acc);
   s.m = mn;
 }

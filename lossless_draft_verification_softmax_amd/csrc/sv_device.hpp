@@ -120,30 +120,34 @@ __device__ __forceinline__ double shfl_xor_d(double v, int mask) {
 
 // ---------------------------------------------------------------------------
 // Online softmax state over a row slice, in the log2 domain: the slice's
-// maximum m (raw logit units) and z = sum 2^(x sl - fl(m sl)), sl = log2(e) / T,
-// where fl(m sl) is the rounded float32 product.  Every exponential of a row
-// is taken against such a rounded reference (one fused x sl - ref, rounded
-// once), and every rescale and every normaliser uses the same rounded
-// products, so the reference's own rounding cancels exactly: the value of a
-// state is z 2^fl(m sl) at any magnitude of m sl.  (Mixing in the exact
-// product m sl instead would bias p by 2^(m sl - fl(m sl)), up to 1e-5
-// relative once |m sl| passes 128, as at T = 0.3 with logits near 30.)
+// maximum m (raw logit units) and z = sum 2^(x sl - R(m)), sl = log2(e) / T,
+// with the integer reference R(m) = rint(fl(m sl)).  Every exponential of a
+// row is taken against such a reference (one fused x sl - R, rounded once;
+// its argument is at most 1/2 at the maximum), and every rescale and every
+// normaliser uses the same references, so the value of a state is exactly
+// z 2^R(m) at any magnitude of m sl.  Two references differ by an exact
+// integer: a merge rescales by 2^(R(a) - R(m)) without rounding, whichever of
+// a and m is larger (with references fl(m sl) the difference rounds once the
+// two are more than a factor 2 apart, as when a lane holding a T = 1 row's
+// peak is merged against another lane's maximum, and mixing in the exact
+// product m sl biases every p by 2^(m sl - fl(m sl)), up to 1e-5 relative
+// once |m sl| passes 128).
 struct SoftmaxPart {
   float m;
   float z;
 };
 
-// The rounded product fl(m sl): the reference of a state with maximum m.
+// The integer reference R(m) = rint(fl(m sl)) of a state with maximum m
+// (exact as a float while |m sl| < 2^24; -inf and NaN pass through).
 __device__ __forceinline__ float ref_of(float m, float sl) {
 #pragma clang fp contract(off)
-  return m * sl;
+  return __builtin_rintf(m * sl);
 }
 
-// 2^(fl(a sl) - fl(m sl)): the factor that takes a sum relative to a's
-// reference to m's reference (exactly 1 for a = m).
+// 2^(R(a) - R(m)): the factor that takes a sum relative to a's reference to
+// m's reference (exactly 1 for a = m; the exponent is an exact integer).
 __device__ __forceinline__ float rescale(float a, float m, float sl) {
-#pragma clang fp contract(off)
-  return exp2_fast(a * sl - m * sl);
+  return exp2_fast(ref_of(a, sl) - ref_of(m, sl));
 }
 
 // Merge of two partial states (the associative (max, rescaled sum) rule).
@@ -180,9 +184,9 @@ __device__ __forceinline__ SoftmaxPart wave_merge_fast(SoftmaxPart p, float sl) 
 }
 
 // Wave merge against lane 0's maximum instead of the wave maximum: each sum
-// is rescaled to 2^fl(m_0 sl), which needs no max reduction.  The result
+// is rescaled to 2^R(m_0), which needs no max reduction.  The result
 // (m_0, z) is a valid state whether or not m_0 is the largest element: its
-// value is z 2^fl(m_0 sl).  A rescaled sum above 2^100 (or NaN), a non-finite
+// value is z 2^R(m_0).  A rescaled sum above 2^100 (or NaN), a non-finite
 // m_0 or an empty lane 0 takes the exact merge instead.  So every element x
 // under a merged state satisfies (x - m) sl <= 106, through any number of
 // such merges, and sums stay far from float32 overflow.
@@ -196,18 +200,18 @@ __device__ __forceinline__ SoftmaxPart wave_merge_ref(SoftmaxPart p, float sl) {
 }
 
 // The same state against a reference near its log2 normaliser: (m', z') with
-// z' 2^fl(m' sl) = z 2^fl(m sl) and z' in about [0.5, 1), so that log2 z' is
-// small and exact to about 1e-7, whatever reference the merges used (merges
+// z' 2^R(m') = z 2^R(m) and z' in about [0.5, 1), so that log2 z' is small
+// and exact to about 1e-7, whatever reference the merges used (merges
 // against lane 0's maximum leave sums up to 2^100, and one float32 ulp of a
-// log2 near 100 is 8e-6: up to 1e-5 relative in every p taken from it).  With z = mant 2^k (exact), c = fl(fl(m sl) + k)
-// and its rounding error e (two-sum, exact): z 2^fl(m sl) = mant 2^(c + e);
-// m' = c / sl (to within an ulp or two: any m' with fl(m' sl) near c will
-// do) and z' = mant 2^((c - fl(m' sl)) + e), the difference being exact (two
-// nearby floats).  Empty, zero-sum or non-finite states, and
+// log2 near 100 is 8e-6: up to 1e-5 relative in every p taken from it).
+// With z = mant 2^k (exact), c = fl(R(m) + k) and its rounding error e
+// (two-sum; 0 while |R(m)| < 2^23): z 2^R(m) = mant 2^(c + e); m' = c / sl
+// (to within an ulp or two: any m' with R(m') near c will do) and
+// z' = mant 2^((c - R(m')) + e).  Empty, zero-sum or non-finite states, and
 // products out of range, are returned unchanged.
 __device__ __forceinline__ SoftmaxPart renormalise(SoftmaxPart s, float sl) {
 #pragma clang fp contract(off)
-  const float r0 = s.m * sl;
+  const float r0 = ref_of(s.m, sl);
   if (!(s.z > 0.0f) || !(s.z < INFINITY) || !(fabsf(r0) < 0x1p100f)) return s;
   int k;
   const float mant = frexpf(s.z, &k);
@@ -217,20 +221,20 @@ __device__ __forceinline__ SoftmaxPart renormalise(SoftmaxPart s, float sl) {
   const float e = (r0 - (c - bb)) + (kf - bb);
   const float m1 = c * __builtin_amdgcn_rcpf(sl);
   if (!(fabsf(m1) < INFINITY)) return s;
-  const float c1 = m1 * sl;
+  const float c1 = ref_of(m1, sl);
   return {m1, mant * exp2_fast((c - c1) + e)};
 }
 
-// A state's log2 value fl(m sl) + log2 z as a reference c near it plus a
-// small remainder lz, exact to about 1e-7 whatever reference the merges used:
-// with z = mant 2^k (exact), c = fl(fl(m sl) + k), e its rounding error
-// (two-sum, exact) and lz = log2(mant) + e.  For a state with z > 0 and a
-// finite product m sl.
+// A state's log2 value R(m) + log2 z as a reference c near it plus a small
+// remainder lz, exact to about 1e-7 whatever reference the merges used: with
+// z = mant 2^k (exact), c = fl(R(m) + k), e its rounding error (two-sum; 0
+// while |R(m)| < 2^23) and lz = log2(mant) + e.  For a state with z > 0 and
+// a finite product m sl.
 __device__ __forceinline__ void log2_value(SoftmaxPart s, float sl, float& c, float& lz) {
 #pragma clang fp contract(off)
   int k;
   const float mant = frexpf(s.z, &k);
-  const float r0 = s.m * sl;
+  const float r0 = ref_of(s.m, sl);
   const float kf = (float)k;
   c = r0 + kf;
   const float bb = c - r0;

@@ -125,7 +125,7 @@ template <typename E, bool SH>
 struct Weights32 {
   RowView<E, SH> prow, qrow;
   bool has_q;  // false: bonus draw (w = p)
-  float sl, cp, lzp, cq, lzq;  // references fl(m sl) and log2 sums of the rows
+  float sl, cp, lzp, cq, lzq;  // references R(m) and log2 sums of the rows
   // weights of eight logits a (target) and b (draft; unused for a bonus draw)
   __device__ __forceinline__ void from(const float (&a)[kPer], const float (&b)[kPer],
                                        float (&w)[kPer]) const {
@@ -414,8 +414,8 @@ __device__ __forceinline__ Weights64<E, SH> weights64(const VerifyParams& p, con
 constexpr double kTau64 = 1e-4;
 
 // log2(Zq / Zp) from the float32 row states, with Z = sum 2^((x - m) sl): each
-// log2 sum lz is taken against the rounded reference fl(m sl), so each adds
-// its offset fl(m sl) - m sl (exact in float64, a product of two floats).
+// log2 sum lz is taken against the integer reference R(m), so each adds its
+// offset R(m) - m sl (exact in float64, as the product of two floats is).
 __device__ __forceinline__ double log2_ratio_exact(const DrawState& st) {
   const double op = (double)ref_of(st.mp, st.sl) - (double)st.mp * (double)st.sl;
   const double oq = (double)ref_of(st.mq, st.sl) - (double)st.mq * (double)st.sl;

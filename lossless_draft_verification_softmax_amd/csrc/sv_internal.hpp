@@ -33,9 +33,9 @@ struct DrawState {
   int64_t qrow;     // draft row (residual draws)
   float sl;         // log2(e) / T
   float T;          // temperature
-  float mp, lzp;    // target row: max and log2 of sum 2^(x sl - fl(max sl))
+  float mp, lzp;    // target row: max and log2 of sum 2^(x sl - R(max))
   float mq, lzq;    // draft row: the same
-  float zp;         // target row: sum 2^(x sl - fl(max sl))
+  float zp;         // target row: sum 2^(x sl - R(max))
   float u;          // draw uniform (word 1 of the Philox block at tau)
   int32_t need64;   // set when the float32 draw must be recomputed in float64
   float margin;     // float32 CDF margin of the draw

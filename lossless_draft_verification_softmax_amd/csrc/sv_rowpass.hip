@@ -215,7 +215,7 @@ __device__ __forceinline__ float overlap_batch(const Batch<E, true>& b, float sl
 }
 
 // Pass 2: this thread's share of sum_y 2^min(x_p(y) sl - cp, x_q(y) sl - cq - dlz)
-// with the rows' references cp = fl(m_p sl), cq = fl(m_q sl) and dlz = lz_q -
+// with the rows' references cp = R(m_p), cq = R(m_q) and dlz = lz_q -
 // lz_p, the difference of the log2 sums against them: 2^lz_p times the sum
 // of min(p, q) (padding vectors are -inf and add 0).
 template <typename E>

@@ -33,11 +33,11 @@
 //
 // Software pipeline, step s: the data waves issue the loads of unit s + 2,
 // take the first pass of unit s and then the second pass of unit s - 1.  The
-// first pass of a row pair keeps its exponentials 2^(x sl - fl(m_t sl)) (m_t
+// first pass of a row pair keeps its exponentials 2^(x sl - R(m_t)) (m_t
 // the thread's maximum over its vectors) and parks them in LDS (one slot of
 // 2 * NV * VEC float32 values per data thread, VEC elements per 16-byte
 // vector; each thread reads back only what it wrote), so the second pass
-// sums min(ep Kp, eq Kq) with one Kp = 2^(fl(m_t sl) - c_p - lz_p) per thread
+// sums min(ep Kp, eq Kq) with one Kp = 2^(R(m_t) - c_p - lz_p) per thread
 // and row (c_p + lz_p the log2 of the row's sum of 2^(x sl), lz_p small)
 // instead of an exponential per element.  The communication wave gathers the
 // team normalisers of unit s in the same step.  Three register buffers
@@ -287,7 +287,7 @@ __device__ __forceinline__ void load_unit(const VerifyParams& p, const UnitDesc&
 // Data waves.
 
 // (max, sum) of N values with their exponentials kept: e[i] = 2^(x[i] sl -
-// msl), msl = fl(m sl) (m = 0 if every value is -inf), summed in the order of
+// msl), msl = R(m) (m = 0 if every value is -inf), summed in the order of
 // softmax_group from an empty state.
 template <int N>
 __device__ __forceinline__ SoftmaxPart softmax_keep(const float (&x)[N], float sl, float (&e)[N],
@@ -499,8 +499,8 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
 // exponentials kept by the first pass: p = ep Kp and q = eq Kq with
 // Kp = 2^((mslp - c_p) - lz_p), Kq = 2^((mslq - c_q) - lz_q) (mslp - c_p is
 // a difference of two nearby floats, exact while it matters), and
-// min(p, q) = Kp min(ep, eq Kq / Kp).  Kp <= 1 (the thread maximum is at most
-// the row maximum); a thread with Kp under 2^-60 holds p values that small
+// min(p, q) = Kp min(ep, eq Kq / Kp).  Kp <= 2^(1/2) (the thread maximum is at
+// most the row maximum, and R(m_t) at most half above m_t sl); a thread with Kp under 2^-60 holds p values that small
 // and adds nothing.  One sum per wave into LDS.
 template <typename E, int NV>
 __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const UnitDesc& u,

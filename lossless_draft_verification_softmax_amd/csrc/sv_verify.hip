@@ -166,7 +166,7 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
         }
       }
       if (k < n && bits == 0u) {
-        // log2 p(d) - log2 q(d), each as (x sl - fl(m sl)) - log2 z: against
+        // log2 p(d) - log2 q(d), each as (x sl - R(m)) - log2 z: against
         // the same rounded reference as the row's sum z
         const float lp = __builtin_fmaf(pd, sl, -ref_of(sp.m, sl)) - __log2f(sp.z);
         const float lq = __builtin_fmaf(qd, sl, -ref_of(sq.m, sl)) - __log2f(sq.z);
