@@ -20,7 +20,8 @@
  *
  * Conventions for every entry point:
  *  - All array arguments are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no state between calls.
+ *    allocates nothing and keeps no state between calls (the one exception
+ *    is the static scratch array of sv_verify_batch_noalloc).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *    asynchronous and stream-ordered; the library never synchronises the
  *    host.  Results are ready when the stream reaches them.
@@ -45,7 +46,9 @@ typedef enum sv_status {
   SV_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, negative size, D_max > 64 ... */
   SV_ERR_UNSUPPORTED = 2,        /* misaligned rows, unknown dtype or flag         */
   SV_ERR_WORKSPACE_TOO_SMALL = 3,
-  SV_ERR_DEVICE = 4              /* a HIP launch failed                            */
+  SV_ERR_DEVICE = 4,             /* a HIP launch failed                            */
+  SV_ERR_SCRATCH_TOO_SMALL = 5   /* sv_verify_batch_noalloc: the batch needs more
+                                    than SV_NOALLOC_SCRATCH_BYTES of scratch        */
 } sv_status;
 
 typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
@@ -229,6 +232,35 @@ sv_status sv_verify_batch_sharded(const sv_verify_args* args, int32_t n_shards,
 size_t sv_verify_workspace_bytes(int32_t B, int32_t D_max, int64_t V);
 
 sv_status sv_verify_batch(const sv_verify_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sv_verify_batch_noalloc -- sv_verify_batch for callers that cannot
+ * allocate device memory at all (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same verification, the same
+ * kernels and the same results, with the scratch taken from a static device
+ * array of SV_NOALLOC_SCRATCH_BYTES that the library holds on each device
+ * until the process ends, instead of the caller's workspace.
+ *
+ * args->workspace and args->workspace_bytes are ignored; every other field,
+ * the outputs and the errors are those of sv_verify_batch.  A batch whose
+ * sv_verify_workspace_bytes(B, D_max, V) exceeds SV_NOALLOC_SCRATCH_BYTES is
+ * rejected with SV_ERR_SCRATCH_TOO_SMALL before any GPU work (32 MiB covers,
+ * for example, B = 256 requests x D_max = 16 at V = 262144, or B = 512 x 16
+ * at V = 151936).  The call allocates nothing: no hipMalloc, no hipFree and
+ * no allocating library routine.  The first call on a device resolves the
+ * array's device address there (hipGetSymbolAddress, with that device
+ * current), which also loads the library's code object on that device if no
+ * earlier call did.
+ *
+ * Every call on one device uses that device's one array, and the scratch
+ * holds the last call's contents (the kernels clear what must start at zero
+ * themselves).  Calls that overlap on one device -- on different streams, or
+ * from different host threads without ordering -- race on the array and give
+ * undefined results; order them on one stream.
+ * ------------------------------------------------------------------------- */
+#define SV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+sv_status sv_verify_batch_noalloc(const sv_verify_args* args, void* stream);
 
 /* ---------------------------------------------------------------------------
  * sv_accept_stats -- acceptance statistics of one verified batch (equation

@@ -5,9 +5,17 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "specverify.h"
 #include "sv_internal.hpp"
+
+// Scratch of sv_verify_batch_noalloc: one copy per device, allocated by the
+// HIP runtime when the code object is loaded and held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// array: host code only ever uses the device address that
+// hipGetSymbolAddress returns for the current device (scratch_address).
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -17,6 +25,25 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // each); cached per device.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
+
+// Device address of `scratch` on each device, resolved once per device (with
+// that device current) on the first sv_verify_batch_noalloc call there.
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
 
 int device_cu_count() {
   int dev = 0;
@@ -72,6 +99,8 @@ const char* sv_status_string(sv_status status) {
     case SV_ERR_UNSUPPORTED: return "unsupported layout, dtype or flag";
     case SV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case SV_ERR_DEVICE: return "device launch failed";
+    case SV_ERR_SCRATCH_TOO_SMALL:
+      return "batch needs more scratch than the no-allocation entry point holds";
   }
   return "unknown status";
 }
@@ -171,6 +200,27 @@ sv_status sv_verify_batch(const sv_verify_args* a, void* stream) {
   if (st != SV_OK) return st;
   if (a->B == 0) return SV_OK;
   return run_verify(a, 1, a->V, nullptr, nullptr, stream);
+}
+
+sv_status sv_verify_batch_noalloc(const sv_verify_args* a, void* stream) {
+  if (!a) return SV_ERR_INVALID_ARGUMENT;
+  // Size check first, on the host, before the device is touched.
+  const size_t need = sv_verify_workspace_bytes(a->B, a->D_max, a->V);
+  if (need > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_SCRATCH_TOO_SMALL;
+  sv_verify_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (b.B > 0) {
+    void* ptr = scratch_address();
+    if (!ptr) return SV_ERR_DEVICE;
+    b.workspace = ptr;
+    b.workspace_bytes = SV_NOALLOC_SCRATCH_BYTES;
+  }
+  size_t need2 = 0;
+  const sv_status st = validate_verify(&b, b.V, &need2);
+  if (st != SV_OK) return st;
+  if (b.B == 0) return SV_OK;
+  return run_verify(&b, 1, b.V, nullptr, nullptr, stream);
 }
 
 sv_status sv_verify_batch_sharded(const sv_verify_args* a, int32_t n_shards, int64_t shard_width,

@@ -21,6 +21,8 @@ SV_ERR_INVALID_ARGUMENT = 1
 SV_ERR_UNSUPPORTED = 2
 SV_ERR_WORKSPACE_TOO_SMALL = 3
 SV_ERR_DEVICE = 4
+SV_ERR_SCRATCH_TOO_SMALL = 5
+SV_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 SV_DTYPE_BF16 = 0
 SV_DTYPE_FP32 = 1
@@ -42,7 +44,7 @@ BIT_SYNC_TIMEOUT = 64
 EXPORTS = ["sv_status_string", "sv_version", "sv_k_rho", "sv_allocate_budget",
            "sv_verify_workspace_bytes", "sv_verify_batch", "sv_accept_stats",
            "sv_draft_confidence_workspace_bytes", "sv_draft_confidence", "sv_select_budget_ratio",
-           "sv_sample_rows", "sv_verify_batch_sharded"]
+           "sv_sample_rows", "sv_verify_batch_sharded", "sv_verify_batch_noalloc"]
 MAX_SHARDS = 16
 MAX_RATIOS = 8
 DCUT_RATIOS = (0.25, 0.5, 0.75, 1.0)
@@ -97,6 +99,8 @@ def load() -> ctypes.CDLL:
     L.sv_verify_workspace_bytes.restype = ctypes.c_size_t
     L.sv_verify_batch.argtypes = [ctypes.POINTER(SvVerifyArgs), vp]
     L.sv_verify_batch.restype = ctypes.c_int
+    L.sv_verify_batch_noalloc.argtypes = [ctypes.POINTER(SvVerifyArgs), vp]
+    L.sv_verify_batch_noalloc.restype = ctypes.c_int
     L.sv_allocate_budget.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64, vp,
                                      vp, vp, vp, vp]
     L.sv_allocate_budget.restype = ctypes.c_int
@@ -404,7 +408,15 @@ class Verifier:
             *[e.cuda_event if e is not None else None for e in events])
         self.args.stage_events = ctypes.cast(self._events, ctypes.c_void_p)
 
-    def run(self) -> VerifyOutputs:
+    def run(self, noalloc: bool = False) -> VerifyOutputs:
+        """One verification call; noalloc=True calls sv_verify_batch_noalloc
+        (the library's static scratch instead of this object's workspace)."""
+        if noalloc:
+            if self._shards is not None:
+                raise ValueError("the no-allocation entry point takes unsharded logits")
+            st = load().sv_verify_batch_noalloc(ctypes.byref(self.args), _stream(self.device))
+            _check(st, "sv_verify_batch_noalloc")
+            return self.out
         if self._shards is not None:
             n, w = self._shards
             st = load().sv_verify_batch_sharded(ctypes.byref(self.args), n, w, self._tsh,
