@@ -99,9 +99,15 @@ def lib() -> ctypes.CDLL:
     L.svo_allocate_budget.restype = ctypes.c_int
     L.svo_fixed_depth.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _i32p]
     L.svo_fixed_depth.restype = None
+    L.svo_fixed_depth_budget.argtypes = [_f32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                         _i32p, _i64p, _i64p, _f64p]
+    L.svo_fixed_depth_budget.restype = ctypes.c_int
     L.svo_accept_stats.argtypes = [_i32p, _f64p, _i32p, ctypes.c_int32, ctypes.c_int32, _f64p,
                                    _f64p, _f64p]
     L.svo_accept_stats.restype = ctypes.c_int
+    L.svo_accept_accumulate.argtypes = [_i32p, _f64p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                        _f64p, _f64p]
+    L.svo_accept_accumulate.restype = ctypes.c_int
     L.svo_draft_confidence.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                        ctypes.c_int32, _i64p, _i32p, _i32p, _f32p, _f32p]
     L.svo_draft_confidence.restype = ctypes.c_int
@@ -304,6 +310,22 @@ def fixed_depth(B: int, D: int, K: int) -> np.ndarray:
     return depth
 
 
+def fixed_depth_budget(conf, K: int):
+    """The fixed-depth baseline at K: depths, row offsets and utility
+    (kept products, all products), as allocate_budget returns them."""
+    c = _f32(conf)
+    B, D = c.shape
+    depth = np.zeros(B, dtype=np.int32)
+    dr0 = np.zeros(B, dtype=np.int64)
+    tr0 = np.zeros(B, dtype=np.int64)
+    util = np.zeros(2, dtype=np.float64)
+    st = lib().svo_fixed_depth_budget(_p(c, _f32p), B, D, int(K), _p(depth, _i32p),
+                                      _p(dr0, _i64p), _p(tr0, _i64p), _p(util, _f64p))
+    if st != 0:
+        raise ValueError("svo_fixed_depth_budget: invalid argument")
+    return dict(depth=depth, draft_row0=dr0, target_row0=tr0, utility=util)
+
+
 # ---- drafter confidence and keep-ratio choice --------------------------------
 
 def draft_confidence(draft, draft_row0, draft_tokens, temperature, depth=None):
@@ -374,6 +396,25 @@ def accept_stats(depth, alpha_mat, accepted_len, D_max: int):
     return dict(expected_len=e, per_depth=pd[: 3 * D_max].reshape(3, D_max), summary=sm)
 
 
+def accept_accumulate(depth, alpha_mat, accepted_len, D_max: int, accum=None):
+    """Adds one verified batch to the running statistics accum (a float64
+    array of 3 + 2 D_max, created when None); returns (accum, summary) with
+    summary = (MAL, expected MAL, mean acceptance, P(tau >= 1..D_max))."""
+    dep = np.ascontiguousarray(depth, dtype=np.int32)
+    B = dep.size
+    al = None if alpha_mat is None else np.ascontiguousarray(alpha_mat, dtype=np.float64).reshape(
+        B, D_max)
+    acc = np.ascontiguousarray(accepted_len, dtype=np.int32)
+    if accum is None:
+        accum = np.zeros(3 + 2 * D_max, dtype=np.float64)
+    summ = np.zeros(3 + D_max, dtype=np.float64)
+    st = lib().svo_accept_accumulate(_p(dep, _i32p), _p(al, _f64p), _p(acc, _i32p), B, D_max,
+                                     _p(accum, _f64p), _p(summ, _f64p))
+    if st != 0:
+        raise ValueError("svo_accept_accumulate: invalid argument")
+    return accum, summ
+
+
 # ---- multi-step decoding on a Markov target ---------------------------------
 # The decode loop the pages' eval server runs ([T] "The MTP path": MAL and
 # position-wise acceptance measured over whole generations; [A] "MTP": a
@@ -404,14 +445,17 @@ def markov_decode(P_table, Q_table, start, D: int, temperature, steps: int, seed
     draft table (row = previous token), verify them against the target table
     rows of the same contexts, keep the emitted tokens, continue from the last
     one.  Returns per-step lists of emitted tokens, accepted lengths, the
-    drafts and each request's (draft, accept, draw) margins, and the smallest
-    margins met."""
+    drafts and each request's (draft, accept, draw) margins, the smallest
+    margins met, and after each step the running statistics of
+    accept_accumulate (the totals and the summary: MAL, expected MAL (0 here:
+    no acceptance rates), mean acceptance, P(tau >= k))."""
     P_table = _f32(P_table)
     Q_table = _f32(Q_table)
     B = len(start)
     rid = list(range(B)) if request_id is None else [int(x) for x in request_id]
     last = [int(t) for t in start]
-    emitted, taus, drafts, step_margins = [], [], [], []
+    emitted, taus, drafts, step_margins, step_stats = [], [], [], [], []
+    accum = None
     min_margin = {"draft": float("inf"), "accept": float("inf"), "draw": float("inf")}
     for step in range(steps):
         em_s, tau_s, dr_s, mg_s = [], [], [], []
@@ -443,5 +487,8 @@ def markov_decode(P_table, Q_table, start, D: int, temperature, steps: int, seed
         taus.append(tau_s)
         drafts.append(dr_s)
         step_margins.append(mg_s)
+        accum, summ = accept_accumulate(np.full(B, D, np.int32), None, np.asarray(tau_s, np.int32),
+                                        D, accum)
+        step_stats.append((accum.copy(), summ))
     return dict(emitted=emitted, tau=taus, drafts=drafts, margins=min_margin,
-                step_margins=step_margins)
+                step_margins=step_margins, step_stats=step_stats)

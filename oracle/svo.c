@@ -464,6 +464,41 @@ void svo_fixed_depth(int32_t B, int32_t D_max, int64_t K, int32_t* depth) {
   }
 }
 
+/* The fixed-depth baseline's allocation and utility: the depths of
+ * svo_fixed_depth, row offsets as svo_allocate_budget writes them, and
+ * utility = (sum of the prefix-confidence products of the kept positions,
+ * sum over every position), the products taken as in svo_allocate_budget.
+ * The budget widget of section "D-cut" compares the first with the global
+ * top-K's at the same K (utility retained, global vs fixed). */
+int svo_fixed_depth_budget(const float* conf, int32_t B, int32_t D_max, int64_t K, int32_t* depth,
+                           int64_t* draft_row0, int64_t* target_row0, double* utility) {
+  if (B < 0 || D_max < 0 || !depth || (B > 0 && D_max > 0 && !conf))
+    return SVO_ERR_INVALID_ARGUMENT;
+  svo_fixed_depth(B, D_max, K, depth);
+  double kept = 0.0, total = 0.0;
+  int64_t dr = 0, tr = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    float s = 1.0f;
+    for (int32_t k = 0; k < D_max; ++k) {
+      float c = conf[(int64_t)r * D_max + k];
+      if (!(c >= 0.0f)) c = 0.0f; /* NaN and negatives read as 0 */
+      if (c > 1.0f) c = 1.0f;
+      s = s * c;
+      total += (double)s;
+      if (k < depth[r]) kept += (double)s;
+    }
+    if (draft_row0) draft_row0[r] = dr;
+    if (target_row0) target_row0[r] = tr;
+    dr += depth[r];
+    tr += depth[r] + 1;
+  }
+  if (utility) {
+    utility[0] = kept;
+    utility[1] = total;
+  }
+  return SVO_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Statistics: equation L_e2e (expected accepted length) and the MAL /
  * mean-acceptance figures of "The MTP path" (tradepoint.io page), whose
@@ -503,6 +538,47 @@ int svo_accept_stats(const int32_t* depth, const double* alpha, const int32_t* a
     summary[1] = B ? 1.0 + sum_e / B : 0.0;
     summary[2] = sum_n > 0 ? sum_tau / sum_n : 0.0;
     summary[3] = sum_n;
+  }
+  return SVO_OK;
+}
+
+/* Statistics over many verified batches (the decode loop's steps), as the
+ * tradepoint.io page, "The MTP path", reports them over whole generations:
+ * MAL, mean acceptance and position-wise acceptance.  accum (length
+ * 3 + 2 D_max) is added to: accum[0] += sum of (tau + 1) (tokens emitted),
+ * accum[1] += B, accum[2] += sum of E[tau_r] (0 without alpha),
+ * accum[3 + k] += #requests with depth > k (position k verified),
+ * accum[3 + D_max + k] += #requests with tau > k (position k accepted), with
+ * depth clamped to [0, D_max].  summary (length 3 + D_max) is then taken from
+ * the totals: MAL = accum[0] / accum[1]; expected MAL = 1 + accum[2] /
+ * accum[1]; mean acceptance = sum tau / sum depth; position-wise acceptance
+ * at position k + 1 (1-based) = P(tau >= k + 1) = accum[3 + D_max + k] /
+ * accum[1], so that MAL = 1 + the sum of the position-wise acceptances. */
+int svo_accept_accumulate(const int32_t* depth, const double* alpha, const int32_t* accepted_len,
+                          int32_t B, int32_t D_max, double* accum, double* summary) {
+  if (B < 0 || D_max < 0 || !accum || (B > 0 && (!depth || !accepted_len)))
+    return SVO_ERR_INVALID_ARGUMENT;
+  for (int32_t r = 0; r < B; ++r) {
+    int32_t n = depth[r];
+    if (n < 0) n = 0;
+    if (n > D_max) n = D_max;
+    const int32_t tau = accepted_len[r];
+    accum[0] += (double)(tau + 1);
+    accum[1] += 1.0;
+    if (alpha) accum[2] += svo_expected_accepted(alpha + (int64_t)r * D_max, n);
+    for (int32_t k = 0; k < D_max; ++k) {
+      if (n > k) accum[3 + k] += 1.0;
+      if (tau > k) accum[3 + D_max + k] += 1.0;
+    }
+  }
+  if (summary) {
+    double sum_n = 0.0;
+    for (int32_t k = 0; k < D_max; ++k) sum_n += accum[3 + k];
+    const double req = accum[1];
+    summary[0] = req > 0 ? accum[0] / req : 0.0;
+    summary[1] = req > 0 ? 1.0 + accum[2] / req : 0.0;
+    summary[2] = sum_n > 0 ? (accum[0] - req) / sum_n : 0.0;
+    for (int32_t k = 0; k < D_max; ++k) summary[3 + k] = req > 0 ? accum[3 + D_max + k] / req : 0.0;
   }
   return SVO_OK;
 }

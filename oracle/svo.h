@@ -156,6 +156,13 @@ int svo_allocate_budget(const float* conf, int32_t B, int32_t D_max, const int32
  * depth, floor(K / B), and the first K mod B requests get one more. */
 void svo_fixed_depth(int32_t B, int32_t D_max, int64_t K, int32_t* depth);
 
+/* The fixed-depth allocation at K with its row offsets (as svo_allocate_budget
+ * writes them) and utility[2] = (sum of the kept positions' prefix-confidence
+ * products, sum over all B * D_max positions); products as in
+ * svo_allocate_budget. */
+int svo_fixed_depth_budget(const float* conf, int32_t B, int32_t D_max, int64_t K, int32_t* depth,
+                           int64_t* draft_row0, int64_t* target_row0, double* utility);
+
 /* Drafter confidence: conf[r * D_max + k] = softmax(draft row / T_r)[d]
  * (T_r = 0 read as 1) for k < depth[r] (depth NULL = D_max), row
  * draft_row0[r] + k of a buffer with row_stride elements per row, d =
@@ -192,6 +199,14 @@ int svo_select_budget_ratio(const float* conf, int32_t B, int32_t D_max, const i
 int svo_accept_stats(const int32_t* depth, const double* alpha, const int32_t* accepted_len,
                      int32_t B, int32_t D_max, double* expected_len, double* per_depth,
                      double* summary);
+
+/* Statistics over many verified batches: adds the batch to accum
+ * (3 + 2 D_max doubles: tokens emitted, requests, sum of E[tau], #verified at
+ * each position, #accepted at each position) and writes, from the totals,
+ * summary (3 + D_max): MAL, expected MAL, mean acceptance, and the
+ * position-wise acceptance P(tau >= k) for k = 1..D_max. */
+int svo_accept_accumulate(const int32_t* depth, const double* alpha, const int32_t* accepted_len,
+                          int32_t B, int32_t D_max, double* accum, double* summary);
 
 #ifdef __cplusplus
 }

@@ -142,3 +142,79 @@ def test_widget_global_beats_fixed(svo):
         fixed = svo.fixed_depth(6, 8, 24)
         s = scores(conf).astype(np.float64)
         assert res["utility"][0] >= sum(s[r, :fixed[r]].sum() for r in range(6)) - 1e-12
+
+
+def test_fixed_depth_hand_values(svo):
+    """The fixed-depth baseline against hand values (tests/golden/fixed_depth.txt):
+    the remainder goes to the first K mod B requests, K past B D clamps to D,
+    K <= 0 keeps nothing, B = 0 is empty."""
+    for row in golden("fixed_depth.txt"):
+        B, D, K = int(row[0]), int(row[1]), int(row[2])
+        want = [int(x) for x in row[4:]]
+        assert list(svo.fixed_depth(B, D, K)) == want, row
+        if B > 0:
+            res = svo.fixed_depth_budget(np.full((B, D), 0.5, np.float32), K)
+            assert list(res["depth"]) == want
+            assert list(res["draft_row0"]) == list(np.concatenate([[0], np.cumsum(want)[:-1]]))
+            assert list(res["target_row0"]) == list(
+                np.concatenate([[0], np.cumsum(np.asarray(want) + 1)[:-1]]))
+
+
+def test_fixed_and_global_utility_hand_values(svo):
+    conf = np.array([[0.75, 0.75, 0.5], [0.25, 1.0, 1.0]], np.float32)
+    for K, kind, d0, d1, kept, total in golden("fixed_vs_global_utility.txt"):
+        res = (svo.fixed_depth_budget if kind == "fixed" else svo.allocate_budget)(conf, int(K))
+        assert list(res["depth"]) == [int(d0), int(d1)]
+        assert res["utility"][0] == float(kept)
+        assert res["utility"][1] == float(total)
+
+
+def test_fixed_depth_utility_against_library_products(svo):
+    """Kept and total utility of the fixed baseline equal sums of numpy's
+    float32 cumprod over the kept prefixes; retained utility global >= fixed."""
+    rng = np.random.default_rng(24)
+    for _ in range(100):
+        B = int(rng.integers(1, 12))
+        D = int(rng.integers(1, 12))
+        conf = rng.beta(3, 2, size=(B, D)).astype(np.float32)
+        conf[rng.random((B, D)) < 0.05] = np.nan
+        K = int(rng.integers(-2, B * D + 4))
+        res = svo.fixed_depth_budget(conf, K)
+        s = scores(conf).astype(np.float64)
+        want = svo.fixed_depth(B, D, K)
+        assert list(res["depth"]) == list(want)
+        assert res["utility"][0] == pytest.approx(sum(s[r, :want[r]].sum() for r in range(B)),
+                                                  rel=1e-12, abs=1e-30)
+        assert res["utility"][1] == pytest.approx(s.sum(), rel=1e-12, abs=1e-30)
+        glob = svo.allocate_budget(conf, K)
+        assert glob["utility"][0] >= res["utility"][0] - 1e-12
+
+
+def test_accept_accumulate_hand_values(svo):
+    rows = {r[0]: [float(x) for x in r[1:]] for r in golden("accept_accumulate.txt")}
+    depth = np.array([3, 3, 2, 0], np.int32)
+    tau = np.array([0, 3, 1, 0], np.int32)
+    alpha = np.array([[0.5, 0.5, 0.5], [1, 1, 1], [0.5, 1, 0], [0, 0, 0]], np.float64)
+    acc, summ = svo.accept_accumulate(depth, alpha, tau, 3)
+    assert list(acc) == rows["accum1"]
+    assert list(summ) == rows["summary"]
+    acc, summ = svo.accept_accumulate(depth, alpha, tau, 3, acc)
+    assert list(acc) == rows["accum2"]
+    assert list(summ) == rows["summary"]
+
+
+def test_accept_accumulate_printed_mal_relation(svo):
+    """With every request verified at depth D, MAL = 1 + D x mean acceptance
+    and MAL = 1 + sum of the position-wise acceptances, the relation of the
+    printed pairs 2.58 / 52.8% and 2.99 / 66.4% at D = 3 ([T] "The MTP
+    path"; tests/golden/mtp_ttt_mal.txt)."""
+    rng = np.random.default_rng(25)
+    D = 3
+    acc = None
+    for _ in range(50):
+        B = int(rng.integers(1, 40))
+        tau = rng.integers(0, D + 1, size=B).astype(np.int32)
+        acc, summ = svo.accept_accumulate(np.full(B, D, np.int32), None, tau, D, acc)
+    assert summ[0] == pytest.approx(1 + D * summ[2], rel=1e-12)
+    assert summ[0] == pytest.approx(1 + summ[3:].sum(), rel=1e-12)
+    assert np.all(np.diff(summ[3:]) <= 0)     # P(tau >= k) does not increase with k
