@@ -71,6 +71,10 @@ typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
 #define SV_FLAG_EXACT_FP64_MASSES 4u  /* float64 draws: compute every tile mass directly
                                          with the float64 normalisers (a second pass over the
                                          row) instead of from the one-pass decomposition */
+#define SV_FLAG_TEAM_WAIT_GIVE_UP 8u  /* testing: every team wait of the team row pass gives
+                                         up at once, so every member takes the fallback
+                                         (streams the pair's full rows itself); results are
+                                         those of a normal call, only slower */
 
 /* sv_diag.bits */
 #define SV_BIT_BAD_DEPTH 1u        /* depth[r] outside [0, D_max]                      */
@@ -79,7 +83,11 @@ typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
 #define SV_BIT_RESIDUAL_ZERO 8u    /* residual mass was zero: the draw used p          */
 #define SV_BIT_BAD_TEMPERATURE 16u /* temperature[r] negative, NaN or infinite         */
 #define SV_BIT_FP64_DRAW 32u       /* the draw was recomputed in float64               */
-#define SV_BIT_SYNC_TIMEOUT 64u    /* the row pass's team wait expired: results invalid */
+#define SV_BIT_SYNC_TIMEOUT 64u    /* information only: a team wait of the row pass
+                                      expired (members of a team were not resident at
+                                      once, e.g. other work held compute units) and the
+                                      waiting member took its row normalisers from the
+                                      full rows itself; results are valid */
 
 /* Per-request diagnostics (written when sv_verify_args.diag != NULL). */
 typedef struct sv_diag {
@@ -123,6 +131,23 @@ sv_status sv_allocate_budget(const float* conf, int32_t B, int32_t D_max,
                              const int32_t* max_depth, int64_t K, int32_t* depth,
                              int64_t* draft_row0, int64_t* target_row0, float* utility,
                              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sv_allocate_fixed_depth -- the fixed-depth baseline that the budget widget
+ * of "AngelSpec: specialize the drafter...", section "D-cut", sets against
+ * the global top-K: the same K draft positions spread evenly, every request
+ * cut at depth floor(K / B) and the first K mod B requests one deeper, never
+ * past D_max (K < 0 reads as 0).  depth, draft_row0, target_row0 as
+ * sv_allocate_budget writes them; utility (optional, float[2]) = (sum of the
+ * kept positions' prefix-confidence products, sum over all B * D_max
+ * positions), products as in sv_allocate_budget, so that
+ * utility[0] / utility[1] of the two calls at one K is the widget's retained
+ * utility, fixed vs global.  Same size limits and errors as
+ * sv_allocate_budget.
+ * ------------------------------------------------------------------------- */
+sv_status sv_allocate_fixed_depth(const float* conf, int32_t B, int32_t D_max, int64_t K,
+                                  int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
+                                  float* utility, void* stream);
 
 /* ---------------------------------------------------------------------------
  * sv_verify_batch -- lossless verification of a batch of drafted blocks
@@ -280,6 +305,34 @@ sv_status sv_accept_stats(const int32_t* depth, const float* alpha, const int32_
                           float* summary, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * sv_accept_stats_accumulate -- statistics over many verified batches, e.g.
+ * the steps of a decode loop: MAL, mean acceptance and position-wise
+ * acceptance over whole generations, as the tradepoint.io page, "The MTP
+ * path", reports them (MAL 2.58 -> 2.99 with mean acceptance 52.8% -> 66.4%
+ * at depth 3; position-1 acceptance 0.799 -> 0.814).
+ *
+ * Adds one batch to the caller's running totals accum (device double
+ * [3 + 2 * D_max], zeroed by the caller before the first batch):
+ *   accum[0] += sum_r (tau_r + 1)        tokens emitted
+ *   accum[1] += B                        requests
+ *   accum[2] += sum_r E[tau_r]           (alpha given; equation L_e2e)
+ *   accum[3 + k] += #{r: depth_r > k}    position k + 1 verified
+ *   accum[3 + D_max + k] += #{r: tau_r > k}  position k + 1 accepted
+ * (depth clamped to [0, D_max]; counts are exact integers in double up to
+ * 2^53), then writes summary (device float [3 + D_max], optional) from the
+ * new totals: [0] MAL = accum[0] / accum[1], [1] expected MAL
+ * 1 + accum[2] / accum[1], [2] mean acceptance sum tau / sum depth, [3 + k]
+ * position-wise acceptance P(tau >= k + 1) = accum[3 + D_max + k] /
+ * accum[1].  With every depth equal to D_max, MAL = 1 + D_max * mean
+ * acceptance = 1 + sum of the position-wise acceptances.
+ * Inputs: depth [B], accepted_len [B] (device int32), alpha [B, D_max]
+ * (device float) or NULL.  Stream-ordered; one call at a time per accum.
+ * ------------------------------------------------------------------------- */
+sv_status sv_accept_stats_accumulate(const int32_t* depth, const float* alpha,
+                                     const int32_t* accepted_len, int32_t B, int32_t D_max,
+                                     double* accum, float* summary, void* stream);
+
+/* ---------------------------------------------------------------------------
  * sv_draft_confidence -- the drafter's confidence in each drafted token, the
  * scores the D-cut budget ranks ("AngelSpec: specialize the drafter...",
  * section "D-cut": Figure 3 panel 1, confidence-scored candidate tokens;
@@ -374,6 +427,19 @@ sv_status sv_sample_rows(sv_dtype dtype, int32_t B, int64_t V, int64_t row_strid
                          int64_t index_stride, const float* temperature,
                          const uint32_t* request_id, uint64_t seed, uint32_t step,
                          uint32_t position, int32_t* tokens, int64_t token_stride, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sv_stream_read -- calibration, not part of the method: reads `bytes` bytes
+ * of device memory at `buf` once (16-byte vector loads, grid-stride over
+ * blocks_per_cu 256-thread workgroups per compute unit) and folds them by xor
+ * into sink[0] (one atomic per workgroup; sink is device memory of one
+ * uint32).  Its time gives the HBM read rate this chip reaches with no
+ * arithmetic and no writes, the practical ceiling of the row passes, which
+ * read each logit row once.  buf 16-byte aligned, bytes a multiple of 16,
+ * 1 <= blocks_per_cu <= 32; else SV_ERR_INVALID_ARGUMENT before any launch.
+ * ------------------------------------------------------------------------- */
+sv_status sv_stream_read(const void* buf, size_t bytes, int32_t blocks_per_cu, uint32_t* sink,
+                         void* stream);
 
 #ifdef __cplusplus
 }

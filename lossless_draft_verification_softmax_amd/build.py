@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libspecverify.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["sv_api.hip", "sv_verify.hip", "sv_rowpass.hip", "sv_rowteam.hip", "sv_draw.hip", "sv_budget.hip",
-           "sv_confidence.hip", "sv_sample.hip"]
+           "sv_confidence.hip", "sv_sample.hip", "sv_calib.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 ops are switched off: the compiler emits them from plain float

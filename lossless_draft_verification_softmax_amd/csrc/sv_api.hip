@@ -65,7 +65,8 @@ sv_status validate_verify(const sv_verify_args* a, int64_t row_width, size_t* ne
   if (a->B < 0 || a->D_max < 0 || a->D_max > SV_MAX_DEPTH) return SV_ERR_INVALID_ARGUMENT;
   if (a->V < 1 || a->V > INT32_MAX || a->row_stride < row_width) return SV_ERR_INVALID_ARGUMENT;
   if (a->dtype != SV_DTYPE_BF16 && a->dtype != SV_DTYPE_FP32) return SV_ERR_UNSUPPORTED;
-  if (a->flags & ~(SV_FLAG_FORCE_FP64_DRAW | SV_FLAG_STREAMING_ROW_PASS | SV_FLAG_EXACT_FP64_MASSES))
+  if (a->flags & ~(SV_FLAG_FORCE_FP64_DRAW | SV_FLAG_STREAMING_ROW_PASS |
+                   SV_FLAG_EXACT_FP64_MASSES | SV_FLAG_TEAM_WAIT_GIVE_UP))
     return SV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * (a->D_max + 1) > (int64_t)INT32_MAX / 64) return SV_ERR_INVALID_ARGUMENT;
   if (a->B == 0) {
@@ -262,6 +263,19 @@ sv_status sv_allocate_budget(const float* conf, int32_t B, int32_t D_max,
   return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
+sv_status sv_allocate_fixed_depth(const float* conf, int32_t B, int32_t D_max, int64_t K,
+                                  int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
+                                  float* utility, void* stream) {
+  if (B < 0 || D_max < 0) return SV_ERR_INVALID_ARGUMENT;
+  if (B > SV_MAX_BUDGET_POSITIONS || (int64_t)B * D_max > SV_MAX_BUDGET_POSITIONS)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SV_OK;
+  if (!depth || (D_max > 0 && !conf)) return SV_ERR_INVALID_ARGUMENT;
+  const hipError_t e = sv::launch_budget_fixed(conf, B, D_max, K, depth, draft_row0, target_row0,
+                                               utility, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
 size_t sv_draft_confidence_workspace_bytes(sv_dtype dtype, int32_t B, int32_t D_max, int64_t V) {
   if (B < 0 || D_max < 0 || V < 1 || V > INT32_MAX) return 0;
   if (dtype != SV_DTYPE_BF16 && dtype != SV_DTYPE_FP32) return 0;
@@ -397,6 +411,16 @@ sv_status sv_accept_stats(const int32_t* depth, const float* alpha, const int32_
   if (!depth || !accepted_len) return SV_ERR_INVALID_ARGUMENT;
   const hipError_t e = sv::launch_stats(depth, alpha, accepted_len, B, D_max, expected_len,
                                         per_depth, summary, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
+sv_status sv_accept_stats_accumulate(const int32_t* depth, const float* alpha,
+                                     const int32_t* accepted_len, int32_t B, int32_t D_max,
+                                     double* accum, float* summary, void* stream) {
+  if (B < 0 || D_max < 0 || D_max > SV_MAX_DEPTH || !accum) return SV_ERR_INVALID_ARGUMENT;
+  if (B > 0 && (!depth || !accepted_len)) return SV_ERR_INVALID_ARGUMENT;
+  const hipError_t e = sv::launch_accumulate(depth, alpha, accepted_len, B, D_max, accum, summary,
+                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 

@@ -261,6 +261,76 @@ hipError_t launch_budget(const float* conf, int32_t B, int32_t D, const int32_t*
   return hipGetLastError();
 }
 
+// The fixed-depth baseline of the budget widget ("AngelSpec: specialize the
+// drafter...", section "D-cut"): the same K positions spread evenly, depth
+// floor(K / B) for every request and one more for the first K mod B, never
+// past D_max.  Scores, the kept utility and the row offsets as k_budget
+// writes them, so that the two allocations' retained utility compare.
+__global__ __launch_bounds__(kBudgetThreads) void k_budget_fixed(const float* conf, int32_t B,
+                                                                 int32_t D, int64_t K,
+                                                                 int32_t* depth,
+                                                                 int64_t* draft_row0,
+                                                                 int64_t* target_row0,
+                                                                 float* utility) {
+  __shared__ BudgetLds S;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  uint64_t key[kKeySlots];
+  float total = build_keys(conf, B, D, nullptr, S, key);
+  const int64_t kk = K < 0 ? 0 : K;
+  const int64_t base = kk / B, extra = kk % B;
+  auto fixed = [&](int r) {
+    const int64_t n = base + (r < extra ? 1 : 0);
+    return (int32_t)(n > D ? D : n);
+  };
+  float kept = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kKeySlots; ++j) {
+    const int i = j * kBudgetThreads + tid;
+    if (i < B * D && (i % D) < fixed(i / D)) kept += __uint_as_float((uint32_t)(key[j] >> 32));
+  }
+  kept = block_sum_budget(kept, S.red);
+  total = block_sum_budget(total, S.red);
+  // row offsets: exclusive scans of n_r and n_r + 1 over the requests, thread
+  // t taking kKeySlots consecutive requests
+  int32_t c[kKeySlots];
+  int32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kKeySlots; ++j) {
+    const int r = tid * kKeySlots + j;
+    c[j] = r < B ? fixed(r) : 0;
+    mine += c[j];
+  }
+  const int32_t wincl = wave_incl_scan(mine);
+  if (lane == kWave - 1) S.wtot[wave] = wincl;
+  __syncthreads();
+  int32_t before = wincl - mine;
+  for (int w = 0; w < wave; ++w) before += S.wtot[w];
+  int64_t dr = before;
+#pragma unroll
+  for (int j = 0; j < kKeySlots; ++j) {
+    const int r = tid * kKeySlots + j;
+    if (r < B) {
+      depth[r] = c[j];
+      if (draft_row0) draft_row0[r] = dr;
+      if (target_row0) target_row0[r] = dr + r;
+    }
+    dr += c[j];
+  }
+  if (utility && tid == 0) {
+    utility[0] = kept;
+    utility[1] = total;
+  }
+}
+
+hipError_t launch_budget_fixed(const float* conf, int32_t B, int32_t D, int64_t K, int32_t* depth,
+                               int64_t* draft_row0, int64_t* target_row0, float* utility,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(k_budget_fixed, dim3(1), dim3(kBudgetThreads), 0, stream, conf, B, D, K,
+                     depth, draft_row0, target_row0, utility);
+  return hipGetLastError();
+}
+
 // D-cut's keep ratio ("AngelSpec: specialize the drafter...", section
 // "D-cut": the ratio is picked each step from a few values by a runtime
 // cost table so as to maximise projected throughput, not kept length).
@@ -429,6 +499,105 @@ __global__ __launch_bounds__(kStatsThreads) void k_accept_stats(
     summary[2] = n > 0.0f ? t / n : 0.0f;
     summary[3] = n;
   }
+}
+
+// Statistics over many verified batches (the decode loop's steps; MAL,
+// mean acceptance and position-wise acceptance over whole generations, as
+// the tradepoint.io page, "The MTP path", reports them).  One workgroup adds
+// one batch to the caller's running totals (float64, so counts stay exact
+// to 2^53) and writes the summary of the new totals.  Layout of accum:
+// [0] tokens emitted (sum of tau + 1), [1] requests, [2] sum of E[tau],
+// [3 + k] requests with depth > k, [3 + D + k] requests with tau > k.
+__global__ __launch_bounds__(kStatsThreads) void k_accept_accumulate(
+    const int32_t* depth, const float* alpha, const int32_t* accepted_len, int32_t B, int32_t D,
+    double* accum, float* summary) {
+  __shared__ int32_t s_ver[kStatsWaves][kWave];
+  __shared__ int32_t s_acc[kStatsWaves][kWave];
+  __shared__ double s_e[kStatsWaves];
+  __shared__ int64_t s_emit[kStatsWaves];
+  __shared__ double s_tot[3 + 2 * kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int32_t ver = 0, acc = 0;
+  double esum = 0.0;  // lane 0
+  int64_t emit = 0;   // lane 0
+  for (int r = wave; r < B; r += kStatsWaves) {
+    int n = depth[r];
+    const int tau = accepted_len[r];
+    const float a_raw = (alpha && lane < D) ? alpha[(int64_t)r * D + lane] : 1.0f;
+    n = n < 0 ? 0 : (n > D ? D : n);
+    if (lane < n) ver += 1;
+    if (lane < D && tau > lane) acc += 1;
+    if (alpha) {
+      const bool in = lane < n;
+      float pref = in ? a_raw : 1.0f;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const float o = __shfl_up(pref, d);
+        if (lane >= d) pref *= o;
+      }
+      const float e = wave_sum(in ? pref : 0.0f);
+      esum += (double)e;
+    }
+    emit += tau + 1;
+  }
+  s_ver[wave][lane] = ver;
+  s_acc[wave][lane] = acc;
+  if (lane == 0) {
+    s_e[wave] = esum;
+    s_emit[wave] = emit;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    if (lane < D) {
+      int32_t v = 0, a = 0;
+      for (int w = 0; w < kStatsWaves; ++w) {
+        v += s_ver[w][lane];
+        a += s_acc[w][lane];
+      }
+      const double tv = accum[3 + lane] + (double)v;
+      const double ta = accum[3 + D + lane] + (double)a;
+      accum[3 + lane] = tv;
+      accum[3 + D + lane] = ta;
+      s_tot[3 + lane] = tv;
+      s_tot[3 + D + lane] = ta;
+    }
+    if (lane == 0) {
+      double e = 0.0;
+      int64_t m = 0;
+      for (int w = 0; w < kStatsWaves; ++w) {
+        e += s_e[w];
+        m += s_emit[w];
+      }
+      const double t0 = accum[0] + (double)m, t1 = accum[1] + (double)B, t2 = accum[2] + e;
+      accum[0] = t0;
+      accum[1] = t1;
+      accum[2] = t2;
+      s_tot[0] = t0;
+      s_tot[1] = t1;
+      s_tot[2] = t2;
+    }
+  }
+  __syncthreads();
+  if (summary && wave == 0) {
+    const double req = s_tot[1];
+    if (lane < D) summary[3 + lane] = req > 0.0 ? (float)(s_tot[3 + D + lane] / req) : 0.0f;
+    if (lane == 0) {
+      double sum_n = 0.0;
+      for (int k = 0; k < D; ++k) sum_n += s_tot[3 + k];
+      summary[0] = req > 0.0 ? (float)(s_tot[0] / req) : 0.0f;
+      summary[1] = req > 0.0 ? (float)(1.0 + s_tot[2] / req) : 0.0f;
+      summary[2] = sum_n > 0.0 ? (float)((s_tot[0] - req) / sum_n) : 0.0f;
+    }
+  }
+}
+
+hipError_t launch_accumulate(const int32_t* depth, const float* alpha, const int32_t* accepted_len,
+                             int32_t B, int32_t D, double* accum, float* summary,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(k_accept_accumulate, dim3(1), dim3(kStatsThreads), 0, stream, depth, alpha,
+                     accepted_len, B, D, accum, summary);
+  return hipGetLastError();
 }
 
 hipError_t launch_stats(const int32_t* depth, const float* alpha, const int32_t* accepted_len,

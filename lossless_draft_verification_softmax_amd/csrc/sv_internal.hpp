@@ -188,6 +188,12 @@ void launch_draw(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_budget(const float* conf, int32_t B, int32_t D, const int32_t* max_depth,
                          int64_t K, int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
                          float* utility, hipStream_t stream);
+hipError_t launch_budget_fixed(const float* conf, int32_t B, int32_t D, int64_t K, int32_t* depth,
+                               int64_t* draft_row0, int64_t* target_row0, float* utility,
+                               hipStream_t stream);
+hipError_t launch_accumulate(const int32_t* depth, const float* alpha, const int32_t* accepted_len,
+                             int32_t B, int32_t D, double* accum, float* summary,
+                             hipStream_t stream);
 hipError_t launch_stats(const int32_t* depth, const float* alpha, const int32_t* accepted_len,
                         int32_t B, int32_t D, float* expected_len, float* per_depth,
                         float* summary, hipStream_t stream);

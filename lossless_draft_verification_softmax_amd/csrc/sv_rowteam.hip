@@ -49,9 +49,16 @@
 // A member publishes n only after it has read every member's n - 1, which
 // every member published only after reading all of n - 2, so by then every
 // reader is done with n - 4, the previous user of the ring slot.  The words
-// are cleared before each launch.  The wait is bounded; on expiry the kernel
-// sets an error word that the accept kernel turns into SV_BIT_SYNC_TIMEOUT
-// on every request, and the member stops waiting.
+// are cleared before each launch.  The wait is bounded.  A team needs all of
+// its members resident at once, which holds when the kernel has the device to
+// itself (one workgroup per CU); when other work holds CUs a member may not
+// start until others finish.  So a member whose wait expires does not depend
+// on the team any more: its communication wave streams the pair's two full
+// rows itself and takes their states from them (slower, same results to
+// rounding), sets a word that the accept kernel reports as
+// SV_BIT_SYNC_TIMEOUT, and from then on polls each later pair once before
+// doing the same.  Tags keep this sound when members fall out of step: a
+// record is used only if it carries the pair's own ordinal.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -62,6 +69,7 @@
 #include "sv_block.hpp"
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
+#include "sv_shard.hpp"
 
 namespace sv {
 
@@ -662,43 +670,92 @@ __device__ __forceinline__ TeamPoll team_poll(const VerifyParams& p, const UnitD
   return t;
 }
 
+// The state (max, sum) of one whole row, streamed by the communication wave
+// alone: the fallback of a member whose team wait expired.  U 16-byte loads
+// per lane in flight, then the ragged tail element by element; the exact wave
+// merge at the end.
+template <typename E, bool SH>
+__device__ SoftmaxPart wave_row_state(const VerifyParams& p, bool draft, int64_t row, float sl) {
+  constexpr int VEC = E::kPerVec;
+  constexpr int U = SH ? 2 : 8;
+  const int lane = threadIdx.x & (kWave - 1);
+  const RowView<E, SH> rv = row_view<E, SH>(p, draft, row);
+  const int64_t nvec = p.V / VEC;
+  SoftmaxPart s{-INFINITY, 0.0f};
+  int64_t v = lane;
+  for (; v + (U - 1) * kWave < nvec; v += U * kWave) {
+    uint4 raw[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) raw[i] = load16(rv.at((v + i * kWave) * VEC));
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float x[VEC];
+      E::unpack(raw[i], x);
+      softmax_group<VEC>(s, x, sl);
+    }
+  }
+  for (; v < nvec; v += kWave) {
+    float x[VEC];
+    E::unpack(load16(rv.at(v * VEC)), x);
+    softmax_group<VEC>(s, x, sl);
+  }
+  for (int64_t i = nvec * VEC + lane; i < p.V; i += kWave) {
+    float x1[1] = {E::load1(rv.at(i), 0)};
+    softmax_group<1>(s, x1, sl);
+  }
+  return wave_merge(s, sl);
+}
+
 // Team wait for row pair u: the records are polled until every member has
-// published (or the bounded wait expires).  Then the members' states are
-// combined into the row log2 normalisers (member 0 also stores the row
-// states in its slots).
+// published (or the bounded wait expires, or the test flag
+// SV_FLAG_TEAM_WAIT_GIVE_UP asks for no wait at all).  Then the members'
+// states are combined into the row log2 normalisers; a member whose wait
+// expired takes them from the two full rows instead.  Member 0 also stores
+// the row states in its slots.
+template <typename E, bool SH>
 __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const UnitDesc& u,
                                                TeamLds& L, int b, int team, int member,
                                                bool& failed) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nt = p.team;
   const uint32_t need = (uint32_t)(u.ordinal + 1);
+  const bool give_up = (p.flags & SV_FLAG_TEAM_WAIT_GIVE_UP) != 0u;
   auto complete = [&](const TeamPoll& q) {
     bool mine = true;
 #pragma unroll
     for (int k = 0; k < 4; ++k) mine = mine && (uint32_t)(q.w[k] >> 32) == need;
     return __all(lane >= nt || mine) != 0;
   };
-  TeamPoll t = team_poll(p, u, team);
-  bool done = complete(t);
-  const uint32_t limit = failed ? 1u : kSpinLimit;
-  for (uint32_t spin = 0; !done && spin < limit; ++spin) {
-    __builtin_amdgcn_s_sleep(1);
+  TeamPoll t{};
+  bool done = false;
+  if (!give_up) {
     t = team_poll(p, u, team);
     done = complete(t);
+    const uint32_t limit = failed ? 1u : kSpinLimit;
+    for (uint32_t spin = 0; !done && spin < limit; ++spin) {
+      __builtin_amdgcn_s_sleep(1);
+      t = team_poll(p, u, team);
+      done = complete(t);
+    }
   }
+  const float sl = u.sl;
+  SoftmaxPart a{-INFINITY, 0.0f}, c{-INFINITY, 0.0f};
   if (!done) {
     if (!failed && lane == 0)
       __hip_atomic_store(p.sync_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     failed = true;
+    const PlanItem* it = p.plan_pairs + ((int64_t)team + (int64_t)p.nteams * u.ordinal);
+    const int64_t trow = it->trow, drow = it->drow;
+    a = wave_row_state<E, SH>(p, false, trow, sl);
+    c = wave_row_state<E, SH>(p, true, drow, sl);
+  } else {
+    if (lane < nt) {
+      a = SoftmaxPart{__uint_as_float((uint32_t)t.w[0]), __uint_as_float((uint32_t)t.w[1])};
+      c = SoftmaxPart{__uint_as_float((uint32_t)t.w[2]), __uint_as_float((uint32_t)t.w[3])};
+    }
+    float none = 0.0f;
+    wave_merge_ref2(a, c, true, none, sl);
   }
-  const float sl = u.sl;
-  SoftmaxPart a{-INFINITY, 0.0f}, c{-INFINITY, 0.0f};
-  if (lane < nt) {
-    a = SoftmaxPart{__uint_as_float((uint32_t)t.w[0]), __uint_as_float((uint32_t)t.w[1])};
-    c = SoftmaxPart{__uint_as_float((uint32_t)t.w[2]), __uint_as_float((uint32_t)t.w[3])};
-  }
-  float none = 0.0f;
-  wave_merge_ref2(a, c, true, none, sl);
   if (lane == 0) {
     // Member 0 replaces its slice states with the row states, so that the
     // accept kernel reads one slot per row of a pair.
@@ -879,7 +936,7 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
       const UnitDesc u = comm_unit(s);
       first_pass_comm(p, u, comm_second(s), L, (int)(s & 1), team, member, um2,
                       (int)((s - 2) & 1));
-      if (wants_alpha(p, u)) team_wait_comm(p, u, L, (int)(s & 1), team, member, failed);
+      if (wants_alpha(p, u)) team_wait_comm<E, SH>(p, u, L, (int)(s & 1), team, member, failed);
       um2 = um1;
       um1 = u;
     }

@@ -98,8 +98,10 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
   if (k == 0) s_bits = 0u;
   if (r == 0 && k == 0) *p.fb_count = 0;  // float64 draw queue, filled by k_draw_pick32
 
+  // a team wait that expired is reported, not an error: the member took the
+  // row normalisers from the full rows instead
+  const uint32_t info = sync_err ? SV_BIT_SYNC_TIMEOUT : 0u;
   uint32_t bits = 0u;
-  if (sync_err) bits |= SV_BIT_SYNC_TIMEOUT;
   if (n < 0 || n > D) bits |= SV_BIT_BAD_DEPTH;
   if (!temperature_ok(T)) bits |= SV_BIT_BAD_TEMPERATURE;
   const bool live = (bits == 0u) && k <= n;
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       p.accepted_len[r] = 0;
       p.num_out[r] = 0;
       p.req[r].mode = kDrawNone;
-      if (p.diag) p.diag[r] = sv_diag{INFINITY, INFINITY, all_bits, 0};
+      if (p.diag) p.diag[r] = sv_diag{INFINITY, INFINITY, all_bits | info, 0};
     }
     return;
   }
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
     if (p.diag) {
       float mm = INFINITY;
       for (int j = 0; j <= tau && j < n; ++j) mm = fminf(mm, s_margin[j]);
-      p.diag[r] = sv_diag{mm, INFINITY, 0u, 0};
+      p.diag[r] = sv_diag{mm, INFINITY, info, 0};
     }
   }
 }

@@ -15,7 +15,10 @@ the draft table Q.  One step, per request:
      first D (a device-side row gather standing in for the target forward
      that produces these rows in a real system);
   3. sv_verify_batch (words 0 and 1 of the same blocks), then
-     sv_accept_stats;
+     sv_accept_stats_accumulate, which adds the step to the running totals
+     (tokens emitted, requests, expected accepted lengths, verified and
+     accepted counts per position) and derives MAL, expected MAL, mean
+     acceptance and the position-wise acceptance P(tau >= k);
   4. the last emitted token is the next step's first context.
 Nothing here synchronises the host inside a step; every computation of the
 method runs in the library's kernels.
@@ -52,11 +55,8 @@ class MarkovDecodeLoop:
         self.verifier.prepare(self.target_rows, self.draft_rows, self.tr0, self.dr0,
                               self.drafts[:, :D], self.depth, self.T, seed=seed, step=0)
         self.step_no = 0
-        # running statistics (device)
-        self.sum_tau = torch.zeros((), dtype=torch.float64, device=self.dev)
-        self.sum_expected = torch.zeros((), dtype=torch.float64, device=self.dev)
-        self.reached = torch.zeros(D, dtype=torch.float64, device=self.dev)
-        self.accepted = torch.zeros(D, dtype=torch.float64, device=self.dev)
+        # running statistics, kept by the library on the device
+        self.stats = sv.AcceptAccumulator(D, self.dev)
         self.steps_done = 0
 
     def step(self):
@@ -73,26 +73,18 @@ class MarkovDecodeLoop:
             torch.index_select(self.Q, 0, ctx[:, :D].reshape(-1), out=self.draft_rows)
         self.verifier.args.step = self.step_no
         out = self.verifier.run()
-        stats = sv.accept_stats(self.depth, out.alpha, out.accepted_len, D)
+        self.stats.add(self.depth, out.alpha, out.accepted_len)
         tau = out.accepted_len.to(torch.int64)
         self.last = out.out_tokens.gather(1, tau[:, None]).reshape(B).to(torch.int32)
-        self.sum_tau += tau.sum()
-        self.sum_expected += stats["expected_len"].to(torch.float64).sum()
-        if D:
-            pd = stats["per_depth"].reshape(3, D).to(torch.float64)
-            self.reached += pd[0]
-            self.accepted += pd[1]
         self.steps_done += 1
         self.step_no += 1
         return out
 
     def summary(self) -> dict:
-        """MAL = 1 + mean tau over requests and steps; expected MAL from the
-        acceptance rates; position-wise acceptance P(position k accepted |
-        reached) over all steps."""
-        n = self.B * max(self.steps_done, 1)
-        acc = (self.accepted / self.reached.clamp(min=1)).cpu().tolist()
-        return {"steps": self.steps_done,
-                "mal": 1.0 + float(self.sum_tau.item()) / n,
-                "expected_mal": 1.0 + float(self.sum_expected.item()) / n,
-                "position_acceptance": acc}
+        """The library's statistics over every step so far: MAL (tokens
+        emitted per request and step), expected MAL from the acceptance
+        rates, mean acceptance (accepted over verified positions) and the
+        position-wise acceptance P(tau >= k), k = 1..D."""
+        s = self.stats.summary.cpu().tolist()
+        return {"steps": self.steps_done, "mal": s[0], "expected_mal": s[1],
+                "mean_acceptance": s[2], "position_acceptance": s[3:]}

@@ -31,6 +31,7 @@ SV_MAX_BUDGET_POSITIONS = 4096
 SV_FLAG_FORCE_FP64_DRAW = 1
 SV_FLAG_STREAMING_ROW_PASS = 2
 SV_FLAG_EXACT_FP64_MASSES = 4
+SV_FLAG_TEAM_WAIT_GIVE_UP = 8
 SV_NUM_STAGE_EVENTS = 5
 
 BIT_BAD_DEPTH = 1
@@ -44,7 +45,8 @@ BIT_SYNC_TIMEOUT = 64
 EXPORTS = ["sv_status_string", "sv_version", "sv_k_rho", "sv_allocate_budget",
            "sv_verify_workspace_bytes", "sv_verify_batch", "sv_accept_stats",
            "sv_draft_confidence_workspace_bytes", "sv_draft_confidence", "sv_select_budget_ratio",
-           "sv_sample_rows", "sv_verify_batch_sharded", "sv_verify_batch_noalloc"]
+           "sv_sample_rows", "sv_verify_batch_sharded", "sv_verify_batch_noalloc",
+           "sv_stream_read", "sv_allocate_fixed_depth", "sv_accept_stats_accumulate"]
 MAX_SHARDS = 16
 MAX_RATIOS = 8
 DCUT_RATIOS = (0.25, 0.5, 0.75, 1.0)
@@ -104,6 +106,12 @@ def load() -> ctypes.CDLL:
     L.sv_allocate_budget.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64, vp,
                                      vp, vp, vp, vp]
     L.sv_allocate_budget.restype = ctypes.c_int
+    L.sv_allocate_fixed_depth.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, vp,
+                                          vp, vp, vp, vp]
+    L.sv_allocate_fixed_depth.restype = ctypes.c_int
+    L.sv_accept_stats_accumulate.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                             vp]
+    L.sv_accept_stats_accumulate.restype = ctypes.c_int
     L.sv_accept_stats.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     L.sv_accept_stats.restype = ctypes.c_int
     L.sv_draft_confidence_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
@@ -127,6 +135,8 @@ def load() -> ctypes.CDLL:
                                           ctypes.c_int64, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                           vp]
     L.sv_verify_batch_sharded.restype = ctypes.c_int
+    L.sv_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]
+    L.sv_stream_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -194,6 +204,24 @@ def allocate_budget(conf: torch.Tensor, K: int, max_depth: torch.Tensor | None =
                                    _ptr(out["draft_row0"]), _ptr(out["target_row0"]),
                                    _ptr(out["utility"]), _stream(dev))
     _check(st, "sv_allocate_budget")
+    return out
+
+
+def allocate_fixed_depth(conf: torch.Tensor, K: int, out: dict | None = None) -> dict:
+    """The fixed-depth baseline on the GPU (sv_allocate_fixed_depth): the same
+    outputs as allocate_budget.  conf: float32 (B, D_max) device tensor."""
+    assert conf.is_cuda and conf.dtype == torch.float32 and conf.is_contiguous()
+    B, D = conf.shape
+    dev = conf.device
+    if out is None:
+        out = dict(depth=torch.empty(B, dtype=torch.int32, device=dev),
+                   draft_row0=torch.empty(B, dtype=torch.int64, device=dev),
+                   target_row0=torch.empty(B, dtype=torch.int64, device=dev),
+                   utility=torch.empty(2, dtype=torch.float32, device=dev))
+    st = load().sv_allocate_fixed_depth(_ptr(conf), B, D, int(K), _ptr(out["depth"]),
+                                        _ptr(out["draft_row0"]), _ptr(out["target_row0"]),
+                                        _ptr(out["utility"]), _stream(dev))
+    _check(st, "sv_allocate_fixed_depth")
     return out
 
 
@@ -443,6 +471,15 @@ def verify(target: torch.Tensor, draft: torch.Tensor | None, target_row0: torch.
     return v.run()
 
 
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks_per_cu: int = 4) -> None:
+    """Calibration: one plain streaming read of buf (sv_stream_read)."""
+    assert buf.is_cuda and buf.is_contiguous() and sink.is_cuda and sink.numel() >= 1
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    st = load().sv_stream_read(_ptr(buf), nbytes, int(blocks_per_cu), _ptr(sink),
+                               _stream(buf.device))
+    _check(st, "sv_stream_read")
+
+
 def accept_stats(depth: torch.Tensor, alpha: torch.Tensor | None, accepted_len: torch.Tensor,
                  D_max: int) -> dict:
     B = depth.numel()
@@ -455,3 +492,21 @@ def accept_stats(depth: torch.Tensor, alpha: torch.Tensor | None, accepted_len: 
                                 _ptr(out["summary"]), _stream(dev))
     _check(st, "sv_accept_stats")
     return out
+
+
+class AcceptAccumulator:
+    """Running acceptance statistics over verified batches
+    (sv_accept_stats_accumulate): totals on the device, summary =
+    (MAL, expected MAL, mean acceptance, P(tau >= 1..D_max))."""
+
+    def __init__(self, D_max: int, device):
+        self.D = D_max
+        self.accum = torch.zeros(3 + 2 * D_max, dtype=torch.float64, device=device)
+        self.summary = torch.zeros(3 + D_max, dtype=torch.float32, device=device)
+
+    def add(self, depth: torch.Tensor, alpha: torch.Tensor | None, accepted_len: torch.Tensor):
+        st = load().sv_accept_stats_accumulate(_ptr(depth), _ptr(alpha), _ptr(accepted_len),
+                                               depth.numel(), self.D, _ptr(self.accum),
+                                               _ptr(self.summary), _stream(depth.device))
+        _check(st, "sv_accept_stats_accumulate")
+        return self.summary

@@ -85,7 +85,9 @@ def test_verify_validation_codes(sv):
     assert call(sv, _args(sv, V=0)) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(sv, _args(sv, row_stride=32)) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(sv, _args(sv, dtype=7)) == sv.SV_ERR_UNSUPPORTED
-    assert call(sv, _args(sv, flags=8)) == sv.SV_ERR_UNSUPPORTED
+    assert call(sv, _args(sv, flags=16)) == sv.SV_ERR_UNSUPPORTED
+    # a known flag passes validation (the too-small workspace is caught next)
+    assert call(sv, _args(sv, flags=sv.SV_FLAG_TEAM_WAIT_GIVE_UP)) == sv.SV_ERR_WORKSPACE_TOO_SMALL
     assert call(sv, _args(sv, target_logits=None)) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(sv, _args(sv, draft_row0=None)) == sv.SV_ERR_INVALID_ARGUMENT
     assert call(sv, _args(sv, target_logits=(1 << 20) + 2)) == sv.SV_ERR_UNSUPPORTED
@@ -211,3 +213,21 @@ def test_sharded_verify_validation_codes(sv):
     assert call(stride=60) == sv.SV_ERR_INVALID_ARGUMENT   # stride below the shard width
     assert call(dshards=(fake, fake)) == sv.SV_ERR_INVALID_ARGUMENT            # no draft_row0
     assert call(B=0) == sv.SV_OK
+
+
+def test_noalloc_and_stream_read_validation_codes(sv):
+    lib = sv.load()
+    fake = 1 << 20
+    # sizes whose workspace exceeds the static scratch: rejected on the host
+    big = _args(sv, B=4096, D_max=64, V=262144, row_stride=262144)
+    assert lib.sv_verify_batch_noalloc(ctypes.byref(big), None) == sv.SV_ERR_SCRATCH_TOO_SMALL
+    assert lib.sv_verify_batch_noalloc(None, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert "scratch" in sv.status_string(sv.SV_ERR_SCRATCH_TOO_SMALL)
+    sink = fake
+    assert lib.sv_stream_read(None, 1024, 4, sink, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert lib.sv_stream_read(fake + 4, 1024, 4, sink, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert lib.sv_stream_read(fake, 1000, 4, sink, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert lib.sv_stream_read(fake, 1024, 0, sink, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert lib.sv_stream_read(fake, 1024, 33, sink, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert lib.sv_stream_read(fake, 1024, 4, None, None) == sv.SV_ERR_INVALID_ARGUMENT
+    assert lib.sv_stream_read(fake, 0, 4, sink, None) == sv.SV_OK

@@ -86,12 +86,13 @@ def test_decode_loop_matches_oracle(dtype):
     temps = np.array([0.0, 0.7, 1.0, 1.3, 1.0, 0.5], np.float32)
     loop = MarkovDecodeLoop(P.to(DEV), Q.to(DEV), torch.from_numpy(start), D,
                             torch.from_numpy(temps), seed=42)
-    got = []
+    got, accs = [], []
     for _ in range(steps):
         out = loop.step()
         tau = out.accepted_len.cpu().numpy()
         toks = out.out_tokens.cpu().numpy()
         got.append([list(toks[r, : tau[r] + 1]) for r in range(B)])
+        accs.append((loop.stats.accum.cpu().numpy().copy(), loop.stats.summary.cpu().numpy().copy()))
     ref = oracle.markov_decode(P.float().numpy(), Q.float().numpy(), start, D, temps, steps,
                                seed=42)
     live = [True] * B
@@ -107,8 +108,50 @@ def test_decode_loop_matches_oracle(dtype):
             assert got[s][r] == ref["emitted"][s][r], (s, r, got[s][r], ref["emitted"][s][r])
             compared += 1
     assert compared >= B * steps * 0.9
+    # The library's running statistics against the oracle's loop, step by
+    # step while no request's streams may have parted: the counts (tokens
+    # emitted, requests, verified and accepted per position) exactly, the
+    # summary (MAL, mean acceptance, P(tau >= k)) to float32 rounding.
+    parted = min([s for s in range(steps) for r in range(B)
+                  if min(ref["step_margins"][s][r][0], ref["step_margins"][s][r][2]) < DRAW_BAND
+                  or ref["step_margins"][s][r][1] < ACCEPT_BAND] + [steps])
+    for s in range(parted):
+        g_acc, g_sum = accs[s]
+        o_acc, o_sum = ref["step_stats"][s]
+        keep = np.r_[0, 1, np.arange(3, 3 + 2 * D)]   # [2]: the oracle's loop has no alpha
+        assert np.array_equal(g_acc[keep], o_acc[keep]), (s, g_acc, o_acc)
+        sel = np.r_[0, 2, np.arange(3, 3 + D)]
+        assert np.allclose(g_sum[sel], o_sum[sel], rtol=1e-6), (s, g_sum, o_sum)
+    assert parted >= steps // 2
     summ = loop.summary()
     mean_tau = np.mean([len(e) - 1 for st in got for e in st])
-    assert summ["mal"] == pytest.approx(1.0 + mean_tau, rel=1e-9)
+    assert summ["mal"] == pytest.approx(1.0 + mean_tau, rel=1e-6)
+    assert summ["mal"] == pytest.approx(1.0 + sum(summ["position_acceptance"]), rel=1e-6)
+    assert summ["mal"] == pytest.approx(1.0 + D * summ["mean_acceptance"], rel=1e-6)
     assert 1.0 <= summ["mal"] <= D + 1
     assert len(summ["position_acceptance"]) == D
+
+
+def test_accept_accumulate_matches_oracle():
+    """sv_accept_stats_accumulate over several batches (ragged and
+    out-of-range depths, random acceptance rates, D up to 64) against the
+    oracle's accept_accumulate: counts exactly, the sum of E[tau] within 1e-5
+    relative, the summary to float32 rounding."""
+    rng = np.random.default_rng(31)
+    for D in (1, 3, 16, 64):
+        acc = sv.AcceptAccumulator(D, DEV)
+        ref = None
+        for _ in range(5):
+            B = int(rng.integers(1, 300))
+            depth = rng.integers(-1, D + 2, size=B).astype(np.int32)
+            tau = np.minimum(rng.integers(0, D + 1, size=B), np.clip(depth, 0, D)).astype(np.int32)
+            alpha = rng.uniform(0, 1, size=(B, D)).astype(np.float32)
+            acc.add(torch.from_numpy(depth).to(DEV), torch.from_numpy(alpha).to(DEV),
+                    torch.from_numpy(tau).to(DEV))
+            ref, summ = oracle.accept_accumulate(depth, alpha.astype(np.float64), tau, D, ref)
+            g = acc.accum.cpu().numpy()
+            counts = np.r_[0, 1, np.arange(3, 3 + 2 * D)]
+            assert np.array_equal(g[counts], ref[counts])
+            assert g[2] == pytest.approx(ref[2], rel=1e-5)
+            assert np.allclose(acc.summary.cpu().numpy().astype(np.float64), summ, rtol=1e-5,
+                               atol=1e-7)

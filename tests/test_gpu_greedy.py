@@ -116,7 +116,7 @@ def test_greedy_argmax_edge_rows(dtype, V, row_pass):
                    torch.from_numpy(depth).to(DEV), torch.from_numpy(temps).to(DEV), flags=flags,
                    V=V)
     o = oracle_verify(Ph, None, tr0.cpu().numpy(), None, tokens, depth, temps, np.arange(B))
-    compare(g, o, np.arange(B), temps, depth, check_alpha=False)
+    compare(g, o, np.arange(B), temps, depth, check_alpha=False, check_flag_rate=False)
     # the patterns above decide: valid requests accept both drafts
     valid = [0, 1, 5, 6, 7]
     assert np.all(g["bits"][[2, 3, 4]] & sv.BIT_BAD_ROW)

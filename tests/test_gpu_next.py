@@ -17,6 +17,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 CONF_RTOL = 1e-5      # float32 normalisers against the oracle's long double
 CONF_ATOL = 1e-12
+CHOICE_BAND = 2e-6    # keep-ratio choices whose best projections lie this close are flagged
+FLAGGED_CHOICES = []
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -113,8 +115,15 @@ def check_choice(conf, ratios, tb, tl, max_depth=None):
     proj = g["projected"].cpu().numpy().astype(np.float64)
     assert np.allclose(proj, o["projected"], rtol=1e-5)
     j = int(g["choice"].item())
-    # the choice is a best ratio up to float32 rounding of the utilities
-    assert o["projected"][j] >= o["projected"].max() * (1 - 1e-5)
+    # The choice must be the oracle's, except where the oracle's best
+    # projection and another ratio's lie within CHOICE_BAND of each other
+    # (the GPU sums the kept utility in float32: relative error under
+    # 13 * 2^-24 for up to 4096 positions, 1e-6 with margin); such a choice
+    # is flagged and may be any ratio inside the band.
+    if j != o["choice"]:
+        best = o["projected"].max()
+        assert o["projected"][j] >= best * (1 - CHOICE_BAND), (j, o["choice"], o["projected"])
+        FLAGGED_CHOICES.append((j, o["choice"]))
     B, D = conf.shape
     lim = np.full(B, D) if max_depth is None else np.clip(max_depth, 0, D)
     K = int(g["K"].item())
@@ -138,6 +147,56 @@ def test_ratio_choice_c4_confidences():
         tl = (base + slope * np.array(ratios)[None, :]).astype(np.float32)
         md = rng.integers(0, D + 1, size=B).astype(np.int32) if trial % 3 == 0 else None
         check_choice(conf, ratios, tb, tl, md)
+
+
+def test_ratio_choice_flag_count():
+    """Across the random choices above, choices that differ from the oracle's
+    (only ever inside the flag band) stay rare."""
+    rng = np.random.default_rng(13)
+    ratios = list(sv.DCUT_RATIOS)
+    n = 0
+    start = len(FLAGGED_CHOICES)
+    for trial in range(40):
+        B = int(rng.integers(1, 65))
+        D = int(rng.integers(1, 17))
+        conf = beta_conf(rng, B, D)
+        tl = (rng.uniform(10, 20) + rng.uniform(0, 40) * np.array(ratios))[None, :].astype(
+            np.float32)
+        check_choice(conf, ratios, [B], tl)
+        n += 1
+    flagged = len(FLAGGED_CHOICES) - start
+    print(f"keep-ratio choices: {n}, flagged and different from the oracle: {flagged}")
+    assert flagged <= 1
+
+
+def test_fixed_depth_parity():
+    """sv_allocate_fixed_depth against the oracle's fixed-depth baseline:
+    depths and row offsets bit-exact, utilities within 1e-5 relative, on the
+    hand-worked case, the c4 confidences and random shapes with NaN and
+    out-of-range confidences and K below 0 and past B D."""
+    cases = [(np.array([[0.75, 0.75, 0.5], [0.25, 1.0, 1.0]], np.float32), [1, 3, 4, 6, 9])]
+    cases.append((synth.make("c4", device="cpu", V=8).conf.numpy(), [0, 1, 63, 256, 512, 1024]))
+    rng = np.random.default_rng(14)
+    for _ in range(30):
+        B = int(rng.integers(1, 200))
+        D = int(rng.integers(0, 20))
+        if B * D > sv.SV_MAX_BUDGET_POSITIONS:
+            D = sv.SV_MAX_BUDGET_POSITIONS // B
+        conf = rng.beta(3, 2, size=(B, D)).astype(np.float32)
+        conf[rng.random((B, D)) < 0.05] = np.nan
+        conf[rng.random((B, D)) < 0.05] = 1.5
+        cases.append((conf, [int(rng.integers(-3, B * D + 5)) for _ in range(3)]))
+    for conf, Ks in cases:
+        c_dev = torch.from_numpy(np.ascontiguousarray(conf)).to(DEV)
+        for K in Ks:
+            g = sv.allocate_fixed_depth(c_dev, K)
+            torch.cuda.synchronize()
+            o = oracle.fixed_depth_budget(conf, K)
+            assert np.array_equal(g["depth"].cpu().numpy(), o["depth"]), (conf.shape, K)
+            assert np.array_equal(g["draft_row0"].cpu().numpy(), o["draft_row0"])
+            assert np.array_equal(g["target_row0"].cpu().numpy(), o["target_row0"])
+            assert np.allclose(g["utility"].cpu().numpy().astype(np.float64), o["utility"],
+                               rtol=1e-5, atol=1e-30)
 
 
 def test_ratio_choice_ties_and_extremes():

@@ -1,7 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded synthetic inputs, for the five workloads (c1 tiny, c2 MTP chat,
 c3 block at T = 0 and T = 1, c4 budget, c5 mixed temperature) and the full
-64 x 16 x 151936 bf16 batch the benchmark times."""
+64 x 16 x 151936 bf16 batch the benchmark times, every request of each
+against the oracle (its requests spread over a pool of host threads)."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,8 @@ import torch
 import oracle
 from lossless_draft_verification_softmax_amd import specverify as sv
 from lossless_draft_verification_softmax_amd import synth
-from tests.parity import (compare, gpu_verify, host_f32, oracle_verify, padded_offsets)
+from tests.parity import (compare, gpu_verify, host_f32, oracle_verify_parallel,
+                          padded_offsets)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +36,9 @@ def full_depth_case(name, B=None, V=None, seeds=(0,), sample=None, flags=0):
     for seed in seeds:
         g = gpu_verify(w.target, w.draft, tr0, dr0, w.draft_tokens, depth, w.temperature,
                        seed=seed, flags=flags)
-        o = oracle_verify(th, dh, tr0.cpu().numpy(), dr0.cpu().numpy(), w.draft_tokens.cpu().numpy(),
-                          depth.cpu().numpy(), temps, reqs, seed=seed)
+        o = oracle_verify_parallel(th, dh, tr0.cpu().numpy(), dr0.cpu().numpy(),
+                                   w.draft_tokens.cpu().numpy(), depth.cpu().numpy(), temps, reqs,
+                                   seed=seed)
         reports.append(compare(g, o, reqs, temps, depth.cpu().numpy()))
     return reports
 
@@ -79,8 +82,25 @@ def test_c3_block_t0_full():
     full_depth_case("c3_t0")
 
 
-def test_c3_block_t1_sampled():
-    full_depth_case("c3", sample=[0, 5, 13, 31])
+def test_c3_block_t1_full():
+    rep = full_depth_case("c3")
+    print(rep)
+
+
+def test_flag_rate_many_draws():
+    """Draws the oracle flags (accept margin under 1e-5, CDF margin under
+    1e-12) stay below 1e-4 of all draws over many seeds of the MTP-chat and
+    block workloads, and every unflagged draw matches the oracle."""
+    reps = full_depth_case("c2", seeds=range(2, 222)) + full_depth_case("c3", seeds=(1, 2, 3, 4))
+    draws = sum(r["draws"] for r in reps)
+    flagged = sum(r["flagged"] for r in reps)
+    literal = sum(r["flagged_literal"] for r in reps)
+    print(f"draws={draws} flagged={flagged} flagged_literal_1e-5={literal} "
+          f"mismatched={sum(r['mismatched'] for r in reps)} "
+          f"fp64_draws={sum(r['fp64_draws'] for r in reps)} "
+          f"max_draw_margin_err32={max(r['max_draw_margin_err32'] for r in reps):.3g}")
+    assert draws > 10000
+    assert flagged < 1e-4 * draws
 
 
 def budget_case(name, sample=None, packed=True, flags=0):
@@ -111,8 +131,8 @@ def budget_case(name, sample=None, packed=True, flags=0):
     th, dh = host_f32(target).reshape(-1, V), host_f32(w.draft).reshape(-1, V)
     temps = w.temperature.cpu().numpy()
     reqs = np.arange(B) if sample is None else np.asarray(sample)
-    o = oracle_verify(th, dh, tr0.cpu().numpy(), dr0.cpu().numpy(), w.draft_tokens.cpu().numpy(),
-                      depth, temps, reqs)
+    o = oracle_verify_parallel(th, dh, tr0.cpu().numpy(), dr0.cpu().numpy(),
+                               w.draft_tokens.cpu().numpy(), depth, temps, reqs)
     return compare(g, o, reqs, temps, depth), g, depth
 
 
@@ -129,18 +149,17 @@ def test_c4_packed_equals_padded():
         assert np.array_equal(g1[k], g2[k])
 
 
-def test_c5_mixed_temperature_sampled():
-    w = synth.make("c5", device="cpu", B=64, V=8)  # temperatures only
-    temps = w.temperature.numpy()
-    pick = [int(np.flatnonzero(temps == t)[i]) for t in (0.0, 0.6, 1.0) for i in range(3)]
-    rep, _, _ = budget_case("c5", sample=sorted(pick))
+def test_c5_mixed_temperature_full():
+    rep, _, _ = budget_case("c5")
     print(rep)
 
 
-def test_c4full_bench_config_sampled():
+def test_c4full_bench_config_full():
     """The batch the benchmark times: 64 x 16 x 151936 bf16 at K = 1024 (every
-    position), through the budget and the packed row offsets it returns."""
-    rep, g, depth = budget_case("c4full", sample=[0, 17, 45, 63])
+    position), through the budget and the packed row offsets it returns;
+    every request against the oracle."""
+    rep, g, depth = budget_case("c4full")
+    print(rep)
     assert np.all(depth == 16)
     assert np.all(g["num_out"] == g["accepted_len"] + 1)
 

@@ -82,7 +82,7 @@ def test_random_shapes(dtype, trial, row_pass):
     Qh = Qd.float().cpu().numpy()[:, :V].copy()
     o = oracle_verify(Ph, Qh, tr0.cpu().numpy(), dr0.cpu().numpy(), tokens.reshape(B, D), depth,
                       temps, np.arange(B), seed=seed, step=step, request_id=rid, D_max=D)
-    rep = compare(g, o, np.arange(B), temps, depth)
+    rep = compare(g, o, np.arange(B), temps, depth, check_flag_rate=False)
     assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"]
 
 
@@ -105,7 +105,7 @@ def test_invalid_inputs():
                    torch.from_numpy(temps).to(DEV))
     o = oracle_verify(P, Q, tr0.cpu().numpy(), dr0.cpu().numpy(), tokens, depth, temps,
                       np.arange(B), D_max=D)
-    compare(g, o, np.arange(B), temps, depth)
+    compare(g, o, np.arange(B), temps, depth, check_flag_rate=False)
     assert list(g["bits"][1:8]) == [sv.BIT_BAD_ROW, sv.BIT_BAD_ROW, sv.BIT_BAD_ROW,
                                     sv.BIT_BAD_TOKEN, sv.BIT_BAD_TOKEN, sv.BIT_BAD_DEPTH,
                                     sv.BIT_BAD_TEMPERATURE]
@@ -143,7 +143,7 @@ def test_degenerate_shapes():
                    torch.zeros(B, dtype=torch.int32, device=DEV), torch.from_numpy(temps).to(DEV))
     o = oracle_verify(P, None, tr0.cpu().numpy(), None, np.zeros((B, 0), np.int32),
                       np.zeros(B, np.int32), temps, np.arange(B), D_max=0)
-    compare(g, o, np.arange(B), temps, np.zeros(B, np.int32))
+    compare(g, o, np.arange(B), temps, np.zeros(B, np.int32), check_flag_rate=False)
     assert np.all(g["num_out"] == 1)
     # V = 1: p = q = 1, every draft kept, bonus token 0
     B, D = 3, 4
@@ -168,7 +168,7 @@ def test_draft_logits_absent_with_sampling_request():
     assert g["bits"][0] == 0 and g["bits"][1] == sv.BIT_BAD_ROW and g["bits"][2] == 0
     o = oracle_verify(P.cpu().numpy(), None, tr0.cpu().numpy(), None, tokens, depth, temps,
                       np.arange(B))
-    compare(g, o, np.arange(B), temps, depth, check_alpha=False)
+    compare(g, o, np.arange(B), temps, depth, check_alpha=False, check_flag_rate=False)
 
 
 def test_identical_draft_accepts_all_on_gpu():
@@ -282,7 +282,7 @@ def test_extreme_logit_ranges(dtype, row_pass):
     Qh = Qd.float().cpu().numpy()
     o = oracle_verify(Ph, Qh, tr0.cpu().numpy(), dr0.cpu().numpy(), tokens, depth, temps,
                       np.arange(B), seed=9)
-    rep = compare(g, o, np.arange(B), temps, depth)
+    rep = compare(g, o, np.arange(B), temps, depth, check_flag_rate=False)
     assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"]
     assert np.all(g["bits"] & sv.BIT_SYNC_TIMEOUT == 0)
 
@@ -314,7 +314,7 @@ def test_long_fp32_rows_low_temperature(row_pass):
                    flags=sv.SV_FLAG_STREAMING_ROW_PASS if row_pass == "stream" else 0)
     o = oracle_verify(P, Q, tr0.cpu().numpy(), dr0.cpu().numpy(), tokens, depth, temps,
                       np.arange(B), seed=5)
-    rep = compare(g, o, np.arange(B), temps, depth)
+    rep = compare(g, o, np.arange(B), temps, depth, check_flag_rate=False)
     assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"]
 
 
@@ -351,7 +351,7 @@ def test_large_references_low_temperature(dtype, row_pass):
                    flags=sv.SV_FLAG_STREAMING_ROW_PASS if row_pass == "stream" else 0)
     o = oracle_verify(Ph, Qh, tr0.cpu().numpy(), dr0.cpu().numpy(), tokens, depth, temps,
                       np.arange(B), seed=9)
-    rep = compare(g, o, np.arange(B), temps, depth)
+    rep = compare(g, o, np.arange(B), temps, depth, check_flag_rate=False)
     assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"]
     conf = sv.draft_confidence(Qd, dr0, tok_d, temps_d).cpu().numpy().astype(np.float64)
     ref = oracle.draft_confidence(Qh, dr0.cpu().numpy(), tokens, temps)

@@ -80,5 +80,5 @@ def test_random_sweep(sweep_seed):
                            torch.from_numpy(c["depth"]).to(DEV),
                            torch.from_numpy(c["temps"]).to(DEV), seed=c["seed"], flags=flags,
                            V=c["V"])
-            rep = compare(g, o, np.arange(B), c["temps"], c["depth"])
+            rep = compare(g, o, np.arange(B), c["temps"], c["depth"], check_flag_rate=False)
             assert rep["mismatched"] == 0 or rep["flagged"] >= rep["mismatched"], (case, flags)
