@@ -3,14 +3,14 @@
 roofline of the dominant kernel and the CPU oracle timed beside it.
 
 One step = the whole hot path on one batch already resident in HBM:
-  sv_allocate_budget (prefix-confidence products + LDS bitonic top-K)
+  sv_allocate_budget (prefix-confidence products + radix select of the top K)
   -> sv_verify_batch (row statistics, acceptance rates, accept scan, draw)
   -> sv_accept_stats.
 Default workload: the 64 x 16 x 151936 bf16 batch at T = 1 with the budget
 keeping every position (K = 1024).  Inputs are synthetic (seeded Gaussian
-logits shaped like the AngelSpec pages' block-drafting workload).  Two input
-copies alternate between steps so that no step finds its logits in the
-256 MB Infinity Cache.
+logits shaped like the AngelSpec pages' block-drafting workload).  Four input
+copies rotate between steps so that no step finds its logits in the 256 MB
+Infinity Cache.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4full]
 Prints one JSON line.
@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the draft-side, decode-loop and sharded figures (profiling runs)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain streaming-read measurement (k_stream_read)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(a reference dispatch for scaling rocprofv3 byte counters)")
@@ -128,12 +130,68 @@ def cpu_baseline(w, target_packed, depth, tr0, dr0, seconds: float):
         for f in [ex.submit(worker) for _ in range(workers)]:
             f.result()
     elapsed = time.perf_counter() - t0
+    # the same oracle on one core: requests in order, one per call, until the
+    # batch is done or a third of the budget has passed
+    t1 = time.perf_counter()
+    one_pos = one_done = 0
+    for r in range(w.B):
+        if time.perf_counter() - t1 >= seconds / 3.0:
+            break
+        oracle.verify_batch(th, dh, tr[r:r + 1], dr[r:r + 1], tok[r:r + 1], dep[r:r + 1],
+                            temps[r:r + 1], request_id=np.array([r], np.uint32), D_max=w.D)
+        one_pos += int(dep[r])
+        one_done += 1
+    one_s = time.perf_counter() - t1
     return dict(value=state["positions"] / elapsed, unit="positions/s", cores=workers,
                 kind="oracle",
                 sample=f"{state['done']} of {w.B} requests ({state['positions']} verified "
                        f"positions) of the {w.name} batch, one request per call on "
                        f"{workers} host threads, {elapsed:.1f} s wall; budget "
-                       f"{budget_s * 1e3:.2f} ms single-threaded")
+                       f"{budget_s * 1e3:.2f} ms single-threaded",
+                cpu_model=cpu_model(),
+                single_core={"value": one_pos / one_s if one_s > 0 else None,
+                             "unit": "positions/s", "cores": 1,
+                             "sample": f"requests 0..{one_done - 1} of the {w.name} batch "
+                                       f"({one_pos} verified positions) in order on one host "
+                                       f"thread, {one_s:.1f} s"})
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo, as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_ceiling(sv, torch, dev, nbytes: int, reps: int = 10):
+    """The chip's plain streaming-read rate (sv_stream_read) over two buffers
+    of the row pass's algorithmic size, read alternately so that neither is
+    served from the 256 MB Infinity Cache: the best of three launch shapes."""
+    n = (nbytes + 15) // 16 * 16
+    bufs = [torch.full((n // 4,), 1.0, dtype=torch.float32, device=dev) for _ in range(2)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = None
+    for per_cu in (2, 4, 8):
+        for b in bufs:
+            sv.stream_read(b, sink, per_cu)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            sv.stream_read(bufs[i % 2], sink, per_cu)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, per_cu)
+    del bufs
+    return {"kernel": "k_stream_read", "bytes": n, "GBps": round(best[0], 1),
+            "workgroups_per_cu": best[1], "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
 
 
 def draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize):
@@ -186,6 +244,20 @@ def draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize):
     torch.cuda.synchronize()
     sel_us = e0.elapsed_time(e1) / n * 1e3
     ach = conf_bytes / (conf_us * 1e-6) / 1e9
+    # utility retained at the chosen K: the global top-K against the
+    # fixed-depth baseline (the budget widget's comparison)
+    K_sel = int(sel["K"].item())
+
+    def retained_at(c):
+        ug = sv.allocate_budget(c, K_sel)["utility"].cpu().tolist()
+        uf = sv.allocate_fixed_depth(c, K_sel)["utility"].cpu().tolist()
+        return {"global": round(ug[0] / ug[1], 4) if ug[1] else None,
+                "fixed": round(uf[0] / uf[1], 4) if uf[1] else None}
+
+    retained = {"K": K_sel, "kernels": "k_budget, k_budget_fixed",
+                "drafter_confidence": retained_at(conf)}
+    if w.conf is not None:  # the workload's Beta(8, 2) / Beta(3, 3) confidences
+        retained["beta_confidence"] = retained_at(w.conf.to(conf.device).contiguous())
     return {
         "draft_confidence": {"kernels": "k_conf_part + k_conf_final", "us": round(conf_us, 2),
                              "algorithmic_bytes": conf_bytes, "achieved_GBps": round(ach, 1),
@@ -194,6 +266,7 @@ def draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize):
                          "ratios": ratios, "verify_us_at_ratio": [round(x, 1) for x in lat],
                          "projected_tokens_per_us": [round(float(x), 5) for x in sel["projected"].cpu()],
                          "choice": int(sel["choice"].item()), "K": int(sel["K"].item())},
+        "utility_retained": retained,
     }
 
 
@@ -263,7 +336,8 @@ def decode_loop_figure(sv, torch, dev, V=32768, B=64, D=8, steps=30):
     return {"workload": f"Markov target V={V} bf16, B={B}, D={D}, T=1", "us_per_step": round(us, 1),
             "emitted_tokens_per_s": round(float(emitted.item()) / (us * steps * 1e-6), 1),
             "mal": round(summ["mal"], 4), "expected_mal": round(summ["expected_mal"], 4),
-            "position_acceptance": [round(x, 4) for x in summ["position_acceptance"]]}
+            "mean_acceptance": round(summ["mean_acceptance"], 4),
+            "position_acceptance_P_tau_ge_k": [round(x, 4) for x in summ["position_acceptance"]]}
 
 
 def main():
@@ -382,6 +456,22 @@ def main():
     stage_ms = [sum(evs[j].elapsed_time(evs[j + 1]) for evs in events) / n_st
                 for j in range(nev - 1)]
 
+    # Step-time distribution: one event between consecutive steps (each
+    # recorded event leaves a few microseconds of idle GPU, so these spans
+    # sit slightly above the timed loop's mean).
+    n_ds = max(args.steps, 20)
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(n_ds + 1)]
+    torch.cuda.synchronize()
+    bounds[0].record()
+    for i in range(n_ds):
+        step(verifiers[i % len(verifiers)])
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    spans = sorted(bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(n_ds))
+
+    def pct(q):
+        return round(spans[min(n_ds - 1, int(round(q * (n_ds - 1))))], 2)
+
     achieved = rowpass_bytes / (rowpass_ms * 1e-3) / 1e9
     digest = source_digest(row_kernel)
     traffic = measured_traffic(row_kernel, args.workload, digest)
@@ -411,6 +501,8 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": rowpass_bytes,
                      "avg_launch_us": round(rowpass_ms * 1e3, 2)},
+        "step_us_distribution": {"p10": pct(0.10), "p50": pct(0.50), "p90": pct(0.90),
+                                 "steps": n_ds, "note": "one event per step boundary"},
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": step_bytes,
         "stages_us": {"plan": round(stage_ms[0] * 1e3, 2), "rowpass": round(stage_ms[1] * 1e3, 2),
@@ -420,6 +512,10 @@ def main():
         "expected_mean_accepted_length": round(float(stats_out["summary"][1]), 4),
         "source_digest": digest,
     }
+    if not args.no_read_ceiling:
+        rc = read_ceiling(sv, torch, dev, rowpass_bytes)
+        rc["rowpass_frac_of_ceiling"] = round(achieved / rc["GBps"], 4)
+        res["read_ceiling"] = rc
     if D > 0 and draft_rows > 0 and not args.no_extras:
         res["draft_side"] = draft_side(sv, torch, w, copies, dr0, bud, verifiers, esize)
         res["decode_loop"] = decode_loop_figure(sv, torch, dev)
