@@ -163,6 +163,8 @@ sv_status run_verify(const sv_verify_args* a, int32_t nshard, int64_t shard_w,
   p.part_p = reinterpret_cast<float2*>(ws + L.part_p);
   p.part_q = reinterpret_cast<float2*>(ws + L.part_q);
   p.part_a = reinterpret_cast<float*>(ws + L.part_a);
+  p.pair_p = reinterpret_cast<float2*>(ws + L.pair_p);
+  p.pair_q = reinterpret_cast<float2*>(ws + L.pair_q);
   p.req = reinterpret_cast<sv::DrawState*>(ws + L.req);
   p.seg_w32 = reinterpret_cast<float*>(ws + L.seg_w32);
   p.seg_zp64 = reinterpret_cast<double*>(ws + L.seg_zp64);

@@ -1,18 +1,14 @@
-// sv_draw.hip -- the emitted token at the stop position: inverse-CDF draw
-// from normalize(max(0, p - q)) after a rejection, or from p after a fully
-// accepted block (the standard rejection-sampling rule behind the lossless
-// verification of the tradepoint.io page, "Why one universal drafter
-// underperforms").
+// sv_draw.hip -- the float64 recompute of the draws that the float32 draw
+// of the accept-and-draw kernel (sv_verify.hip) leaves too close to a CDF
+// boundary: inverse-CDF draw from normalize(max(0, p - q)) after a
+// rejection, or from p after a fully accepted block (the standard
+// rejection-sampling rule behind the lossless verification of the
+// tradepoint.io page, "Why one universal drafter underperforms").
 //
 // The row is cut into tiles of 2048 elements (one 16-byte load of bf16 per
 // thread of a 256-thread workgroup).  A tile's mass is the last value of a
 // fixed-order block scan of its weights, so the pass that finds the crossing
 // tile and the pass that scans inside it agree bit for bit.
-//   k_draw_mass32   float32 mass of every tile of every request's draw row
-//   k_draw_pick32   scan of the tile masses -> crossing tile -> LDS block scan
-//                   inside it -> token.  A draw whose float32 CDF margin is
-//                   under 1e-5 (or that rounding leaves undecided) is queued
-//                   for float64.
 //   k_draw_tile64   one float64 pass over the rows of queued requests: tile
 //                   normaliser partials and the one-pass split of the tile
 //                   residual masses
@@ -27,40 +23,13 @@
 #include "specverify.h"
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
+#include "sv_drawrow.hpp"
 #include "sv_shard.hpp"
 
 namespace sv {
 
 constexpr int kDrawThreads = 256;
-constexpr int kPer = 8;  // elements per thread per tile
-constexpr float kDrawMargin32 = 1e-5f;
 constexpr int kQueueGrid = 2048;
-
-// Eight consecutive logits starting at i0 (< hi, a multiple of 8); entries at
-// or past hi read as -inf, which gives them weight 0.  The eight never cross a
-// vocabulary shard.
-template <typename E, bool SH>
-__device__ __forceinline__ void load8(const RowView<E, SH>& row, int64_t i0, int64_t hi,
-                                      float (&x)[kPer]) {
-  if (i0 + kPer <= hi) {
-    const typename E::Storage* g = row.at(i0);
-    if constexpr (E::kPerVec == 8) {
-      E::unpack(load16(g), x);
-    } else {
-      float a[4], b[4];
-      E::unpack(load16(g), a);
-      E::unpack(load16(g + 4), b);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = a[j];
-        x[4 + j] = b[j];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) x[j] = (i0 + j < hi) ? E::load1(row.at(i0 + j), 0) : -INFINITY;
-  }
-}
 
 // Fixed-order block scan (Hillis-Steele in each wavefront, wave totals in
 // order).  Returns the inclusive value; *total gets the block total.
@@ -120,49 +89,6 @@ __device__ __forceinline__ T block_sum256(T v, T* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// Weights.
-template <typename E, bool SH>
-struct Weights32 {
-  RowView<E, SH> prow, qrow;
-  bool has_q;  // false: bonus draw (w = p)
-  float sl, cp, lzp, cq, lzq;  // references R(m) and log2 sums of the rows
-  // weights of eight logits a (target) and b (draft; unused for a bonus draw)
-  __device__ __forceinline__ void from(const float (&a)[kPer], const float (&b)[kPer],
-                                       float (&w)[kPer]) const {
-    if (!has_q) {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) w[j] = exp2_fast(__builtin_fmaf(a[j], sl, -cp) - lzp);
-      return;
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const float pv = exp2_fast(__builtin_fmaf(a[j], sl, -cp) - lzp);
-      const float qv = exp2_fast(__builtin_fmaf(b[j], sl, -cq) - lzq);
-      w[j] = fmaxf(pv - qv, 0.0f);
-    }
-  }
-  __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, float (&w)[kPer]) const {
-    float a[kPer], b[kPer];
-    load8<E, SH>(prow, i0, hi, a);
-    if (has_q) load8<E, SH>(qrow, i0, hi, b);
-    from(a, b, w);
-  }
-};
-
-template <typename E, bool SH>
-__device__ __forceinline__ Weights32<E, SH> weights32(const VerifyParams& p, const DrawState& st) {
-  Weights32<E, SH> w;
-  w.has_q = st.mode == kDrawResidual;
-  w.prow = row_view<E, SH>(p, false, st.prow);
-  w.qrow = row_view<E, SH>(p, true, w.has_q ? st.qrow : 0);
-  w.sl = st.sl;
-  w.cp = ref_of(st.mp, st.sl);
-  w.lzp = st.lzp;
-  w.cq = ref_of(st.mq, st.sl);
-  w.lzq = st.lzq;
-  return w;
-}
-
 // Float64 weights: the temperature is applied as a multiplication by the
 // float64 reciprocal of T (one extra rounding, about 1e-16 relative, where a
 // division would cost ten float64 operations per element); the normalisers
@@ -344,41 +270,6 @@ __device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W&
 }
 
 // ---------------------------------------------------------------------------
-template <typename E, bool SH>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_mass32(VerifyParams p) {
-  __shared__ float lds[kDrawThreads / kWave];
-  const int r = blockIdx.y;
-  const DrawState st = p.req[r];
-  if (st.mode == kDrawNone) return;
-  const Weights32<E, SH> w = weights32<E, SH>(p, st);
-  for (int64_t tile = blockIdx.x; tile < p.S2; tile += gridDim.x) {
-    const float m = tile_mass<float>(w, tile, p.V, lds);
-    if (threadIdx.x == 0) p.seg_w32[(int64_t)r * p.S2 + tile] = m;
-  }
-}
-
-template <typename E, bool SH>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_pick32(VerifyParams p) {
-  __shared__ PickLds<float> L;
-  const int r = blockIdx.x;
-  const DrawState st = p.req[r];
-  if (st.mode == kDrawNone) return;
-  const Weights32<E, SH> w = weights32<E, SH>(p, st);
-  PickResult res{-1, 0.0, 0.0, 0};
-  const bool force64 = (p.flags & SV_FLAG_FORCE_FP64_DRAW) != 0u;
-  if (!force64) res = pick<float>(p.seg_w32 + (int64_t)r * p.S2, p.S2, p.V, st.u, w, L);
-  if (threadIdx.x == 0) {
-    if (force64 || !res.found || !(res.margin >= (double)kDrawMargin32)) {
-      p.req[r].need64 = 1;
-      const int slot = atomicAdd(p.fb_count, 1);
-      p.fb_list[slot] = r;
-    } else {
-      p.out_tokens[(int64_t)r * (p.D + 1) + st.tau] = (int32_t)res.y;
-      if (p.diag) p.diag[r].draw_margin = (float)res.margin;
-    }
-  }
-}
-
 template <typename E, bool SH>
 __device__ __forceinline__ Weights64<E, SH> weights64(const VerifyParams& p, const DrawState& st,
                                                   bool unnormalised) {
@@ -682,9 +573,6 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
 
 template <typename E, bool SH>
 static void launch_draw_t(const VerifyParams& p, hipStream_t stream) {
-  const unsigned gx = (unsigned)(p.S2 < 1024 ? p.S2 : 1024);
-  hipLaunchKernelGGL((k_draw_mass32<E, SH>), dim3(gx, (unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
-  hipLaunchKernelGGL((k_draw_pick32<E, SH>), dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
   hipLaunchKernelGGL((k_draw_tile64<E, SH>), dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
   hipLaunchKernelGGL((k_draw_pick64<E, SH>), dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
 }

@@ -1,0 +1,94 @@
+// sv_drawrow.hpp -- the float32 weights of a draw row, shared by the
+// accept-and-draw kernel and the float64 recompute: the residual
+// max(0, p - q) after a rejection, or p for the bonus token (the standard
+// rejection-sampling rule behind the lossless verification of the
+// tradepoint.io page, "Why one universal drafter underperforms").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+#include "sv_shard.hpp"
+
+namespace sv {
+
+constexpr int kPer = 8;  // consecutive elements per thread and load group
+// A float32 draw whose CDF margin (distance of u R to the nearest boundary
+// around the drawn token) is below this is recomputed in float64.
+constexpr float kDrawMargin32 = 1e-5f;
+
+// Eight consecutive logits starting at i0 (< hi; a multiple of the 16-byte
+// vector, 8 bf16 or 4 fp32 elements); entries at or past hi read as -inf,
+// which gives them weight 0.  Each 16-byte vector is addressed through the
+// row view, so with vocabulary shards (widths a multiple of 8 elements) the
+// two fp32 vectors may lie in different shards.
+template <typename E, bool SH>
+__device__ __forceinline__ void load8(const RowView<E, SH>& row, int64_t i0, int64_t hi,
+                                      float (&x)[kPer]) {
+  if (i0 + kPer <= hi) {
+    if constexpr (E::kPerVec == 8) {
+      E::unpack(load16(row.at(i0)), x);
+    } else {
+      float a[4], b[4];
+      E::unpack(load16(row.at(i0)), a);
+      E::unpack(load16(row.at(i0 + 4)), b);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = a[j];
+        x[4 + j] = b[j];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) x[j] = (i0 + j < hi) ? E::load1(row.at(i0 + j), 0) : -INFINITY;
+  }
+}
+
+// Float32 weights of a draw row, against the row states of the accept
+// kernel: 2^((x sl - R(m)) - log2 z), as the accept ratio takes them.
+template <typename E, bool SH>
+struct Weights32 {
+  RowView<E, SH> prow, qrow;
+  bool has_q;  // false: bonus draw (w = p)
+  float sl, cp, lzp, cq, lzq;  // references R(m) and log2 sums of the rows
+  // weights of eight logits a (target) and b (draft; unused for a bonus draw)
+  __device__ __forceinline__ void from(const float (&a)[kPer], const float (&b)[kPer],
+                                       float (&w)[kPer]) const {
+    if (!has_q) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) w[j] = exp2_fast(__builtin_fmaf(a[j], sl, -cp) - lzp);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float pv = exp2_fast(__builtin_fmaf(a[j], sl, -cp) - lzp);
+      const float qv = exp2_fast(__builtin_fmaf(b[j], sl, -cq) - lzq);
+      w[j] = fmaxf(pv - qv, 0.0f);
+    }
+  }
+  __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, float (&w)[kPer]) const {
+    float a[kPer], b[kPer];
+    load8<E, SH>(prow, i0, hi, a);
+    if (has_q) load8<E, SH>(qrow, i0, hi, b);
+    from(a, b, w);
+  }
+};
+
+template <typename E, bool SH>
+__device__ __forceinline__ Weights32<E, SH> weights32(const VerifyParams& p, const DrawState& st) {
+  Weights32<E, SH> w;
+  w.has_q = st.mode == kDrawResidual;
+  w.prow = row_view<E, SH>(p, false, st.prow);
+  w.qrow = row_view<E, SH>(p, true, w.has_q ? st.qrow : 0);
+  w.sl = st.sl;
+  w.cp = ref_of(st.mp, st.sl);
+  w.lzp = st.lzp;
+  w.cq = ref_of(st.mq, st.sl);
+  w.lzq = st.lzq;
+  return w;
+}
+
+}  // namespace sv

@@ -59,8 +59,11 @@ struct VerifyParams {
   int32_t B, D;            // batch, D_max
   int64_t V, stride;       // vocabulary, row stride (elements)
   int32_t S1, seg1;        // row pass: partial-state slots per row, segment length
-  int32_t pair_slots;      // partial-state slots of a T > 0 row pair (1 or S1)
-  int32_t alpha_slots;     // partial sums of min(p, q) per row pair (1 or S1)
+  // Slices of a draw row, as the row pass leaves them: slot s of a row pair
+  // (a single row) holds the state of columns [s len, min(V, (s + 1) len)) of
+  // its target row and, for a pair, the sum of min(p, q) over them.
+  int32_t pair_ns, single_ns;    // slices per row pair / per single row
+  int64_t pair_len, single_len;  // slice length (elements)
   int32_t team, nteams;    // team row pass: members per row, teams
   int64_t team_len;        // team row pass: slice length (elements)
   int32_t S2, seg2;        // draw: tiles per row, tile length
@@ -92,6 +95,8 @@ struct VerifyParams {
   float2* part_p;    // [U][S1]  (max, sum) or (max, arg max bits) at T = 0
   float2* part_q;    // [U][S1]
   float* part_a;     // [U][S1]  partial sum min(p, q)
+  float2* pair_p;    // [U]      row state of a pair's target row (the normaliser its rates used)
+  float2* pair_q;    // [U]      row state of a pair's draft row
   DrawState* req;    // [B]
   float* seg_w32;    // [B][S2]
   double* seg_zp64;  // [B][S2]
@@ -139,7 +144,7 @@ inline void draw_geometry(int64_t V, int32_t* S2, int32_t* seg2) {
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WorkspaceLayout {
-  size_t part_p, part_q, part_a, req, seg_w32, seg_zp64, seg_zq64, seg_w64, seg_a64, seg_t64, seg_u32, seg_e64,
+  size_t part_p, part_q, part_a, pair_p, pair_q, req, seg_w32, seg_zp64, seg_zq64, seg_w64, seg_a64, seg_t64, seg_u32, seg_e64,
       fb_count, fb_list,
       plan_pairs, plan_singles, plan_counts, team_xch, shard_tab, sync_error, total;
   int32_t slots;
@@ -157,6 +162,8 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
   L.part_p = off; off += align256(U * slots * sizeof(float2));
   L.part_q = off; off += align256(U * slots * sizeof(float2));
   L.part_a = off; off += align256(U * slots * sizeof(float));
+  L.pair_p = off; off += align256(U * sizeof(float2));
+  L.pair_q = off; off += align256(U * sizeof(float2));
   L.req = off; off += align256((size_t)B * sizeof(DrawState));
   L.seg_w32 = off; off += align256((size_t)B * S2 * sizeof(float));
   L.seg_zp64 = off; off += align256((size_t)B * S2 * sizeof(double));

@@ -104,6 +104,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
     p.plan_counts[0] = carry_pairs;
     p.plan_counts[1] = carry_singles;
     *p.sync_error = 0;
+    *p.fb_count = 0;  // float64 draw queue, appended to by k_accept_draw
   }
   if (p.nshard > 1 && threadIdx.x < 2 * kMaxShards) {
     const int s = (int)threadIdx.x % kMaxShards;
@@ -255,12 +256,15 @@ __device__ void pair_item(const VerifyParams& p, const PlanItem& it, SoftmaxPart
   stream_softmax<E, true>(prow, qrow, 0, p.V, sl, sp, sq);
   sp = block_merge(sp, sl, lds_sm);
   sq = block_merge(sq, sl, lds_sm);
-  const int64_t slot = ((int64_t)r * (p.D + 1) + k) * p.S1;
+  const int64_t unit = (int64_t)r * (p.D + 1) + k;
+  const int64_t slot = unit * p.S1;
   if (threadIdx.x == 0) {
+    // the row states, and the same as the one slice state of the pair
+    p.pair_p[unit] = make_float2(sp.m, sp.z);
+    p.pair_q[unit] = make_float2(sq.m, sq.z);
     p.part_p[slot] = make_float2(sp.m, sp.z);
     p.part_q[slot] = make_float2(sq.m, sq.z);
   }
-  if (!p.alpha) return;
   float a = 0.0f;
   const bool finite = sp.m == sp.m && sq.m == sq.m && fabsf(sp.m) < INFINITY &&
                       fabsf(sq.m) < INFINITY;

@@ -163,6 +163,8 @@ struct TeamLds {
   float acc[2][kDataWaves];          // per-wave sum of min(p, q)
   float c[2][2];                     // team row values of p and q in log2:
   float lz[2][2];                    // a reference c and a small remainder lz
+  float ep[2];                       // 2^-lz of the target row
+  float rq[2];                       // 2^(lz_p - lz_q)
   int ok[2];
 };
 
@@ -227,8 +229,12 @@ __device__ __forceinline__ UnitDesc unit_at(const VerifyParams& p, int64_t j, in
   return u;
 }
 
+// Every row pair gets its sum of min(p, q) per slice (the acceptance rate
+// and, per slice, the draw's residual masses), whether or not the caller
+// asked for the rates.
 __device__ __forceinline__ bool wants_alpha(const VerifyParams& p, const UnitDesc& u) {
-  return u.kind == 1 && p.alpha != nullptr;
+  (void)p;
+  return u.kind == 1;
 }
 
 __device__ __forceinline__ int64_t unit_slot(const VerifyParams& p, const UnitDesc& u,
@@ -505,11 +511,15 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
 // Second pass of a row pair: this thread's share of sum min(p, q) with the
 // team's row values c + lz (log2 of each row's sum of 2^(x sl)), from the
 // exponentials kept by the first pass: p = ep Kp and q = eq Kq with
-// Kp = 2^((mslp - c_p) - lz_p), Kq = 2^((mslq - c_q) - lz_q) (mslp - c_p is
-// a difference of two nearby floats, exact while it matters), and
-// min(p, q) = Kp min(ep, eq Kq / Kp).  Kp <= 2^(1/2) (the thread maximum is at
-// most the row maximum, and R(m_t) at most half above m_t sl); a thread with Kp under 2^-60 holds p values that small
-// and adds nothing.  One sum per wave into LDS.
+// Kp = 2^(mslp - c_p) 2^-lz_p, Kq = 2^(mslq - c_q) 2^-lz_q, where mslp - c_p
+// and mslq - c_q are exact integers (differences of integer references) and
+// 2^-lz_p, 2^(lz_p - lz_q) are the row pair's two constants, so that
+// Kp = ldexp(2^-lz_p, mslp - c_p) and Kq / Kp = ldexp(2^(lz_p - lz_q),
+// (mslq - c_q) - (mslp - c_p)) are exact scalings of them; then
+// min(p, q) = Kp min(ep, eq Kq / Kp).  Kp <= 2^(1/2) (the thread maximum is
+// at most the row maximum, and R(m_t) at most half above m_t sl); a thread
+// whose Kp is under 2^-60 holds p values that small and adds nothing.  One
+// sum per wave into LDS.
 template <typename E, int NV>
 __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const UnitDesc& u,
                                                  const Slice& sc,
@@ -526,9 +536,9 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
   const bool ok = L.ok[b] != 0;
   float acc = 0.0f;
   if (ok) {
-    const float kp = exp2_fast((mslp - cp) - lzp), kq = exp2_fast((mslq - cq) - lzq);
-    // kp in (2^-60, 1]: the hardware reciprocal (1 ulp) instead of a division
-    const float r = kp > 0x1p-60f ? kq * __builtin_amdgcn_rcpf(kp) : 0.0f;
+    const int ip = (int)(mslp - cp), iq = (int)(mslq - cq);
+    const float kp = ip > -60 ? __builtin_ldexpf(L.ep[b], ip) : 0.0f;
+    const float r = ip > -60 ? __builtin_ldexpf(L.rq[b], iq - ip) : 0.0f;
     // chunks of G 16-byte vectors of each row
     constexpr int G = H >= 2 ? 2 : 1;
     float sum = 0.0f;
@@ -757,12 +767,12 @@ __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const Unit
     wave_merge_ref2(a, c, true, none, sl);
   }
   if (lane == 0) {
-    // Member 0 replaces its slice states with the row states, so that the
-    // accept kernel reads one slot per row of a pair.
+    // Member 0 stores the row states the team's rates were taken against
+    // (the slots keep every member's slice state, which the draw uses).
     if (member == 0) {
-      const int64_t slot = unit_slot(p, u, 0);
-      p.part_p[slot] = make_float2(a.m, a.z);
-      p.part_q[slot] = make_float2(c.m, c.z);
+      const int64_t unit = (int64_t)(u.code >> 7) * (p.D + 1) + (u.code & 127u);
+      p.pair_p[unit] = make_float2(a.m, a.z);
+      p.pair_q[unit] = make_float2(c.m, c.z);
     }
     const bool ok = a.m == a.m && c.m == c.m && fabsf(a.m) < INFINITY && fabsf(c.m) < INFINITY;
     L.ok[b] = ok;
@@ -779,6 +789,9 @@ __device__ __forceinline__ void team_wait_comm(const VerifyParams& p, const Unit
     L.c[b][1] = cq;
     L.lz[b][0] = lzp;
     L.lz[b][1] = lzq;
+    // the second pass's per-thread factors are these times exact powers of 2
+    L.ep[b] = exp2_fast(-lzp);
+    L.rq[b] = exp2_fast(lzp - lzq);
   }
 }
 

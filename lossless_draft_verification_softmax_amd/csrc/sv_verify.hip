@@ -8,13 +8,15 @@
 // L_e2e); at T = 0 the test is an arg-max match ("The MTP path").
 //
 // Pipeline (all on the caller's stream, no host synchronisation):
-//   k_plan,      row statistics and acceptance rates (sv_rowpass.hip): the
-//   k_rowpass    HBM-streaming pass.
-//   k_accept     one workgroup per request: merge the segments, Philox accept
-//                test per position, wavefront ballot + first set bit = tau,
-//                emitted drafts, alpha, the draw's normalisers.
-//   k_draw_*     inverse-CDF draw of the correction / bonus token
-//                (sv_draw.hip).
+//   k_plan          the work list (sv_rowpass.hip).
+//   k_rowteam       row statistics and acceptance rates, per slice of every
+//   (k_rowpass)     row (sv_rowteam.hip; the streaming pass in sv_rowpass.hip).
+//   k_accept_draw   one workgroup per request: the accept test per position,
+//                   wavefront ballot + first set bit = tau, emitted drafts,
+//                   alpha, and the float32 inverse-CDF draw of the correction
+//                   / bonus token from the slices' masses and one slice scan.
+//   k_draw_tile64,  float64 recompute of the draws left within the float32
+//   k_draw_pick64   error of a CDF boundary (sv_draw.hip).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -22,6 +24,7 @@
 #include "specverify.h"
 #include "sv_block.hpp"
 #include "sv_device.hpp"
+#include "sv_drawrow.hpp"
 #include "sv_internal.hpp"
 #include "sv_shard.hpp"
 
@@ -74,29 +77,59 @@ __device__ __forceinline__ ArgMax merge_row_argmax(const float2 (&v0)[kMergeChun
 __device__ __forceinline__ bool finite_f(float x) { return x == x && x != INFINITY && x != -INFINITY; }
 
 // ---------------------------------------------------------------------------
-// k_accept: one workgroup (2 wavefronts) per request.  Thread k handles
-// target row k (k <= n) and, for k < n, draft row k and the accept test.
+// k_accept_draw: one 1024-thread workgroup per request.
+//
+// Accept (threads 0..D): thread k takes target row k (k <= n) and, for
+// k < n, draft row k and the accept test; a wavefront ballot of the rejected
+// positions and its first set bit give tau; the emitted drafts, alpha and the
+// diagnostics follow.
+//
+// Draw (T > 0, the whole workgroup), float32, without a pass over the row:
+// the row pass left, for every slice s of the draw row (a team member's
+// slice, or a streaming segment), the slice's state of the target row and,
+// for a row pair, its sum alpha_s of min(p, q).  The slice's share of p is
+// P_s = z_s 2^(R(m_s) - log2 Z_p), so its residual mass is
+// max(0, P_s - alpha_s) (P_s for a bonus draw).  A wavefront scan of those
+// masses gives R and the slice holding t = u R; only that slice is then
+// read and scanned element by element.  The token is written when its CDF
+// margin is at least kDrawMargin32 (which covers the float32 errors of the
+// slice masses and of the scan); otherwise, or when rounding leaves t outside
+// the slice, the request joins the float64 queue (sv_draw.hip).
+constexpr int kAcceptDrawThreads = 1024;
+constexpr int kAcceptDrawWaves = kAcceptDrawThreads / kWave;
+constexpr int kChunk = kAcceptDrawThreads * kPer;  // elements per scan round
+
+struct AcceptDrawLds {
+  uint32_t bits;
+  int tau;
+  float margin[kWave + 1];
+  DrawState st;
+  int slice;       // crossing slice, or -1
+  float c0, t;     // cumulative mass before the slice, target u R
+  float wtot[kAcceptDrawWaves];
+  int wfirst[kAcceptDrawWaves];
+  int found;
+  int32_t y;
+  float before, at;
+};
+
 template <typename E, bool SH>
-__global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
-  using S = typename E::Storage;
-  __shared__ uint32_t s_bits;
-  __shared__ int s_tau;
-  __shared__ float s_margin[128];
+__global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams p) {
+  __shared__ AcceptDrawLds L;
   const int r = blockIdx.x;
   const int k = threadIdx.x;
+  const int lane = k & (kWave - 1), wave = k / kWave;
   const int D = p.D;
-  // Loads in two rounds: the request's scalars, thread k's token and the
-  // first chunk of its row states and alpha partials (read whatever the depth
-  // and temperature turn out to be: the slots lie inside the workspace, and
-  // those past a row's count are discarded below); then p(d) and q(d).
+  // Loads in two rounds: the request's scalars, thread k's token, its row
+  // states and alpha partials (slots past a row's count are discarded
+  // below); then p(d) and q(d).
   const int n = p.depth[r];
   const float T = p.temperature[r];
   const uint32_t rid = p.request_id ? p.request_id[r] : (uint32_t)r;
   const int64_t trow0 = p.target_row0[r];
   const int64_t drow0 = p.draft_row0 ? p.draft_row0[r] : 0;
   const int sync_err = *p.sync_error;
-  if (k == 0) s_bits = 0u;
-  if (r == 0 && k == 0) *p.fb_count = 0;  // float64 draw queue, filled by k_draw_pick32
+  if (k == 0) L.bits = 0u;
 
   // a team wait that expired is reported, not an error: the member took the
   // row normalisers from the full rows instead
@@ -108,28 +141,28 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
   const int64_t unit = (int64_t)r * (D + 1) + k;
   const bool pair = live && k < n;
   const bool greedy = T == 0.0f;
-  // slots merged per row: every slot at T = 0 and for a single row, the
-  // pair's slots for a row pair; q only for a T > 0 pair with draft logits
-  const int np_ = live ? ((greedy || !pair) ? p.S1 : p.pair_slots) : 0;
-  const int nq_ = (pair && !greedy && p.draft != nullptr) ? p.pair_slots : 0;
-  const int na_ = (k < D && k < n && !greedy && bits == 0u && p.alpha) ? p.alpha_slots : 0;
+  // A row pair at T > 0 reads the row states its rates were taken against;
+  // a single row (and every row at T = 0) merges its slot states.
+  const bool pair_state = pair && !greedy;
+  const int np_ = (live && !pair_state) ? p.S1 : 0;
+  const int na_ = (pair_state && bits == 0u) ? p.pair_ns : 0;
   const int32_t tok_k = (k < D) ? p.tokens[(int64_t)r * D + k] : 0;
-  float2 pv[kMergeChunk], qv[kMergeChunk];
+  float2 pv[kMergeChunk];
   float av[kMergeChunk];
-  {
+  float2 pp = make_float2(-INFINITY, 0.0f), pq = make_float2(-INFINITY, 0.0f);
+  if (k <= D) {
     const float2* prow_s = p.part_p + unit * p.S1;
-    const float2* qrow_s = p.part_q + unit * p.S1;
     const float* arow_s = p.part_a + unit * p.S1;
 #pragma unroll
     for (int i = 0; i < kMergeChunk; ++i) {
       pv[i] = prow_s[i];
-      qv[i] = qrow_s[i];
       av[i] = arow_s[i];
     }
+    pp = p.pair_p[unit];
+    pq = p.pair_q[unit];
 #pragma unroll
     for (int i = 0; i < kMergeChunk; ++i) {
       if (i >= np_) pv[i] = make_float2(-INFINITY, greedy ? __int_as_float(INT32_MAX) : 0.0f);
-      if (i >= nq_) qv[i] = make_float2(-INFINITY, 0.0f);
       if (i >= na_) av[i] = 0.0f;
     }
   }
@@ -140,7 +173,7 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
   }
   // p(d), q(d) for the accept test, issued before the merges
   float pd = 0.0f, qd = 0.0f;
-  if (pair && !greedy && bits == 0u && p.draft != nullptr) {
+  if (pair_state && bits == 0u && p.draft != nullptr) {
     pd = E::load1(row_view<E, SH>(p, false, trow0 + k).at(d), 0);
     qd = E::load1(row_view<E, SH>(p, true, drow0 + k).at(d), 0);
   }
@@ -157,13 +190,15 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       if (k < n) keep = (d == am.i);
     } else {
       sl = kLog2e / T;
-      sp = renormalise(merge_row(pv, p.part_p, unit, p.S1, np_, sl), sl);
+      sp = renormalise(pair_state ? SoftmaxPart{pp.x, pp.y}
+                                  : merge_row(pv, p.part_p, unit, p.S1, np_, sl),
+                       sl);
       if (!finite_f(sp.m)) bits |= SV_BIT_BAD_ROW;
       if (k < n) {
         if (p.draft == nullptr) {
           bits |= SV_BIT_BAD_ROW;
         } else {
-          sq = renormalise(merge_row(qv, p.part_q, unit, p.S1, nq_, sl), sl);
+          sq = renormalise(SoftmaxPart{pq.x, pq.y}, sl);
           if (!finite_f(sq.m)) bits |= SV_BIT_BAD_ROW;
         }
       }
@@ -180,10 +215,10 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       }
     }
   }
-  __syncthreads();  // s_bits cleared
-  if (bits) atomicOr(&s_bits, bits);
+  __syncthreads();  // L.bits cleared
+  if (bits) atomicOr(&L.bits, bits);
   __syncthreads();
-  const uint32_t all_bits = s_bits;
+  const uint32_t all_bits = L.bits;
 
   if (all_bits != 0u) {  // nothing emitted for an invalid request
     if (k <= D) p.out_tokens[(int64_t)r * (D + 1) + k] = -1;
@@ -197,14 +232,14 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
     return;
   }
 
-  // First rejection: ballot of rejected positions in wavefront 0 (k < n <= 64).
+  // First rejection: ballot of rejected positions in wavefront 0 (n <= 64).
   if (k < kWave) {
     const uint64_t rejected = __ballot(k < n && !keep);
-    if (k == 0) s_tau = rejected ? (int)__builtin_ctzll(rejected) : n;
+    if (k == 0) L.tau = rejected ? (int)__builtin_ctzll(rejected) : n;
   }
-  s_margin[k] = (k < n) ? margin : INFINITY;
+  if (k <= kWave) L.margin[k] = (k < n) ? margin : INFINITY;
   __syncthreads();
-  const int tau = s_tau;
+  const int tau = L.tau;
 
   if (k <= D) {
     int32_t tok = -1;
@@ -221,10 +256,10 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
 #pragma unroll
         for (int i = 0; i < kMergeChunk; ++i) a += av[i];
         const float* pa = p.part_a + unit * p.S1;
-        for (int j0 = kMergeChunk; j0 < p.alpha_slots; j0 += kMergeChunk) {
+        for (int j0 = kMergeChunk; j0 < p.pair_ns; j0 += kMergeChunk) {
           float v[kMergeChunk];
 #pragma unroll
-          for (int i = 0; i < kMergeChunk; ++i) v[i] = (j0 + i < p.alpha_slots) ? pa[j0 + i] : 0.0f;
+          for (int i = 0; i < kMergeChunk; ++i) v[i] = (j0 + i < p.pair_ns) ? pa[j0 + i] : 0.0f;
 #pragma unroll
           for (int i = 0; i < kMergeChunk; ++i) a += v[i];
         }
@@ -255,14 +290,143 @@ __global__ __launch_bounds__(128) void k_accept(VerifyParams p) {
       st.u = u24(w.w[1]);
     }
     p.req[r] = st;
+    L.st = st;
   }
   if (k == 0) {
     p.accepted_len[r] = tau;
     p.num_out[r] = tau + 1;
     if (p.diag) {
       float mm = INFINITY;
-      for (int j = 0; j <= tau && j < n; ++j) mm = fminf(mm, s_margin[j]);
+      for (int j = 0; j <= tau && j < n; ++j) mm = fminf(mm, L.margin[j]);
       p.diag[r] = sv_diag{mm, INFINITY, info, 0};
+    }
+  }
+  __syncthreads();
+  const DrawState st = L.st;
+  if (st.mode == kDrawNone) return;  // workgroup-uniform
+
+  // ---- draw: locate the slice holding t = u R (wavefront 0) ----
+  const bool residual = st.mode == kDrawResidual;
+  const int ns = residual ? p.pair_ns : p.single_ns;
+  const int64_t slen = residual ? p.pair_len : p.single_len;
+  const bool force64 = (p.flags & SV_FLAG_FORCE_FP64_DRAW) != 0u;
+  const float cp = ref_of(st.mp, st.sl);
+  if (wave == 0) {
+    const int64_t dunit = (int64_t)r * (D + 1) + st.tau;
+    float w = 0.0f;
+    if (lane < ns) {
+      const float2 ms = p.part_p[dunit * p.S1 + lane];
+      const float a = residual ? p.part_a[dunit * p.S1 + lane] : 0.0f;
+      const float ps = (ms.x == -INFINITY)
+                           ? 0.0f
+                           : ms.y * exp2_fast((ref_of(ms.x, st.sl) - cp) - st.lzp);
+      w = residual ? fmaxf(ps - a, 0.0f) : ps;
+    }
+    // inclusive scan over the slices (fixed order)
+    float c = w;
+#pragma unroll
+    for (int dd = 1; dd < kWave; dd <<= 1) {
+      const float o = __shfl_up(c, dd);
+      if (lane >= dd) c += o;
+    }
+    const float R = __shfl(c, ns - 1);
+    const float t = st.u * R;
+    const uint64_t cross = __ballot(lane < ns && w > 0.0f && c > t);
+    const int j = cross ? (int)__builtin_ctzll(cross) : -1;
+    const float before = __shfl_up(c, 1);
+    if (lane == 0) {
+      L.slice = force64 ? -1 : j;
+      L.t = t;
+      L.found = 0;
+    }
+    if (j >= 0 && lane == j) L.c0 = (j == 0) ? 0.0f : before;
+  }
+  __syncthreads();
+  const int j = L.slice;
+  bool found = false;
+  if (j >= 0) {
+    // ---- scan inside slice j, kChunk elements per round ----
+    Weights32<E, SH> wt = weights32<E, SH>(p, st);
+    const float t = L.t;
+    float carry = L.c0;
+    const int64_t lo = (int64_t)j * slen;
+    const int64_t hi = min(p.V, lo + slen);
+    for (int64_t base = lo; base < hi; base += kChunk) {
+      const int64_t i0 = base + (int64_t)k * kPer;
+      float w[kPer];
+      if (i0 < hi) {
+        wt(i0, hi, w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) w[e] = 0.0f;
+      }
+      float run = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) run += w[e];
+      // block exclusive scan of the thread sums (wavefront scans, wave
+      // totals in order)
+      float incl = run;
+#pragma unroll
+      for (int dd = 1; dd < kWave; dd <<= 1) {
+        const float o = __shfl_up(incl, dd);
+        if (lane >= dd) incl += o;
+      }
+      if (lane == kWave - 1) L.wtot[wave] = incl;
+      __syncthreads();
+      float wbase = 0.0f, total = 0.0f;
+      for (int v = 0; v < kAcceptDrawWaves; ++v) {
+        const float x = L.wtot[v];
+        if (v < wave) wbase += x;
+        total += x;
+      }
+      const float excl = carry + (wbase + (incl - run));
+      // the first element of this thread whose cumulative mass passes t
+      float cum = excl;
+      int first = -1;
+      float bprev = 0.0f, bat = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const float prev = cum;
+        cum += w[e];
+        if (first < 0 && w[e] > 0.0f && cum > t) {
+          first = e;
+          bprev = prev;
+          bat = cum;
+        }
+      }
+      const uint64_t hit = __ballot(first >= 0);
+      if (lane == 0) L.wfirst[wave] = hit ? (int)__builtin_ctzll(hit) : -1;
+      __syncthreads();
+      int winner = -1;
+      for (int v = 0; v < kAcceptDrawWaves; ++v)
+        if (L.wfirst[v] >= 0) {
+          winner = v * kWave + L.wfirst[v];
+          break;
+        }
+      if (winner >= 0) {
+        if (k == winner) {
+          L.y = (int32_t)(i0 + first);
+          L.before = bprev;
+          L.at = bat;
+        }
+        __syncthreads();
+        found = true;
+        break;
+      }
+      carry += total;
+      __syncthreads();  // wtot / wfirst reused by the next round
+    }
+  }
+  if (k == 0) {
+    float m = 0.0f;
+    if (found) m = fminf(L.t - L.before, L.at - L.t);
+    if (found && m >= kDrawMargin32) {
+      p.out_tokens[(int64_t)r * (D + 1) + st.tau] = L.y;
+      if (p.diag) p.diag[r].draw_margin = m;
+    } else {
+      p.req[r].need64 = 1;
+      const int slot = atomicAdd(p.fb_count, 1);
+      p.fb_list[slot] = r;
     }
   }
 }
@@ -286,17 +450,20 @@ static hipError_t launch_all(VerifyParams& p, int grid, hipStream_t stream) {
   if (sharded && !team) return hipErrorInvalidValue;
   if (team) {
     p.S1 = T;
-    // with acceptance rates the team pass stores a pair's row states in slot 0
-    p.pair_slots = p.alpha ? 1 : T;
-    p.alpha_slots = T;
     p.team = T;
     p.nteams = grid / T;
     p.team_len = slice;
+    // every row is cut into the team's slices
+    p.pair_ns = p.single_ns = T;
+    p.pair_len = p.single_len = slice;
   } else {
-    p.pair_slots = 1;
-    p.alpha_slots = 1;
     p.team = 0;
     p.nteams = 0;
+    // a row pair is one slice; single rows are cut into S1 segments
+    p.pair_ns = 1;
+    p.pair_len = p.V;
+    p.single_ns = p.S1;
+    p.single_len = p.seg1;
   }
   mark(p, 0, stream);
   launch_plan(p, stream);
@@ -308,16 +475,22 @@ static hipError_t launch_all(VerifyParams& p, int grid, hipStream_t stream) {
     (void)hipGetLastError();
     if (team) {  // fall back: streaming pass with its own slot layout
       stats_geometry(p.B, p.D, p.V, &p.S1, &p.seg1);
-      p.pair_slots = 1;
-      p.alpha_slots = 1;
+      p.team = 0;
+      p.nteams = 0;
+      p.pair_ns = 1;
+      p.pair_len = p.V;
+      p.single_ns = p.S1;
+      p.single_len = p.seg1;
     }
     launch_rowpass(p, grid, stream);
   }
   mark(p, 2, stream);
   if (sharded)
-    hipLaunchKernelGGL((k_accept<E, true>), dim3((unsigned)p.B), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((k_accept_draw<E, true>), dim3((unsigned)p.B), dim3(kAcceptDrawThreads), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((k_accept<E, false>), dim3((unsigned)p.B), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((k_accept_draw<E, false>), dim3((unsigned)p.B), dim3(kAcceptDrawThreads), 0,
+                       stream, p);
   mark(p, 3, stream);
   launch_draw(p, stream);
   mark(p, 4, stream);
