@@ -165,8 +165,6 @@ sv_status run_verify(const sv_verify_args* a, int32_t nshard, int64_t shard_w,
   p.part_a = reinterpret_cast<float*>(ws + L.part_a);
   p.pair_p = reinterpret_cast<float2*>(ws + L.pair_p);
   p.pair_q = reinterpret_cast<float2*>(ws + L.pair_q);
-  p.req = reinterpret_cast<sv::DrawState*>(ws + L.req);
-  p.seg_w32 = reinterpret_cast<float*>(ws + L.seg_w32);
   p.seg_zp64 = reinterpret_cast<double*>(ws + L.seg_zp64);
   p.seg_zq64 = reinterpret_cast<double*>(ws + L.seg_zq64);
   p.seg_w64 = reinterpret_cast<double*>(ws + L.seg_w64);
@@ -174,8 +172,10 @@ sv_status run_verify(const sv_verify_args* a, int32_t nshard, int64_t shard_w,
   p.seg_t64 = reinterpret_cast<double*>(ws + L.seg_t64);
   p.seg_u32 = reinterpret_cast<int32_t*>(ws + L.seg_u32);
   p.seg_e64 = reinterpret_cast<double*>(ws + L.seg_e64);
+  p.seg_h64 = reinterpret_cast<double*>(ws + L.seg_h64);
   p.fb_count = reinterpret_cast<int32_t*>(ws + L.fb_count);
-  p.fb_list = reinterpret_cast<int32_t*>(ws + L.fb_list);
+  p.fb_jobs = reinterpret_cast<sv::DrawJob*>(ws + L.fb_jobs);
+  p.fb_done = reinterpret_cast<int32_t*>(ws + L.fb_done);
   p.plan_pairs = reinterpret_cast<sv::PlanItem*>(ws + L.plan_pairs);
   p.plan_singles = reinterpret_cast<sv::PlanItem*>(ws + L.plan_singles);
   p.plan_counts = reinterpret_cast<int32_t*>(ws + L.plan_counts);

@@ -6,16 +6,12 @@
 // tradepoint.io page, "Why one universal drafter underperforms").
 //
 // The row is cut into tiles of 2048 elements (one 16-byte load of bf16 per
-// thread of a 256-thread workgroup).  A tile's mass is the last value of a
-// fixed-order block scan of its weights, so the pass that finds the crossing
-// tile and the pass that scans inside it agree bit for bit.
-//   k_draw_tile64   one float64 pass over the rows of queued requests: tile
+// thread of a 256-thread workgroup).
+//   k_draw_tile64   one float64 pass over the (queued draw, tile) items: tile
 //                   normaliser partials and the one-pass split of the tile
 //                   residual masses
-//   k_draw_pick64   float64 tile masses (from the split, or directly where
-//                   it is not certain), then the float64 pick
-// The float64 kernels walk the queue on a fixed grid, so an empty queue costs
-// one short dispatch each.
+//   k_draw_pick64   one workgroup per queued draw: tile masses from the
+//                   partials, the crossing tile and the scan inside it
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -24,6 +20,7 @@
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
 #include "sv_drawrow.hpp"
+#include "sv_exp64.hpp"
 #include "sv_shard.hpp"
 
 namespace sv {
@@ -73,131 +70,122 @@ __device__ __forceinline__ T shfl_up1(T v) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ T block_sum256(T v, T* lds) {
-  for (int m = 1; m < kWave; m <<= 1) {
-    if constexpr (sizeof(T) == 8) v += shfl_xor_d(v, m);
-    else v += __shfl_xor(v, m);
-  }
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  if (lane == 0) lds[wave] = v;
-  __syncthreads();
-  T t = T(0);
-  for (int w = 0; w < kDrawThreads / kWave; ++w) t = t + lds[w];
-  __syncthreads();
-  return t;
-}
-
 // ---------------------------------------------------------------------------
 // Float64 weights: the temperature is applied as a multiplication by the
 // float64 reciprocal of T (one extra rounding, about 1e-16 relative, where a
-// division would cost ten float64 operations per element); the normalisers
-// are float64 sums of exp((x - max) / T).
+// division would cost ten float64 operations per element); an element's
+// unnormalised exponentials are ep = exp((a - mp) / T), eq = exp((b - mq) / T)
+// and its weight max(0, ep / Zp - eq / Zq) (residual draw) or ep / Zp (bonus
+// draw), with the float64 normalisers Zp = sum ep, Zq = sum eq applied as
+// reciprocals.  Every path that weighs an element (the kept near-ties, the
+// float32 draw's tile, a directly recomputed tile) uses this one formula.
 template <typename E, bool SH>
 struct Weights64 {
   RowView<E, SH> prow, qrow;
-  bool has_q;
-  double invT, mp, mq, lnzp, lnzq;
-  bool unnormalised;  // w = exp((x - mp) / T): residual mass was zero
-  __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, double (&w)[kPer]) const {
-    float a[kPer];
-    load8<E, SH>(prow, i0, hi, a);
-    if (unnormalised || !has_q) {
-      const double off = unnormalised ? 0.0 : lnzp;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) w[j] = exp(((double)a[j] - mp) * invT - off);
-      return;
-    }
-    float b[kPer];
-    load8<E, SH>(qrow, i0, hi, b);
+  bool has_q;         // residual draw: w = max(0, p - q); else w = p
+  double invT, mp, mq;
+  double izp, izq;    // 1 / Zp, 1 / Zq (izp = 1: the unnormalised p of a zero residual)
+  const double* tab;  // 2^(j/64) table of exp64_tab (LDS)
+  // weights from the unnormalised exponentials
+  __device__ __forceinline__ double weight(double ep, double eq) const {
+    if (!has_q) return ep * izp;
+    const double pv = ep * izp, qv = eq * izq;
+    return pv > qv ? pv - qv : 0.0;
+  }
+  // weights of eight logits a (target) and b (draft; read only if has_q)
+  __device__ __forceinline__ void from(const float (&a)[kPer], const float (&b)[kPer],
+                                       double (&w)[kPer]) const {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const double pv = exp(((double)a[j] - mp) * invT - lnzp);
-      const double qv = exp(((double)b[j] - mq) * invT - lnzq);
-      w[j] = pv > qv ? pv - qv : 0.0;
+      const double ep = exp64_tab(((double)a[j] - mp) * invT, tab);
+      const double eq = has_q ? exp64_tab(((double)b[j] - mq) * invT, tab) : 0.0;
+      w[j] = weight(ep, eq);
     }
+  }
+  __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, double (&w)[kPer]) const {
+    float a[kPer], b[kPer];
+    load8_pair<E, SH>(prow, qrow, has_q, i0, hi, a, b);
+    from(a, b, w);
   }
 };
 
-template <typename T>
-__device__ __forceinline__ T sum8(const T (&w)[kPer]) {
-  T s = w[0];
+template <typename E, bool SH>
+__device__ __forceinline__ Weights64<E, SH> weights64(const VerifyParams& p, const DrawJob& jb,
+                                                      bool unnormalised, double izp, double izq,
+                                                      const double* tab) {
+  Weights64<E, SH> w;
+  w.has_q = jb.mode == kDrawResidual && !unnormalised;
+  w.prow = row_view<E, SH>(p, false, jb.prow);
+  w.qrow = row_view<E, SH>(p, true, w.has_q ? jb.qrow : 0);
+  w.invT = jb.invT;
+  w.mp = jb.mp;
+  w.mq = jb.mq;
+  w.izp = unnormalised ? 1.0 : izp;
+  w.izq = izq;
+  w.tab = tab;
+  return w;
+}
+
+__device__ __forceinline__ double sum8(const double (&w)[kPer]) {
+  double s = w[0];
 #pragma unroll
   for (int j = 1; j < kPer; ++j) s = s + w[j];
   return s;
 }
 
-// Mass of tile `tile` of a row: the block-scan total of the thread sums.
-template <typename T, typename W>
-__device__ __forceinline__ T tile_mass(const W& weights, int64_t tile, int64_t V, T* lds) {
-  const int64_t lo = tile * kDrawTile;
-  const int64_t hi = min(V, lo + (int64_t)kDrawTile);
-  T w[kPer];
-  weights(lo + (int64_t)threadIdx.x * kPer, hi, w);
-  T tot;
-  scan256<T>(sum8(w), lds, &tot);
-  return tot;
-}
-
-struct PickResult {
-  int64_t y;
-  double margin;
-  double R;  // total of the tile masses
-  int found;
-};
-
-template <typename T>
 struct PickLds {
-  T scan[kDrawThreads / kWave];
-  T last[kDrawThreads / kWave];
+  double scan[kDrawThreads / kWave];
+  double last[kDrawThreads / kWave];
   int wave_first[kDrawThreads / kWave];
   int64_t y;
   double margin;
   int found;
   int tile;
-  T c0, t;
+  double c0;
 };
 
-// The draw given per-tile masses: scan the masses (rounds of 256 tiles, carry
-// in order) for the total R and the crossing tile, then scan inside it.  The
-// first y with C(y) > t = u * R wins; margin = min(t - C(y-1), C(y) - t).
-// When the tiles fit one round (S2 <= 256) the one scan gives both the total
+// The crossing tile of a draw given the per-tile masses: one scan of the
+// masses (rounds of 256 tiles, carry in order) for the total R, and
+// t = u R; the crossing tile is the first tile of non-zero mass whose
+// inclusive cumulative mass exceeds t.  tile = -1 when t is at or past the
+// total (rounding).  With at most 256 tiles the one scan gives both the total
 // and every tile's inclusive value.
-template <typename T, typename W>
-__device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W& weights,
-                           PickLds<T>& L) {
+struct TileFind {
+  int tile;
+  double c0;  // cumulative mass before the tile
+  double t;
+  double R;
+};
+
+__device__ TileFind find_tile(const double* masses, int64_t S2, double u, PickLds& L) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  if (tid == 0) {
-    L.found = 0;
-    L.tile = -1;
-  }
-  T carry = T(0);
-  T m1 = T(0), incl1 = T(0);  // this thread's tile (single round)
+  if (tid == 0) L.tile = -1;
+  double carry = 0.0;
+  double m1 = 0.0, incl1 = 0.0;  // this thread's tile (single round)
   for (int64_t base = 0; base < S2; base += kDrawThreads) {
-    const T m = (base + tid < S2) ? masses[base + tid] : T(0);
-    T tot;
-    const T incl = scan256<T>(m, L.scan, &tot);
+    const double m = (base + tid < S2) ? masses[base + tid] : 0.0;
+    double tot;
+    const double incl = scan256<double>(m, L.scan, &tot);
     m1 = m;
     incl1 = incl;
     carry = carry + tot;
   }
-  const T R = carry;
-  const T t = u * R;
-  // crossing tile: the first tile whose inclusive cumulative mass exceeds t
-  carry = T(0);
+  const double R = carry;
+  const double t = u * R;
+  carry = 0.0;
   for (int64_t base = 0; base < S2; base += kDrawThreads) {
-    T m = m1, incl = incl1, tot = R;
+    double m = m1, incl = incl1, tot = R;
     if (S2 > kDrawThreads) {
-      m = (base + tid < S2) ? masses[base + tid] : T(0);
-      incl = carry + scan256<T>(m, L.scan, &tot);
+      m = (base + tid < S2) ? masses[base + tid] : 0.0;
+      incl = carry + scan256<double>(m, L.scan, &tot);
     }
-    T excl = shfl_up1(incl);
+    double excl = shfl_up1(incl);
     // exclusive value across wave boundaries: previous thread's inclusive
     if (lane == kWave - 1) L.last[tid / kWave] = incl;
     __syncthreads();
     if (lane == 0) excl = (tid == 0) ? carry : L.last[tid / kWave - 1];
-    const bool cross = (base + tid < S2) && m > T(0) && incl > t;
+    const bool cross = (base + tid < S2) && m > 0.0 && incl > t;
     const uint64_t mask = __ballot(cross);
     if (lane == 0) L.wave_first[tid / kWave] = mask ? (int)__builtin_ctzll(mask) : -1;
     __syncthreads();
@@ -218,30 +206,40 @@ __device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W&
     carry = carry + tot;
     __syncthreads();
   }
-  PickResult res{-1, 0.0, (double)R, 0};
-  const int tile = L.tile;
-  if (tile < 0) return res;  // t at or past the total: undecided
-  const T c0 = L.c0;
-  const int64_t lo = (int64_t)tile * kDrawTile;
-  const int64_t hi = min(V, lo + (int64_t)kDrawTile);
-  T w[kPer];
-  const int64_t i0 = lo + (int64_t)tid * kPer;
-  weights(i0, hi, w);
-  T tot;
-  const T incl = scan256<T>(sum8(w), L.scan, &tot);
-  T excl = shfl_up1(incl);
+  TileFind f{L.tile, L.c0, t, R};
+  __syncthreads();  // L reused by the caller
+  return f;
+}
+
+// Inside the crossing tile: a block scan of the weights (thread i holding
+// elements i0 .. i0 + 7) from c0; the first y with C(y) > t wins, with
+// margin = min(t - C(y-1), C(y) - t).
+struct InTile {
+  int found;
+  int64_t y;
+  double margin;
+};
+
+__device__ InTile scan_in_tile(const double (&w)[kPer], int64_t i0, double c0, double t,
+                               PickLds& L) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  if (tid == 0) L.found = 0;
+  double tot;
+  const double incl = scan256<double>(sum8(w), L.scan, &tot);
+  double excl = shfl_up1(incl);
   if (lane == kWave - 1) L.last[tid / kWave] = incl;
   __syncthreads();
-  if (lane == 0) excl = (tid == 0) ? T(0) : L.last[tid / kWave - 1];
-  T run = excl;
+  if (lane == 0) excl = (tid == 0) ? 0.0 : L.last[tid / kWave - 1];
+  double run = excl;
   int first = -1;
-  T before = T(0), at = T(0);
+  double before = 0.0, at = 0.0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const T prev = c0 + run;
+    const double prev = c0 + run;
     run = run + w[j];
-    const T cur = c0 + run;
-    if (first < 0 && w[j] > T(0) && cur > t) {
+    const double cur = c0 + run;
+    if (first < 0 && w[j] > 0.0 && cur > t) {
       first = j;
       before = prev;
       at = cur;
@@ -259,33 +257,16 @@ __device__ PickResult pick(const T* masses, int64_t S2, int64_t V, T u, const W&
   if (winner >= 0 && tid == winner) {
     L.found = 1;
     L.y = i0 + first;
-    const T a = t - before, b = at - t;
-    L.margin = (double)(a < b ? a : b);
+    const double a = t - before, b = at - t;
+    L.margin = a < b ? a : b;
   }
   __syncthreads();
-  res.found = L.found;
-  res.y = L.y;
-  res.margin = L.margin;
-  return res;
+  InTile r{L.found, L.y, L.margin};
+  __syncthreads();
+  return r;
 }
 
 // ---------------------------------------------------------------------------
-template <typename E, bool SH>
-__device__ __forceinline__ Weights64<E, SH> weights64(const VerifyParams& p, const DrawState& st,
-                                                  bool unnormalised) {
-  Weights64<E, SH> w;
-  w.has_q = st.mode == kDrawResidual && !unnormalised;
-  w.prow = row_view<E, SH>(p, false, st.prow);
-  w.qrow = row_view<E, SH>(p, true, w.has_q ? st.qrow : 0);
-  w.invT = 1.0 / (double)st.T;
-  w.mp = st.mp;
-  w.mq = st.mq;
-  w.lnzp = 0.0;
-  w.lnzq = 0.0;
-  w.unnormalised = unnormalised;
-  return w;
-}
-
 // Float64 pass over one tile of a queued draw row: the normaliser partials
 // sum exp((x - max) / T) of p and q, and the one-pass split of the residual
 // mass.  With rho = Zq / Zp, an element's residual weight is
@@ -304,217 +285,239 @@ __device__ __forceinline__ Weights64<E, SH> weights64(const VerifyParams& p, con
 // recomputed directly.
 constexpr double kTau64 = 1e-4;
 
-// log2(Zq / Zp) from the float32 row states, with Z = sum 2^((x - m) sl): each
-// log2 sum lz is taken against the integer reference R(m), so each adds its
-// offset R(m) - m sl (exact in float64, as the product of two floats is).
-__device__ __forceinline__ double log2_ratio_exact(const DrawState& st) {
-  const double op = (double)ref_of(st.mp, st.sl) - (double)st.mp * (double)st.sl;
-  const double oq = (double)ref_of(st.mq, st.sl) - (double)st.mq * (double)st.sl;
-  return ((double)st.lzq + oq) - ((double)st.lzp + op);
+struct Draw64Lds {
+  double tab[kExp64Table];  // 2^(j/64) for exp64_tab
+  double red[kDrawThreads / kWave][5];
+  int32_t redu[kDrawThreads / kWave];
+  double z2[kDrawThreads / kWave][2];
+  double mass[kDrawThreads];  // tile masses of a row of at most 256 tiles
+  int redo[kDrawThreads];
+  PickLds pk;
+  unsigned long long last1;
+};
+
+// The exponential table into LDS (read by every exp64_tab of the kernel).
+__device__ __forceinline__ void load_exp_table(Draw64Lds& L) {
+  if (threadIdx.x < kExp64Table) L.tab[threadIdx.x] = kExp2Frac[threadIdx.x];
+  __syncthreads();
+}
+
+// Exponentials of the float32 draw's tile, kept by the tile pass for the pick:
+// [entry][row][element j of a thread][thread].
+__device__ __forceinline__ double* hint_exps(const VerifyParams& p, int slot, int row) {
+  return p.seg_h64 + ((int64_t)slot * 2 + row) * kDrawTile;
 }
 
 template <typename E, bool SH>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
-  __shared__ double lds[kDrawThreads / kWave][5];
-  __shared__ int32_t ldsu[kDrawThreads / kWave];
+__device__ __forceinline__ void tile_pass(const VerifyParams& p, const DrawJob& jb, int slot,
+                                          int64_t tile, Draw64Lds& L) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int64_t items = (int64_t)(*p.fb_count) * p.S2;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int r = p.fb_list[it / p.S2];
-    const int64_t tile = it % p.S2;
-    const DrawState st = p.req[r];
-    const bool residual = st.mode == kDrawResidual;
-    const double invT = 1.0 / (double)st.T;
-    const double rho_e = residual ? exp2(log2_ratio_exact(st)) : 0.0;
-    const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
-    const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
-    float a[kPer], b[kPer];
-    load8<E, SH>(row_view<E, SH>(p, false, st.prow), i0, hi, a);
-    if (residual) load8<E, SH>(row_view<E, SH>(p, true, st.qrow), i0, hi, b);
-    double zp = 0.0, zq = 0.0, D = 0.0, A = 0.0, S = 0.0;
-    uint32_t kmask = 0u;  // elements kept for the pick (their ep, eq recomputed below)
+  const int64_t o = (int64_t)slot * p.S2 + tile;
+  const bool residual = jb.mode == kDrawResidual;
+  const bool hinted = jb.y32 >= 0 && (int64_t)jb.y32 / kDrawTile == tile;
+  const double invT = jb.invT, rho_e = jb.rho_e;
+  const double mp = jb.mp, mq = jb.mq;
+  const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
+  const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
+  float a[kPer], b[kPer];
+  load8_pair<E, SH>(row_view<E, SH>(p, false, jb.prow), row_view<E, SH>(p, true, jb.qrow),
+                    residual, i0, hi, a, b);
+  double* hp = hint_exps(p, slot, 0) + threadIdx.x;
+  double* hq = hint_exps(p, slot, 1) + threadIdx.x;
+  double zp = 0.0, zq = 0.0, D = 0.0, A = 0.0, S = 0.0;
+  uint32_t kmask = 0u;  // elements kept for the pick (their ep, eq recomputed below)
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const double ep = exp64_tab(((double)a[j] - mp) * invT, L.tab);
+    zp += ep;
+    if (hinted) hp[j * kDrawThreads] = ep;
+    if (residual) {
+      const double eq = exp64_tab(((double)b[j] - mq) * invT, L.tab);
+      zq += eq;
+      if (hinted) hq[j * kDrawThreads] = eq;
+      const double d = fma(ep, rho_e, -eq);
+      const double tol = kTau64 * ep * rho_e;
+      if (a[j] == b[j]) {
+        S += ep;
+      } else if (d > tol) {
+        D += d;
+        A += ep;
+      } else if (d >= -tol && (ep > 0.0 || eq > 0.0)) {
+        kmask |= 1u << j;
+      }
+    }
+  }
+  // kept elements: positions by an exclusive scan of the counts in thread
+  // order, so the list is in element order
+  const int32_t U = __builtin_popcount(kmask);
+  int32_t incl = U;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t x = __shfl_up(incl, d);
+    if (lane >= d) incl += x;
+  }
+  if (lane == kWave - 1) L.redu[wave] = incl;
+  __syncthreads();
+  int32_t base = 0, total = 0;
+  for (int w = 0; w < kDrawThreads / kWave; ++w) {
+    if (w < wave) base += L.redu[w];
+    total += L.redu[w];
+  }
+  base += incl - U;
+  if (total <= kDrawKeep64 && kmask != 0u) {
+    double* keep = p.seg_e64 + o * (kDrawKeep64 * 2);
+    int32_t pos = base;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const double ep = exp(((double)a[j] - (double)st.mp) * invT);
-      zp += ep;
-      if (residual) {
-        const double eq = exp(((double)b[j] - (double)st.mq) * invT);
-        zq += eq;
-        const double d = fma(ep, rho_e, -eq);
-        const double tol = kTau64 * ep * rho_e;
-        if (a[j] == b[j]) {
-          S += ep;
-        } else if (d > tol) {
-          D += d;
-          A += ep;
-        } else if (d >= -tol && (ep > 0.0 || eq > 0.0)) {
-          kmask |= 1u << j;
-        }
+      if ((kmask >> j) & 1u) {
+        keep[2 * pos] = exp64_tab(((double)a[j] - mp) * invT, L.tab);
+        keep[2 * pos + 1] = exp64_tab(((double)b[j] - mq) * invT, L.tab);
+        ++pos;
       }
     }
-    // kept elements: positions by an exclusive scan of the counts in thread
-    // order, so the list is in element order
-    const int32_t U = __builtin_popcount(kmask);
-    int32_t incl = U;
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int32_t o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    if (lane == kWave - 1) ldsu[wave] = incl;
-    __syncthreads();
-    int32_t base = 0, total = 0;
-    for (int w = 0; w < kDrawThreads / kWave; ++w) {
-      if (w < wave) base += ldsu[w];
-      total += ldsu[w];
-    }
-    base += incl - U;
-    const int64_t o = (int64_t)r * p.S2 + tile;
-    if (total <= kDrawKeep64 && kmask != 0u) {
-      double* keep = p.seg_e64 + o * (kDrawKeep64 * 2);
-      int32_t pos = base;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if ((kmask >> j) & 1u) {
-          keep[2 * pos] = exp(((double)a[j] - (double)st.mp) * invT);
-          keep[2 * pos + 1] = exp(((double)b[j] - (double)st.mq) * invT);
-          ++pos;
-        }
-      }
-    }
-    // block sums in a fixed order
-    for (int m = 1; m < kWave; m <<= 1) {
-      zp += shfl_xor_d(zp, m);
-      zq += shfl_xor_d(zq, m);
-      D += shfl_xor_d(D, m);
-      A += shfl_xor_d(A, m);
-      S += shfl_xor_d(S, m);
-    }
-    __syncthreads();
-    if (lane == 0) {
-      lds[wave][0] = zp;
-      lds[wave][1] = zq;
-      lds[wave][2] = D;
-      lds[wave][3] = A;
-      lds[wave][4] = S;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double t[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-      for (int w = 0; w < kDrawThreads / kWave; ++w)
-        for (int k = 0; k < 5; ++k) t[k] += lds[w][k];
-      p.seg_zp64[o] = t[0];
-      p.seg_zq64[o] = t[1];
-      p.seg_w64[o] = t[2];
-      p.seg_a64[o] = t[3];
-      p.seg_t64[o] = t[4];
-      p.seg_u32[o] = total;
-    }
-    __syncthreads();
+  }
+  // block sums in a fixed order
+  for (int m = 1; m < kWave; m <<= 1) {
+    zp += shfl_xor_d(zp, m);
+    zq += shfl_xor_d(zq, m);
+    D += shfl_xor_d(D, m);
+    A += shfl_xor_d(A, m);
+    S += shfl_xor_d(S, m);
+  }
+  if (lane == 0) {
+    L.red[wave][0] = zp;
+    L.red[wave][1] = zq;
+    L.red[wave][2] = D;
+    L.red[wave][3] = A;
+    L.red[wave][4] = S;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int w = 0; w < kDrawThreads / kWave; ++w)
+      for (int k = 0; k < 5; ++k) t[k] += L.red[w][k];
+    p.seg_zp64[o] = t[0];
+    p.seg_zq64[o] = t[1];
+    p.seg_w64[o] = t[2];
+    p.seg_a64[o] = t[3];
+    p.seg_t64[o] = t[4];
+    p.seg_u32[o] = total;
   }
 }
 
-// Full-row float64 normalisers of both rows from the tile partials (the same
-// fixed-order tree for each), in one block reduction.
-__device__ __forceinline__ void merge_z64(const double* pp, const double* pq, int64_t S2,
-                                          double (*lds)[2], double& zp, double& zq) {
-  double a = 0.0, b = 0.0;
-  for (int64_t j = threadIdx.x; j < S2; j += kDrawThreads) {
-    a += pp[j];
-    if (pq) b += pq[j];
+// Mass of tile `tile` of a row, recomputed directly: the block total of the
+// thread sums of its float64 weights.
+template <typename W>
+__device__ __forceinline__ double tile_mass(const W& weights, int64_t tile, int64_t V,
+                                            double* lds) {
+  const int64_t lo = tile * kDrawTile;
+  const int64_t hi = min(V, lo + (int64_t)kDrawTile);
+  double w[kPer];
+  weights(lo + (int64_t)threadIdx.x * kPer, hi, w);
+  double tot;
+  scan256<double>(sum8(w), lds, &tot);
+  return tot;
+}
+
+// The float64 draw of queue entry `slot`: full-row normalisers from the tile
+// partials, the tile masses (from the split where it is certain, else
+// directly), the crossing tile and the scan inside it.  The exponentials of
+// the float32 draw's tile, which the tile pass kept, are loaded at the start
+// together with the partials: the crossing tile is almost always that one,
+// as the two draws differ by less than the float32 error.
+template <typename E, bool SH>
+__device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw64Lds& L) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const bool residual = jb.mode == kDrawResidual;
+  const int64_t S2 = p.S2;
+  const int64_t ro = (int64_t)slot * S2;
+  const int64_t htile = jb.y32 >= 0 ? (int64_t)jb.y32 / kDrawTile : -1;
+  double hep[kPer], heq[kPer];
+  if (htile >= 0) {
+    const double* hp = hint_exps(p, slot, 0) + tid;
+    const double* hq = hint_exps(p, slot, 1) + tid;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      hep[j] = hp[j * kDrawThreads];
+      heq[j] = residual ? hq[j * kDrawThreads] : 0.0;
+    }
+  }
+  // the first round of tile partials
+  const bool have0 = tid < S2;
+  double zp0 = 0.0, zq0 = 0.0, d0 = 0.0, a0 = 0.0, s0 = 0.0;
+  int32_t nk0 = 0;
+  if (have0) {
+    zp0 = p.seg_zp64[ro + tid];
+    if (residual) {
+      zq0 = p.seg_zq64[ro + tid];
+      d0 = p.seg_w64[ro + tid];
+      a0 = p.seg_a64[ro + tid];
+      s0 = p.seg_t64[ro + tid];
+      nk0 = p.seg_u32[ro + tid];
+    }
+  }
+  // residual weight per unit of ep of an equal-logit pair (independent of the
+  // loads: computed while they are in flight)
+  const double kappa = exp(((double)jb.mp - (double)jb.mq) * jb.invT);
+  // full-row normalisers: thread sums over the rounds, then a fixed-order tree
+  double zps = zp0, zqs = zq0;
+  for (int64_t j = tid + kDrawThreads; j < S2; j += kDrawThreads) {
+    zps += p.seg_zp64[ro + j];
+    if (residual) zqs += p.seg_zq64[ro + j];
   }
   for (int m = 1; m < kWave; m <<= 1) {
-    a += shfl_xor_d(a, m);
-    b += shfl_xor_d(b, m);
+    zps += shfl_xor_d(zps, m);
+    zqs += shfl_xor_d(zqs, m);
   }
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (lane == 0) {
-    lds[wave][0] = a;
-    lds[wave][1] = b;
+    L.z2[wave][0] = zps;
+    L.z2[wave][1] = zqs;
   }
   __syncthreads();
-  zp = 0.0;
-  zq = 0.0;
+  double Zp = 0.0, Zq = 0.0;
   for (int w = 0; w < kDrawThreads / kWave; ++w) {
-    zp += lds[w][0];
-    zq += lds[w][1];
+    Zp += L.z2[w][0];
+    Zq += L.z2[w][1];
   }
-  __syncthreads();
-}
-
-template <typename E, bool SH>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
-  __shared__ PickLds<double> L;
-  __shared__ double lds[kDrawThreads / kWave];
-  __shared__ double lds2[kDrawThreads / kWave][2];
-  __shared__ int s_redo[kDrawThreads];
-  __shared__ double s_mass[kDrawThreads];
-  const int r = blockIdx.x;
-  const DrawState st = p.req[r];
-  if (st.mode == kDrawNone || !st.need64) return;
-  const bool residual = st.mode == kDrawResidual;
-  const int64_t ro = (int64_t)r * p.S2;
-  // Tile masses stay in LDS when the row has at most one round of tiles.
-  double* masses = p.S2 <= kDrawThreads ? s_mass : p.seg_w64 + ro;
-  // The first round's split results are loaded together with the
-  // normaliser partials: one memory round trip before the masses.
-  const int64_t t0 = threadIdx.x;
-  const bool have0 = residual && t0 < p.S2;
-  int32_t nk0 = 0;
-  double d0 = 0.0, a0 = 0.0, s0 = 0.0;
-  double2 kv0[kDrawKeep64];
-  if (have0) {
-    nk0 = p.seg_u32[ro + t0];
-    d0 = p.seg_w64[ro + t0];
-    a0 = p.seg_a64[ro + t0];
-    s0 = p.seg_t64[ro + t0];
-    const double2* keep = reinterpret_cast<const double2*>(p.seg_e64 + (ro + t0) * (kDrawKeep64 * 2));
-#pragma unroll
-    for (int k = 0; k < kDrawKeep64; ++k) kv0[k] = keep[k];
-  }
-  double Zp, Zq;
-  merge_z64(p.seg_zp64 + ro, residual ? p.seg_zq64 + ro : nullptr, p.S2, lds2, Zp, Zq);
   if (!residual) Zq = 1.0;
-  Weights64<E, SH> w = weights64<E, SH>(p, st, false);
-  w.lnzp = log(Zp);
-  w.lnzq = log(Zq);
-  // Tile masses: from the one-pass split where it is certain, else directly.
-  const double rho = Zq / Zp;
-  const double rho_e = residual ? exp2(log2_ratio_exact(st)) : 0.0;
-  const bool split_ok = residual && (p.flags & SV_FLAG_EXACT_FP64_MASSES) == 0u &&
-                        fabs(rho / rho_e - 1.0) <= 0.5 * kTau64;
-  // residual weight per unit of ep of an equal-logit pair
-  const double kappa = exp(((double)st.mp - (double)st.mq) * w.invT);
-  const double g_tie = fmax(0.0, (Zq - kappa * Zp) / (Zp * Zq));
   const double izp = 1.0 / Zp, izq = 1.0 / Zq;
-  for (int64_t base = 0; base < p.S2; base += kDrawThreads) {
-    const int64_t t = base + threadIdx.x;
+  const Weights64<E, SH> w = weights64<E, SH>(p, jb, false, izp, izq, L.tab);
+  // tile masses: from the one-pass split where it is certain, else directly
+  double* masses = S2 <= kDrawThreads ? L.mass : p.seg_w64 + ro;
+  const double rho = Zq * izp;
+  const double rho_e = jb.rho_e;
+  const bool split_ok = residual && (p.flags & SV_FLAG_EXACT_FP64_MASSES) == 0u &&
+                        fabs(rho - rho_e) <= 0.5 * kTau64 * rho_e;
+  const double g_tie = fmax(0.0, izp - kappa * izq);
+  for (int64_t base = 0; base < S2; base += kDrawThreads) {
+    const int64_t t = base + tid;
     int redo = 0;
-    if (t < p.S2) {
+    if (t < S2) {
       const int64_t o = ro + t;
       if (!residual) {
-        masses[t] = p.seg_zp64[o] / Zp;
+        masses[t] = (base == 0 ? zp0 : p.seg_zp64[o]) * izp;
       } else if (split_ok) {
         int32_t nk = nk0;
         double d = d0, a = a0, sv = s0;
-        double2 kv[kDrawKeep64];
-        if (base == 0) {
-#pragma unroll
-          for (int k = 0; k < kDrawKeep64; ++k) kv[k] = kv0[k];
-        } else {
+        if (base != 0) {
           nk = p.seg_u32[o];
           d = p.seg_w64[o];
           a = p.seg_a64[o];
           sv = p.seg_t64[o];
-          // the whole list is loaded at once (entries past nk are unused)
-          const double2* keep = reinterpret_cast<const double2*>(p.seg_e64 + o * (kDrawKeep64 * 2));
-#pragma unroll
-          for (int k = 0; k < kDrawKeep64; ++k) kv[k] = keep[k];
         }
         if (nk <= kDrawKeep64) {
           double m = (d + (rho - rho_e) * a) * izq + sv * g_tie;
+          // the kept elements, four loads at a time, in element order
+          const double2* keep = reinterpret_cast<const double2*>(p.seg_e64 + o * (kDrawKeep64 * 2));
+          for (int k0 = 0; k0 < nk; k0 += 4) {
+            double2 kv[4];
 #pragma unroll
-          for (int k = 0; k < kDrawKeep64; ++k)
-            if (k < nk) m += fmax(0.0, kv[k].x * izp - kv[k].y * izq);
+            for (int k = 0; k < 4; ++k)
+              kv[k] = (k0 + k < nk) ? keep[k0 + k] : make_double2(0.0, 0.0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (k0 + k < nk) m += w.weight(kv[k].x, kv[k].y);
+          }
           masses[t] = m;
         } else {
           redo = 1;
@@ -523,52 +526,93 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
         redo = 1;
       }
     }
-    s_redo[threadIdx.x] = redo;
+    L.redo[tid] = redo;
     // usually no tile needs a direct recompute: skip the walk over the flags
     if (__syncthreads_or(redo)) {
-      for (int k = 0; k < kDrawThreads && base + k < p.S2; ++k) {
-        if (!s_redo[k]) continue;  // uniform: every thread reads the same flag
-        const double m = tile_mass<double>(w, base + k, p.V, lds);
-        if (threadIdx.x == 0) masses[base + k] = m;
+      for (int k = 0; k < kDrawThreads && base + k < S2; ++k) {
+        if (!L.redo[k]) continue;  // uniform: every thread reads the same flag
+        const double m = tile_mass(w, base + k, p.V, L.pk.scan);
+        if (tid == 0) masses[base + k] = m;
       }
     }
     __syncthreads();
   }
-  // The pick scans the tile masses once for the residual mass R and the
-  // crossing tile.  R = 0 (p = q to float64 precision): draw from p, from the
-  // unnormalised tile partials.
-  PickResult res = pick<double>(masses, p.S2, p.V, (double)st.u, w, L);
-  const bool unnorm = !(res.R > 0.0);
-  if (unnorm) {
-    const Weights64<E, SH> wu = weights64<E, SH>(p, st, true);
-    res = pick<double>(p.seg_zp64 + (int64_t)r * p.S2, p.S2, p.V, (double)st.u, wu, L);
+  // R = 0 (p = q to float64 precision): draw from p, from the unnormalised
+  // tile partials.
+  TileFind f = find_tile(masses, S2, (double)jb.u, L.pk);
+  const bool unnorm = !(f.R > 0.0);
+  if (unnorm) f = find_tile(p.seg_zp64 + ro, S2, (double)jb.u, L.pk);
+  const Weights64<E, SH> wd = unnorm ? weights64<E, SH>(p, jb, true, 1.0, 1.0, L.tab) : w;
+  InTile res{0, -1, 0.0};
+  if (f.tile >= 0) {
+    const int64_t lo = (int64_t)f.tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
+    const int64_t i0 = lo + (int64_t)tid * kPer;
+    double wv[kPer];
+    if (f.tile == htile) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) wv[j] = wd.weight(hep[j], heq[j]);
+    } else {
+      wd(i0, hi, wv);
+    }
+    res = scan_in_tile(wv, i0, f.c0, f.t, L.pk);
   }
   if (!res.found) {
     // t rounded to or past the total: the last token of non-zero weight.
-    __shared__ unsigned long long s_last1;
-    if (threadIdx.x == 0) s_last1 = 0ull;
+    if (tid == 0) L.last1 = 0ull;
     __syncthreads();
-    const Weights64<E, SH> wl = unnorm ? weights64<E, SH>(p, st, true) : w;
-    for (int64_t tile = 0; tile < p.S2; ++tile) {
+    for (int64_t tile = 0; tile < S2; ++tile) {
       const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
-      const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
+      const int64_t i0 = lo + (int64_t)tid * kPer;
       double e[kPer];
-      wl(i0, hi, e);
+      wd(i0, hi, e);
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (e[j] > 0.0) atomicMax(&s_last1, (unsigned long long)(i0 + j + 1));
+        if (e[j] > 0.0) atomicMax(&L.last1, (unsigned long long)(i0 + j + 1));
     }
     __syncthreads();
-    res.y = (int64_t)s_last1 - 1;
+    res.y = (int64_t)L.last1 - 1;
     res.margin = 0.0;
   }
-  if (threadIdx.x == 0) {
-    p.out_tokens[(int64_t)r * (p.D + 1) + st.tau] = (int32_t)res.y;
+  if (tid == 0) {
+    p.out_tokens[(int64_t)jb.r * (p.D + 1) + jb.tau] = (int32_t)res.y;
     if (p.diag) {
-      p.diag[r].draw_margin = (float)res.margin;
-      p.diag[r].bits |= SV_BIT_FP64_DRAW | (unnorm ? SV_BIT_RESIDUAL_ZERO : 0u);
+      p.diag[jb.r].draw_margin = (float)res.margin;
+      p.diag[jb.r].bits |= SV_BIT_FP64_DRAW | (unnorm ? SV_BIT_RESIDUAL_ZERO : 0u);
     }
   }
+}
+
+// Tile pass: workgroups walk the (queue entry, tile) items on a fixed grid.
+// The first entry is read together with the queue length (it is used only
+// once the length shows that it is queued).  An empty queue costs one short
+// dispatch.
+template <typename E, bool SH>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
+  __shared__ Draw64Lds L;
+  const int64_t S2 = p.S2;
+  int64_t it = blockIdx.x;
+  DrawJob jb{};
+  if (it < (int64_t)p.B * S2) jb = p.fb_jobs[it / S2];
+  const int64_t items = (int64_t)(*p.fb_count) * S2;
+  if (it >= items) return;
+  load_exp_table(L);
+  for (; it < items; it += gridDim.x) {
+    const int slot = (int)(it / S2);
+    if (it != (int64_t)blockIdx.x) jb = p.fb_jobs[slot];
+    tile_pass<E, SH>(p, jb, slot, it - (int64_t)slot * S2, L);
+    __syncthreads();
+  }
+}
+
+// Pick: workgroup j draws queue entry j.
+template <typename E, bool SH>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
+  __shared__ Draw64Lds L;
+  const int slot = blockIdx.x;
+  const DrawJob jb = p.fb_jobs[slot];
+  if (slot >= *p.fb_count) return;
+  load_exp_table(L);
+  pick64<E, SH>(p, jb, slot, L);
 }
 
 template <typename E, bool SH>

@@ -47,6 +47,37 @@ __device__ __forceinline__ void load8(const RowView<E, SH>& row, int64_t i0, int
   }
 }
 
+// Eight consecutive logits of the target row (a) and, if has_q, of the draft
+// row (b), as load8 gives them; the vector loads of both rows are issued
+// before either is unpacked, so that the two rows' latencies overlap.
+template <typename E, bool SH>
+__device__ __forceinline__ void load8_pair(const RowView<E, SH>& prow, const RowView<E, SH>& qrow,
+                                           bool has_q, int64_t i0, int64_t hi, float (&a)[kPer],
+                                           float (&b)[kPer]) {
+  if (i0 + kPer <= hi) {
+    constexpr int NV = kPer / E::kPerVec;  // 16-byte vectors per row
+    uint4 x[NV], y[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) x[v] = load16(prow.at(i0 + v * E::kPerVec));
+    if (has_q) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) y[v] = load16(qrow.at(i0 + v * E::kPerVec));
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) E::unpack(x[v], a + v * E::kPerVec);
+    if (has_q) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) E::unpack(y[v], b + v * E::kPerVec);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      a[j] = (i0 + j < hi) ? E::load1(prow.at(i0 + j), 0) : -INFINITY;
+      if (has_q) b[j] = (i0 + j < hi) ? E::load1(qrow.at(i0 + j), 0) : -INFINITY;
+    }
+  }
+}
+
 // Float32 weights of a draw row, against the row states of the accept
 // kernel: 2^((x sl - R(m)) - log2 z), as the accept ratio takes them.
 template <typename E, bool SH>
@@ -71,11 +102,19 @@ struct Weights32 {
   }
   __device__ __forceinline__ void operator()(int64_t i0, int64_t hi, float (&w)[kPer]) const {
     float a[kPer], b[kPer];
-    load8<E, SH>(prow, i0, hi, a);
-    if (has_q) load8<E, SH>(qrow, i0, hi, b);
+    load8_pair<E, SH>(prow, qrow, has_q, i0, hi, a, b);
     from(a, b, w);
   }
 };
+
+// log2(Zq / Zp) from the float32 row states, with Z = sum 2^((x - m) sl): each
+// log2 sum lz is taken against the integer reference R(m), so each adds its
+// offset R(m) - m sl (exact in float64, as the product of two floats is).
+__device__ __forceinline__ double log2_ratio_exact(const DrawState& st) {
+  const double op = (double)ref_of(st.mp, st.sl) - (double)st.mp * (double)st.sl;
+  const double oq = (double)ref_of(st.mq, st.sl) - (double)st.mq * (double)st.sl;
+  return ((double)st.lzq + oq) - ((double)st.lzp + op);
+}
 
 template <typename E, bool SH>
 __device__ __forceinline__ Weights32<E, SH> weights32(const VerifyParams& p, const DrawState& st) {

@@ -25,7 +25,8 @@ constexpr int kMaxTeam = 64;
 // four-word record.
 constexpr int kTeamXchWords = kMaxTeamGrid * 4 * 4;
 
-// What k_accept leaves for the draw kernels of one request.
+// The draw of one request, as the accept phase of k_accept_draw leaves it
+// for the float32 draw of the same kernel.
 struct DrawState {
   int32_t mode;     // DrawMode
   int32_t tau;      // position of the emitted draw
@@ -37,11 +38,23 @@ struct DrawState {
   float mq, lzq;    // draft row: the same
   float zp;         // target row: sum 2^(x sl - R(max))
   float u;          // draw uniform (word 1 of the Philox block at tau)
-  int32_t need64;   // set when the float32 draw must be recomputed in float64
-  float margin;     // float32 CDF margin of the draw
-  uint32_t bits;
+};
+
+// A draw queued for the float64 recompute: everything the float64 kernel
+// needs, in one 64-byte entry, so that its workgroups read one entry before
+// the logits.
+struct DrawJob {
+  int64_t prow, qrow;  // target row; draft row (residual draws, else 0)
+  double invT;         // 1 / T in float64
+  double rho_e;        // Zq / Zp from the float32 row states (residual draws)
+  float mp, mq;        // row maxima (the float64 exponentials are taken against them)
+  float u;             // draw uniform
+  int32_t mode;        // kDrawResidual or kDrawBonus
+  int32_t r, tau;      // request and position of the draw
+  int32_t y32;         // token of the float32 draw (-1: none): its tile is prefetched
   int32_t pad;
 };
+static_assert(sizeof(DrawJob) == 64, "one 64-byte queue entry");
 
 // One row-pass work item, written by the planner so that a workgroup can
 // issue a unit's loads from a single 32-byte read.
@@ -97,8 +110,7 @@ struct VerifyParams {
   float* part_a;     // [U][S1]  partial sum min(p, q)
   float2* pair_p;    // [U]      row state of a pair's target row (the normaliser its rates used)
   float2* pair_q;    // [U]      row state of a pair's draft row
-  DrawState* req;    // [B]
-  float* seg_w32;    // [B][S2]
+  // float64 tile partials, indexed by queue entry
   double* seg_zp64;  // [B][S2]
   double* seg_zq64;  // [B][S2]
   double* seg_w64;   // [B][S2]  float64 tile masses (first the sums D of the one-pass split)
@@ -106,8 +118,10 @@ struct VerifyParams {
   double* seg_t64;   // [B][S2]  float64 sums of ep over equal logit pairs
   int32_t* seg_u32;  // [B][S2]  elements of a tile whose residual sign was not certain
   double* seg_e64;   // [B][S2][kDrawKeep64][2]  their (ep, eq), in element order
-  int32_t* fb_count; // requests queued for the float64 draw
-  int32_t* fb_list;  // [B]
+  double* seg_h64;   // [B][2][kDrawTile]  exponentials of the float32 draw's tile
+  int32_t* fb_count; // draws queued for the float64 recompute
+  DrawJob* fb_jobs;  // [B]  the queue
+  int32_t* fb_done;  // [B]  tiles of queue entry j done (zeroed by k_plan)
   PlanItem* plan_pairs;    // [B * D]        row pairs at T > 0
   PlanItem* plan_singles;  // [B * (D + 1)]  single rows
   int32_t* plan_counts;    // [2]
@@ -144,8 +158,8 @@ inline void draw_geometry(int64_t V, int32_t* S2, int32_t* seg2) {
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WorkspaceLayout {
-  size_t part_p, part_q, part_a, pair_p, pair_q, req, seg_w32, seg_zp64, seg_zq64, seg_w64, seg_a64, seg_t64, seg_u32, seg_e64,
-      fb_count, fb_list,
+  size_t part_p, part_q, part_a, pair_p, pair_q, seg_zp64, seg_zq64, seg_w64, seg_a64, seg_t64,
+      seg_u32, seg_e64, seg_h64, fb_count, fb_jobs, fb_done,
       plan_pairs, plan_singles, plan_counts, team_xch, shard_tab, sync_error, total;
   int32_t slots;
 };
@@ -164,8 +178,6 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
   L.part_a = off; off += align256(U * slots * sizeof(float));
   L.pair_p = off; off += align256(U * sizeof(float2));
   L.pair_q = off; off += align256(U * sizeof(float2));
-  L.req = off; off += align256((size_t)B * sizeof(DrawState));
-  L.seg_w32 = off; off += align256((size_t)B * S2 * sizeof(float));
   L.seg_zp64 = off; off += align256((size_t)B * S2 * sizeof(double));
   L.seg_zq64 = off; off += align256((size_t)B * S2 * sizeof(double));
   L.seg_w64 = off; off += align256((size_t)B * S2 * sizeof(double));
@@ -173,8 +185,10 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t D, int64_t V) {
   L.seg_t64 = off; off += align256((size_t)B * S2 * sizeof(double));
   L.seg_u32 = off; off += align256((size_t)B * S2 * sizeof(int32_t));
   L.seg_e64 = off; off += align256((size_t)B * S2 * kDrawKeep64 * 2 * sizeof(double));
+  L.seg_h64 = off; off += align256((size_t)B * 2 * kDrawTile * sizeof(double));
   L.fb_count = off; off += align256(sizeof(int32_t));
-  L.fb_list = off; off += align256((size_t)B * sizeof(int32_t));
+  L.fb_jobs = off; off += align256((size_t)B * sizeof(DrawJob));
+  L.fb_done = off; off += align256((size_t)B * sizeof(int32_t));
   L.plan_pairs = off; off += align256((size_t)B * (size_t)D * sizeof(PlanItem));
   L.plan_singles = off; off += align256(U * sizeof(PlanItem));
   L.plan_counts = off; off += align256(2 * sizeof(int32_t));

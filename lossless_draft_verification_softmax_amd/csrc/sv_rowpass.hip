@@ -72,6 +72,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(VerifyParams p) {
     float T = 0.0f;
     int64_t t0 = 0, d0 = 0;
     if (r < p.B) {
+      p.fb_done[r] = 0;
       // every load of the request at once
       n = p.depth[r];
       T = p.temperature[r];

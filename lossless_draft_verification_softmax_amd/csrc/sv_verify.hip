@@ -226,7 +226,6 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
     if (k == 0) {
       p.accepted_len[r] = 0;
       p.num_out[r] = 0;
-      p.req[r].mode = kDrawNone;
       if (p.diag) p.diag[r] = sv_diag{INFINITY, INFINITY, all_bits | info, 0};
     }
     return;
@@ -270,9 +269,6 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
   if (k == tau) {
     DrawState st;
     st.tau = tau;
-    st.bits = 0u;
-    st.need64 = 0;
-    st.margin = INFINITY;
     if (T == 0.0f) {
       st.mode = kDrawNone;
     } else {
@@ -289,7 +285,6 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
       const Philox4 w = philox4x32_10((uint32_t)tau, rid, p.step, 0u, p.seed_lo, p.seed_hi);
       st.u = u24(w.w[1]);
     }
-    p.req[r] = st;
     L.st = st;
   }
   if (k == 0) {
@@ -424,9 +419,21 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
       p.out_tokens[(int64_t)r * (D + 1) + st.tau] = L.y;
       if (p.diag) p.diag[r].draw_margin = m;
     } else {
-      p.req[r].need64 = 1;
-      const int slot = atomicAdd(p.fb_count, 1);
-      p.fb_list[slot] = r;
+      const bool residual = st.mode == kDrawResidual;
+      DrawJob jb;
+      jb.prow = st.prow;
+      jb.qrow = residual ? st.qrow : 0;
+      jb.invT = 1.0 / (double)st.T;
+      jb.rho_e = residual ? exp2(log2_ratio_exact(st)) : 0.0;
+      jb.mp = st.mp;
+      jb.mq = st.mq;
+      jb.u = st.u;
+      jb.mode = st.mode;
+      jb.r = r;
+      jb.tau = st.tau;
+      jb.y32 = found ? L.y : -1;
+      jb.pad = 0;
+      p.fb_jobs[atomicAdd(p.fb_count, 1)] = jb;
     }
   }
 }

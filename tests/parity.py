@@ -146,9 +146,14 @@ def compare(gpu: dict, orc: dict, requests, temperature, depth, *, check_alpha=T
 
 
 def _check_margins(gpu, orc, r, i, rep):
-    """Margins of a request whose outputs agree with the oracle's."""
+    """Margins of a request whose outputs agree with the oracle's.  A margin
+    the oracle puts inside its flag band is not compared: there the decision
+    itself may go either way (and a float64 residual that vanishes takes the
+    draw from p), so the two margins need not be close."""
     ga, oa = float(gpu["accept_margin"][r]), float(orc["accept_margin"][i])
-    if np.isinf(oa) or np.isinf(ga):
+    if oa < ACCEPT_BAND:
+        pass
+    elif np.isinf(oa) or np.isinf(ga):
         assert np.isinf(oa) and np.isinf(ga), (r, ga, oa)
     else:
         err = abs(ga - oa)
@@ -156,6 +161,8 @@ def _check_margins(gpu, orc, r, i, rep):
         assert err <= ACCEPT_MARGIN_RTOL * (oa + 1.0), (r, ga, oa)
     gd, od = float(gpu["draw_margin"][r]), float(orc["draw_margin"][i])
     err = abs(gd - od)
+    if od < DRAW_BAND:
+        return
     if int(gpu["bits"][r]) & sv.BIT_FP64_DRAW:
         rep["max_draw_margin_err64"] = max(rep["max_draw_margin_err64"], err)
         assert err <= DRAW_MARGIN_RTOL64 * od + DRAW_MARGIN_ATOL64, (r, gd, od)
