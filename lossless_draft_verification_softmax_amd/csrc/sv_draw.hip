@@ -26,7 +26,9 @@
 namespace sv {
 
 constexpr int kDrawThreads = 256;
-constexpr int kQueueGrid = 2048;
+// Tile-pass workgroups per CU: all resident at once (four waves per SIMD at
+// up to 128 registers per lane).
+constexpr int kTileBlocksPerCu = 4;
 
 // Fixed-order block scan (Hillis-Steele in each wavefront, wave totals in
 // order).  Returns the inclusive value; *total gets the block total.
@@ -74,7 +76,9 @@ __device__ __forceinline__ T shfl_up1(T v) {
 // Float64 weights: the temperature is applied as a multiplication by the
 // float64 reciprocal of T (one extra rounding, about 1e-16 relative, where a
 // division would cost ten float64 operations per element); an element's
-// unnormalised exponentials are ep = exp((a - mp) / T), eq = exp((b - mq) / T)
+// unnormalised exponentials are ep = exp((a - mp) / T), eq = exp((b - mq) / T),
+// their arguments taken in one fma as a / T + (-m / T) (the rounding of
+// -m / T scales a whole row by one factor, which its normaliser cancels),
 // and its weight max(0, ep / Zp - eq / Zq) (residual draw) or ep / Zp (bonus
 // draw), with the float64 normalisers Zp = sum ep, Zq = sum eq applied as
 // reciprocals.  Every path that weighs an element (the kept near-ties, the
@@ -83,7 +87,7 @@ template <typename E, bool SH>
 struct Weights64 {
   RowView<E, SH> prow, qrow;
   bool has_q;         // residual draw: w = max(0, p - q); else w = p
-  double invT, mp, mq;
+  double invT, cp, cq;  // exponent arguments fma(x, 1/T, c): c = -m / T of the row
   double izp, izq;    // 1 / Zp, 1 / Zq (izp = 1: the unnormalised p of a zero residual)
   const double* tab;  // 2^(j/64) table of exp64_tab (LDS)
   // weights from the unnormalised exponentials
@@ -97,8 +101,8 @@ struct Weights64 {
                                        double (&w)[kPer]) const {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const double ep = exp64_tab(((double)a[j] - mp) * invT, tab);
-      const double eq = has_q ? exp64_tab(((double)b[j] - mq) * invT, tab) : 0.0;
+      const double ep = exp64_tab(fma((double)a[j], invT, cp), tab);
+      const double eq = has_q ? exp64_tab(fma((double)b[j], invT, cq), tab) : 0.0;
       w[j] = weight(ep, eq);
     }
   }
@@ -118,8 +122,8 @@ __device__ __forceinline__ Weights64<E, SH> weights64(const VerifyParams& p, con
   w.prow = row_view<E, SH>(p, false, jb.prow);
   w.qrow = row_view<E, SH>(p, true, w.has_q ? jb.qrow : 0);
   w.invT = jb.invT;
-  w.mp = jb.mp;
-  w.mq = jb.mq;
+  w.cp = -(double)jb.mp * jb.invT;
+  w.cq = -(double)jb.mq * jb.invT;
   w.izp = unnormalised ? 1.0 : izp;
   w.izq = izq;
   w.tab = tab;
@@ -298,7 +302,7 @@ struct Draw64Lds {
 
 // The exponential table into LDS (read by every exp64_tab of the kernel).
 __device__ __forceinline__ void load_exp_table(Draw64Lds& L) {
-  if (threadIdx.x < kExp64Table) L.tab[threadIdx.x] = kExp2Frac[threadIdx.x];
+  for (int j = threadIdx.x; j < kExp64Table; j += kDrawThreads) L.tab[j] = kExp2Frac[j];
   __syncthreads();
 }
 
@@ -308,41 +312,52 @@ __device__ __forceinline__ double* hint_exps(const VerifyParams& p, int slot, in
   return p.seg_h64 + ((int64_t)slot * 2 + row) * kDrawTile;
 }
 
+// This thread's eight elements of tile `tile` of a queued draw's rows.
+template <typename E, bool SH>
+__device__ __forceinline__ void tile_load(const VerifyParams& p, const DrawJob& jb, int64_t tile,
+                                          Raw8<E>& raw) {
+  const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
+  load_raw8<E, SH>(row_view<E, SH>(p, false, jb.prow), row_view<E, SH>(p, true, jb.qrow),
+                   jb.mode == kDrawResidual, lo + (int64_t)threadIdx.x * kPer, hi, raw);
+}
+
 template <typename E, bool SH>
 __device__ __forceinline__ void tile_pass(const VerifyParams& p, const DrawJob& jb, int slot,
-                                          int64_t tile, Draw64Lds& L) {
+                                          int64_t tile, const Raw8<E>& raw, Draw64Lds& L) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int64_t o = (int64_t)slot * p.S2 + tile;
   const bool residual = jb.mode == kDrawResidual;
   const bool hinted = jb.y32 >= 0 && (int64_t)jb.y32 / kDrawTile == tile;
   const double invT = jb.invT, rho_e = jb.rho_e;
-  const double mp = jb.mp, mq = jb.mq;
+  const double cp = -(double)jb.mp * invT, cq = -(double)jb.mq * invT;
+  const double tau_rho = kTau64 * rho_e;
   const int64_t lo = tile * kDrawTile, hi = min(p.V, lo + (int64_t)kDrawTile);
   const int64_t i0 = lo + (int64_t)threadIdx.x * kPer;
   float a[kPer], b[kPer];
-  load8_pair<E, SH>(row_view<E, SH>(p, false, jb.prow), row_view<E, SH>(p, true, jb.qrow),
-                    residual, i0, hi, a, b);
+  unpack_raw8<E, SH>(raw, row_view<E, SH>(p, false, jb.prow), row_view<E, SH>(p, true, jb.qrow),
+                     residual, i0, hi, a, b);
   double* hp = hint_exps(p, slot, 0) + threadIdx.x;
   double* hq = hint_exps(p, slot, 1) + threadIdx.x;
   double zp = 0.0, zq = 0.0, D = 0.0, A = 0.0, S = 0.0;
   uint32_t kmask = 0u;  // elements kept for the pick (their ep, eq recomputed below)
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const double ep = exp64_tab(((double)a[j] - mp) * invT, L.tab);
+    const double ep = exp64_tab(fma((double)a[j], invT, cp), L.tab);
     zp += ep;
     if (hinted) hp[j * kDrawThreads] = ep;
     if (residual) {
-      const double eq = exp64_tab(((double)b[j] - mq) * invT, L.tab);
+      const double eq = exp64_tab(fma((double)b[j], invT, cq), L.tab);
       zq += eq;
       if (hinted) hq[j * kDrawThreads] = eq;
       const double d = fma(ep, rho_e, -eq);
-      const double tol = kTau64 * ep * rho_e;
+      const double tol = tau_rho * ep;
       if (a[j] == b[j]) {
         S += ep;
       } else if (d > tol) {
         D += d;
         A += ep;
-      } else if (d >= -tol && (ep > 0.0 || eq > 0.0)) {
+      } else if (d >= -tol && ep > 0.0) {
+        // (ep = 0 weighs max(0, -eq) = 0: never kept)
         kmask |= 1u << j;
       }
     }
@@ -369,8 +384,8 @@ __device__ __forceinline__ void tile_pass(const VerifyParams& p, const DrawJob& 
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       if ((kmask >> j) & 1u) {
-        keep[2 * pos] = exp64_tab(((double)a[j] - mp) * invT, L.tab);
-        keep[2 * pos + 1] = exp64_tab(((double)b[j] - mq) * invT, L.tab);
+        keep[2 * pos] = exp64_tab(fma((double)a[j], invT, cp), L.tab);
+        keep[2 * pos + 1] = exp64_tab(fma((double)b[j], invT, cq), L.tab);
         ++pos;
       }
     }
@@ -458,7 +473,7 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
   }
   // residual weight per unit of ep of an equal-logit pair (independent of the
   // loads: computed while they are in flight)
-  const double kappa = exp(((double)jb.mp - (double)jb.mq) * jb.invT);
+  // (equal logits a = b have eq / ep = exp(cq - cp))
   // full-row normalisers: thread sums over the rounds, then a fixed-order tree
   double zps = zp0, zqs = zq0;
   for (int64_t j = tid + kDrawThreads; j < S2; j += kDrawThreads) {
@@ -482,6 +497,7 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
   if (!residual) Zq = 1.0;
   const double izp = 1.0 / Zp, izq = 1.0 / Zq;
   const Weights64<E, SH> w = weights64<E, SH>(p, jb, false, izp, izq, L.tab);
+  const double kappa = exp(w.cq - w.cp);
   // tile masses: from the one-pass split where it is certain, else directly
   double* masses = S2 <= kDrawThreads ? L.mass : p.seg_w64 + ro;
   const double rho = Zq * izp;
@@ -582,25 +598,41 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
   }
 }
 
-// Tile pass: workgroups walk the (queue entry, tile) items on a fixed grid.
-// The first entry is read together with the queue length (it is used only
+// Tile pass: the (queue entry, tile) items are dealt to a grid of
+// kTileBlocksPerCu workgroups per CU, all resident at once, item it to
+// workgroup it mod grid.  Each workgroup issues the loads of its next item
+// before it works on the current one, and reads the queue entries of its
+// first two items together with the queue length (an entry is used only
 // once the length shows that it is queued).  An empty queue costs one short
 // dispatch.
 template <typename E, bool SH>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_tile64(VerifyParams p) {
+__global__ __launch_bounds__(kDrawThreads, kTileBlocksPerCu) void k_draw_tile64(VerifyParams p) {
   __shared__ Draw64Lds L;
-  const int64_t S2 = p.S2;
+  const int64_t S2 = p.S2, G = gridDim.x, cap = (int64_t)p.B * S2;
   int64_t it = blockIdx.x;
-  DrawJob jb{};
-  if (it < (int64_t)p.B * S2) jb = p.fb_jobs[it / S2];
+  DrawJob jb{}, jn{};
+  if (it < cap) jb = p.fb_jobs[it / S2];
+  if (it + G < cap) jn = p.fb_jobs[(it + G) / S2];
   const int64_t items = (int64_t)(*p.fb_count) * S2;
   if (it >= items) return;
   load_exp_table(L);
-  for (; it < items; it += gridDim.x) {
+  Raw8<E> raw;
+  tile_load<E, SH>(p, jb, it % S2, raw);
+  for (; it < items; it += G) {
+    // the next item's loads (the current item's again past the end, so
+    // that every address is valid and no branch splits the loads)
+    const int64_t nx = it + G;
+    const bool more = nx < items;
+    Raw8<E> rawn;
+    tile_load<E, SH>(p, more ? jn : jb, more ? nx % S2 : it % S2, rawn);
+    DrawJob jnn{};
+    if (nx + G < items) jnn = p.fb_jobs[(nx + G) / S2];
     const int slot = (int)(it / S2);
-    if (it != (int64_t)blockIdx.x) jb = p.fb_jobs[slot];
-    tile_pass<E, SH>(p, jb, slot, it - (int64_t)slot * S2, L);
+    tile_pass<E, SH>(p, jb, slot, it - (int64_t)slot * S2, raw, L);
     __syncthreads();
+    raw = rawn;
+    jb = jn;
+    jn = jnn;
   }
 }
 
@@ -616,19 +648,20 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
 }
 
 template <typename E, bool SH>
-static void launch_draw_t(const VerifyParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((k_draw_tile64<E, SH>), dim3(kQueueGrid), dim3(kDrawThreads), 0, stream, p);
+static void launch_draw_t(const VerifyParams& p, int cus, hipStream_t stream) {
+  hipLaunchKernelGGL((k_draw_tile64<E, SH>), dim3(cus * kTileBlocksPerCu), dim3(kDrawThreads), 0,
+                     stream, p);
   hipLaunchKernelGGL((k_draw_pick64<E, SH>), dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
 }
 
-void launch_draw(const VerifyParams& p, hipStream_t stream) {
+void launch_draw(const VerifyParams& p, int cus, hipStream_t stream) {
   const bool sh = p.nshard > 1;
   if (p.dtype == SV_DTYPE_BF16) {
-    if (sh) launch_draw_t<Bf16, true>(p, stream);
-    else launch_draw_t<Bf16, false>(p, stream);
+    if (sh) launch_draw_t<Bf16, true>(p, cus, stream);
+    else launch_draw_t<Bf16, false>(p, cus, stream);
   } else {
-    if (sh) launch_draw_t<F32, true>(p, stream);
-    else launch_draw_t<F32, false>(p, stream);
+    if (sh) launch_draw_t<F32, true>(p, cus, stream);
+    else launch_draw_t<F32, false>(p, cus, stream);
   }
 }
 

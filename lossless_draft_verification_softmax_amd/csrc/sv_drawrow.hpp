@@ -47,27 +47,40 @@ __device__ __forceinline__ void load8(const RowView<E, SH>& row, int64_t i0, int
   }
 }
 
-// Eight consecutive logits of the target row (a) and, if has_q, of the draft
-// row (b), as load8 gives them; the vector loads of both rows are issued
-// before either is unpacked, so that the two rows' latencies overlap.
+// Eight consecutive logits of the target row and, if has_q, of the draft
+// row, in two steps: the raw 16-byte vectors (issued together, so the two
+// rows' latencies overlap, and early enough to be in flight while other work
+// runs), then the unpacked values a, b as load8 gives them.  A group that
+// reaches past hi is read element by element in the second step.
+template <typename E>
+struct Raw8 {
+  static constexpr int NV = kPer / E::kPerVec;  // 16-byte vectors per row
+  uint4 x[NV], y[NV];
+};
+
 template <typename E, bool SH>
-__device__ __forceinline__ void load8_pair(const RowView<E, SH>& prow, const RowView<E, SH>& qrow,
-                                           bool has_q, int64_t i0, int64_t hi, float (&a)[kPer],
-                                           float (&b)[kPer]) {
+__device__ __forceinline__ void load_raw8(const RowView<E, SH>& prow, const RowView<E, SH>& qrow,
+                                          bool has_q, int64_t i0, int64_t hi, Raw8<E>& r) {
   if (i0 + kPer <= hi) {
-    constexpr int NV = kPer / E::kPerVec;  // 16-byte vectors per row
-    uint4 x[NV], y[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) x[v] = load16(prow.at(i0 + v * E::kPerVec));
+    for (int v = 0; v < Raw8<E>::NV; ++v) r.x[v] = load16(prow.at(i0 + v * E::kPerVec));
     if (has_q) {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) y[v] = load16(qrow.at(i0 + v * E::kPerVec));
+      for (int v = 0; v < Raw8<E>::NV; ++v) r.y[v] = load16(qrow.at(i0 + v * E::kPerVec));
     }
+  }
+}
+
+template <typename E, bool SH>
+__device__ __forceinline__ void unpack_raw8(const Raw8<E>& r, const RowView<E, SH>& prow,
+                                            const RowView<E, SH>& qrow, bool has_q, int64_t i0,
+                                            int64_t hi, float (&a)[kPer], float (&b)[kPer]) {
+  if (i0 + kPer <= hi) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) E::unpack(x[v], a + v * E::kPerVec);
+    for (int v = 0; v < Raw8<E>::NV; ++v) E::unpack(r.x[v], a + v * E::kPerVec);
     if (has_q) {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) E::unpack(y[v], b + v * E::kPerVec);
+      for (int v = 0; v < Raw8<E>::NV; ++v) E::unpack(r.y[v], b + v * E::kPerVec);
     }
   } else {
 #pragma unroll
@@ -76,6 +89,15 @@ __device__ __forceinline__ void load8_pair(const RowView<E, SH>& prow, const Row
       if (has_q) b[j] = (i0 + j < hi) ? E::load1(qrow.at(i0 + j), 0) : -INFINITY;
     }
   }
+}
+
+template <typename E, bool SH>
+__device__ __forceinline__ void load8_pair(const RowView<E, SH>& prow, const RowView<E, SH>& qrow,
+                                           bool has_q, int64_t i0, int64_t hi, float (&a)[kPer],
+                                           float (&b)[kPer]) {
+  Raw8<E> r;
+  load_raw8<E, SH>(prow, qrow, has_q, i0, hi, r);
+  unpack_raw8<E, SH>(r, prow, qrow, has_q, i0, hi, a, b);
 }
 
 // Float32 weights of a draw row, against the row states of the accept

@@ -205,7 +205,7 @@ bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
 hipError_t launch_rowteam(VerifyParams& p, int grid, int nv, hipStream_t stream);
 void launch_plan(const VerifyParams& p, hipStream_t stream);
 void launch_rowpass(const VerifyParams& p, int grid, hipStream_t stream);
-void launch_draw(const VerifyParams& p, hipStream_t stream);
+void launch_draw(const VerifyParams& p, int cus, hipStream_t stream);
 hipError_t launch_budget(const float* conf, int32_t B, int32_t D, const int32_t* max_depth,
                          int64_t K, int32_t* depth, int64_t* draft_row0, int64_t* target_row0,
                          float* utility, hipStream_t stream);

@@ -499,7 +499,7 @@ static hipError_t launch_all(VerifyParams& p, int grid, hipStream_t stream) {
     hipLaunchKernelGGL((k_accept_draw<E, false>), dim3((unsigned)p.B), dim3(kAcceptDrawThreads), 0,
                        stream, p);
   mark(p, 3, stream);
-  launch_draw(p, stream);
+  launch_draw(p, grid, stream);
   mark(p, 4, stream);
   return hipGetLastError();
 }
