@@ -81,7 +81,11 @@ typedef enum sv_dtype { SV_DTYPE_BF16 = 0, SV_DTYPE_FP32 = 1 } sv_dtype;
 #define SV_BIT_BAD_TOKEN 2u        /* a draft token outside [0, V)                     */
 #define SV_BIT_BAD_ROW 4u          /* a verified row has NaN / +inf or is all -inf     */
 #define SV_BIT_RESIDUAL_ZERO 8u    /* residual mass was zero: the draw used p          */
-#define SV_BIT_BAD_TEMPERATURE 16u /* temperature[r] negative, NaN or infinite         */
+#define SV_BIT_BAD_TEMPERATURE 16u /* temperature[r] negative, NaN or infinite, or T > 0
+                                      so small that a verified row's maximum m gives
+                                      |m * (log2(e) / T)| >= 2^24 in float32, past the
+                                      exact range of the row-state arithmetic (below
+                                      T ~ 1e-5 for logits near 100; use T = 0) */
 #define SV_BIT_FP64_DRAW 32u       /* the draw was recomputed in float64               */
 #define SV_BIT_SYNC_TIMEOUT 64u    /* information only: a team wait of the row pass
                                       expired (members of a team were not resident at

@@ -144,6 +144,17 @@ __device__ __forceinline__ float ref_of(float m, float sl) {
   return __builtin_rintf(m * sl);
 }
 
+// The references carry a row state exactly while |fl(m sl)| < 2^24: then
+// R(m) lies within 3/4 of m sl, so x sl - R(m) is within [-3/4, 3/4] at the
+// maximum (past 2^24 the rounding of fl(m sl) alone can exceed the range of
+// 2^x).  A row whose scaled maximum reaches 2^24 (a
+// temperature below about 1e-5 for logits of magnitude 100) is outside the
+// verifier's domain: its request is reported invalid (SV_BIT_BAD_TEMPERATURE).
+constexpr float kMaxScaledMax = 16777216.0f;  // 2^24
+__device__ __forceinline__ bool scale_ok(float m, float sl) {
+  return fabsf(m * sl) < kMaxScaledMax;
+}
+
 // 2^(R(a) - R(m)): the factor that takes a sum relative to a's reference to
 // m's reference (exactly 1 for a = m; the exponent is an exact integer).
 __device__ __forceinline__ float rescale(float a, float m, float sl) {

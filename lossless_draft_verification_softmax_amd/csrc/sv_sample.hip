@@ -17,8 +17,8 @@
 // of 8 elements, read group by group (16-byte vector loads when the row is
 // 16-byte aligned, else element by element; up to 64 bf16 or 32 fp32
 // elements per thread stay in registers for every pass).  The weights are
-// float64 exp(x / T - m / T) (the table-driven exp of the float64 draw, about
-// 2 ulp), each group summed as a tree, a thread's groups in order, then one
+// float64 exp((x - m) / T) (x - m taken in float64; the table-driven exp of
+// the float64 draw, about 2 ulp), which holds at any temperature, each group summed as a tree, a thread's groups in order, then one
 // fixed-order block scan of the thread sums (wavefront scans, then the
 // wavefront totals in order); t = u R, and the thread whose chunk holds t
 // walks it group by group and then inside the group.  A float32 pass would
@@ -230,14 +230,14 @@ __device__ __forceinline__ void sample_row(const SampleParams& p, int32_t* out, 
     return;
   }
 
-  // ---- float64 weights exp(x / T - m / T), group sums as a tree ----
+  // ---- float64 weights exp((x - m) / T), group sums as a tree ----
   const double invT = 1.0 / (double)T;
-  const double cm = -(double)m * invT;
+  const double md = (double)m;
   double sum = 0.0;
   ch.each([&](int64_t, const float (&x)[kPer]) {
     double w[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) w[j] = exp64_tab(fma((double)x[j], invT, cm), L.tab);
+    for (int j = 0; j < kPer; ++j) w[j] = exp64_tab(((double)x[j] - md) * invT, L.tab);
     sum += tree8(w);
     return true;
   });
@@ -256,7 +256,7 @@ __device__ __forceinline__ void sample_row(const SampleParams& p, int32_t* out, 
       ch.each([&](int64_t i0, const float (&x)[kPer]) {
         double w[kPer];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) w[j] = exp64_tab(fma((double)x[j], invT, cm), L.tab);
+        for (int j = 0; j < kPer; ++j) w[j] = exp64_tab(((double)x[j] - md) * invT, L.tab);
         const double gs = tree8(w);
         if (!(c + gs > t)) {  // the whole group lies below t
           c += gs;
@@ -286,7 +286,7 @@ __device__ __forceinline__ void sample_row(const SampleParams& p, int32_t* out, 
   ch.each([&](int64_t i0, const float (&x)[kPer]) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      if (exp64_tab(fma((double)x[j], invT, cm), L.tab) > 0.0) lastp = (int)(i0 + j);
+      if (exp64_tab(((double)x[j] - md) * invT, L.tab) > 0.0) lastp = (int)(i0 + j);
     return true;
   });
   for (int o = 1; o < kWave; o <<= 1) lastp = max(lastp, __shfl_xor(lastp, o));

@@ -194,12 +194,14 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
                                   : merge_row(pv, p.part_p, unit, p.S1, np_, sl),
                        sl);
       if (!finite_f(sp.m)) bits |= SV_BIT_BAD_ROW;
+      else if (!scale_ok(sp.m, sl)) bits |= SV_BIT_BAD_TEMPERATURE;
       if (k < n) {
         if (p.draft == nullptr) {
           bits |= SV_BIT_BAD_ROW;
         } else {
           sq = renormalise(SoftmaxPart{pq.x, pq.y}, sl);
           if (!finite_f(sq.m)) bits |= SV_BIT_BAD_ROW;
+          else if (!scale_ok(sq.m, sl)) bits |= SV_BIT_BAD_TEMPERATURE;
         }
       }
       if (k < n && bits == 0u) {

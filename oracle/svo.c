@@ -87,6 +87,15 @@ int svo_row_valid(const float* x, int64_t V) {
   return finite_seen;
 }
 
+/* |m * sl| < 2^24 in float32 for the row maximum m (a valid row). */
+static int svo_scale_ok(const float* x, int64_t V, float sl) {
+  float m = -INFINITY;
+  for (int64_t y = 0; y < V; ++y)
+    if (x[y] > m) m = x[y];
+  const float scaled = m * sl;
+  return fabsf(scaled) < 16777216.0f;
+}
+
 int64_t svo_argmax(const float* x, int64_t V) {
   int64_t best = -1;
   for (int64_t y = 0; y < V; ++y) {
@@ -335,6 +344,21 @@ int svo_verify_batch(const float* target, const float* draft, int64_t V, int64_t
           Q_rows[k] = draft + (draft_row0[r] + k) * row_stride;
           if (!svo_row_valid(Q_rows[k], V)) b |= SVO_BIT_BAD_ROW;
         }
+      }
+      if (T > 0.0f) {
+        /* Domain of the temperature (a reading; the pages fix none): the
+           verifier scales logits by log2(e)/T in float32 and is exact only
+           while every verified row's maximum m has |m * fl(log2(e)/T)| below
+           2^24, both products rounded to float32.  Past that the request is
+           reported invalid; greedy verification (T = 0) covers that regime. */
+        const float sl = 1.4426950408889634f / T;
+        for (int32_t k = 0; k <= n; ++k)
+          if (svo_row_valid(P_rows[k], V) && !svo_scale_ok(P_rows[k], V, sl))
+            b |= SVO_BIT_BAD_TEMPERATURE;
+        if (draft)
+          for (int32_t k = 0; k < n; ++k)
+            if (svo_row_valid(Q_rows[k], V) && !svo_scale_ok(Q_rows[k], V, sl))
+              b |= SVO_BIT_BAD_TEMPERATURE;
       }
     }
     if (b) {

@@ -52,7 +52,9 @@ enum {
   SVO_BIT_BAD_TOKEN = 2u,      /* a draft token id outside [0, V)                */
   SVO_BIT_BAD_ROW = 4u,        /* a verified row holds NaN / +inf, or only -inf  */
   SVO_BIT_RESIDUAL_ZERO = 8u,  /* residual mass was zero; the target row was used */
-  SVO_BIT_BAD_TEMPERATURE = 16u /* temperature negative, NaN or infinite         */
+  SVO_BIT_BAD_TEMPERATURE = 16u /* temperature negative, NaN or infinite, or so
+                                   small that a verified row's maximum m gives
+                                   |m * fl(log2(e)/T)| >= 2^24 in float32       */
 };
 
 /* ---- counter-based random numbers ---------------------------------------- */

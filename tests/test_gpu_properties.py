@@ -125,6 +125,42 @@ def test_nan_temperature_and_inf_temperature():
     assert np.all(g["bits"] == sv.BIT_BAD_TEMPERATURE)
 
 
+@pytest.mark.parametrize("row_pass", ["team", "stream"])
+def test_temperature_domain_scaled_maximum(row_pass):
+    """Requests whose scaled row maximum |m * fl(log2(e)/T)| reaches 2^24
+    are invalid on both sides (the domain of the float32 row states); just
+    inside it the peaked rows verify bit for bit against the oracle, with
+    full-vocabulary rows and the team or streaming pass."""
+    rng = np.random.default_rng(44)
+    B, D, V = 6, 3, 151936
+    P = (3.0 * rng.standard_normal((B * (D + 1), V))).astype(np.float32)
+    Q = (P[np.arange(B * (D + 1)).reshape(B, D + 1)[:, :D].reshape(-1)]
+         + 0.5 * rng.standard_normal((B * D, V))).astype(np.float32)
+    peak = rng.integers(0, V, size=B)
+    for r in range(B):
+        P[r * (D + 1):(r + 1) * (D + 1), peak[r]] = 100.0
+        Q[r * D:(r + 1) * D, peak[r]] = 100.0
+    P[1 * (D + 1) + 3, 17] = 120.0      # r1: bonus row past 2^24 at T = 1e-5
+    Q[3 * D + 2, :] = -120.0            # r3: an all -120 draft row past it
+    temps = np.array([1e-5, 1e-5, 1e-5, 1e-5, 1e-37, 1e-37], np.float32)
+    P[5 * (D + 1):6 * (D + 1)] *= 1e-32   # r5: tiny logits stay inside at 1e-37
+    Q[5 * D:6 * D] *= 1e-32
+    tokens = np.repeat(peak[:, None], D, axis=1).astype(np.int32)
+    depth = np.full(B, D, np.int32)
+    tr0, dr0 = padded_offsets(B, D, DEV)
+    g = gpu_verify(to_dev(P, torch.float32), to_dev(Q, torch.float32), tr0, dr0,
+                   torch.from_numpy(tokens).to(DEV), torch.from_numpy(depth).to(DEV),
+                   torch.from_numpy(temps).to(DEV),
+                   flags=sv.SV_FLAG_STREAMING_ROW_PASS if row_pass == "stream" else 0)
+    o = oracle_verify(P, Q, tr0.cpu().numpy(), dr0.cpu().numpy(), tokens, depth, temps,
+                      np.arange(B), D_max=D)
+    compare(g, o, np.arange(B), temps, depth, check_flag_rate=False)
+    assert [int(b) & sv.BIT_BAD_TEMPERATURE for b in g["bits"]] == [
+        0, sv.BIT_BAD_TEMPERATURE, 0, sv.BIT_BAD_TEMPERATURE, sv.BIT_BAD_TEMPERATURE, 0]
+    for r in (0, 2, 5):
+        assert g["accepted_len"][r] == D
+
+
 def test_degenerate_shapes():
     # empty batch
     out = sv.verify(torch.zeros((1, 8), device=DEV), None, torch.zeros(0, dtype=torch.int64, device=DEV),

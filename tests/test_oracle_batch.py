@@ -182,6 +182,43 @@ def test_invalid_inputs_are_flagged(svo):
     assert np.all(res["out_tokens"] == -1)
 
 
+def test_temperature_domain_scaled_maximum(svo):
+    """T > 0 is in the verifier's domain while every verified row's maximum m
+    has |m * fl(log2(e)/T)| < 2^24 in float32.  Hand values: at T = 1e-5,
+    fl(log2(e)/T) = 144269.5..., so a row maximum of 100 scales to 1.4427e7
+    (valid) and 120 to 1.7312e7 (past 2^24 = 16777216); T = 1e-37 puts any
+    maximum above 1.2e-30 past it.  Greedy T = 0 has no such limit."""
+    import oracle
+    B, D, V = 6, 2, 16
+    P = np.zeros((B, D + 1, V), np.float32)
+    Q = np.zeros((B, D, V), np.float32)
+    P[:, :, 3] = 100.0
+    Q[:, :, 3] = 100.0
+    P[1, 2, 5] = 120.0          # r1: the bonus row's maximum scales past 2^24
+    Q[2, 1, 6] = -120.0         # r2: a draft row's minimum does not matter ...
+    Q[3, 1, :] = -120.0         # r3: ... but an all -120 draft row's maximum does
+    temps = np.array([1e-5, 1e-5, 1e-5, 1e-5, 1e-37, 1e-37], np.float32)
+    P[5] = 1e-31                # r5: maxima of 1e-31 stay inside at T = 1e-37
+    Q[5] = 1e-31
+    P[5, :, 3] = 2e-31
+    Q[5, :, 3] = 2e-31
+    tokens = np.full((B, D), 3, np.int32)
+    tr0 = np.arange(B, dtype=np.int64) * (D + 1)
+    dr0 = np.arange(B, dtype=np.int64) * D
+    res = svo.verify_batch(P.reshape(-1, V), Q.reshape(-1, V), tr0, dr0, tokens,
+                           np.full(B, D, np.int32), temps, D_max=D)
+    assert list(res["bits"]) == [0, oracle.BIT_BAD_TEMPERATURE, 0, oracle.BIT_BAD_TEMPERATURE,
+                                 oracle.BIT_BAD_TEMPERATURE, 0]
+    # inside the domain the peaked rows verify as the greedy chain would
+    for r in (0, 2, 5):
+        assert res["accepted_len"][r] == D and list(res["out_tokens"][r]) == [3] * (D + 1)
+    assert np.all(res["out_tokens"][[1, 3, 4]] == -1)
+    # the same rows at T = 0 are valid whatever their scale
+    res0 = svo.verify_batch(P.reshape(-1, V), Q.reshape(-1, V), tr0, dr0, tokens,
+                            np.full(B, D, np.int32), np.zeros(B, np.float32), D_max=D)
+    assert np.all(res0["bits"] == 0)
+
+
 # ---- composition with the Philox stream -----------------------------------
 
 def test_batch_uses_per_request_philox_stream(svo):
