@@ -77,29 +77,41 @@ __device__ float build_keys(const float* conf, int32_t B, int32_t D, const int32
   __syncthreads();
 
   // Prefix-confidence products, left to right in float32, one request per
-  // thread; each slot is read and then overwritten by the same thread.
+  // thread; each slot is read and then overwritten by the same thread, eight
+  // positions at a time (the eight reads issued together).
   int valid = 0;
   float total = 0.0f;
   for (int r = tid; r < B; r += kBudgetThreads) {
     int lim = max_depth ? max_depth[r] : D;
     lim = lim < 0 ? 0 : (lim > D ? D : lim);
     float sc = 1.0f;
-    for (int k = 0; k < D; ++k) {
-      const int idx = r * D + k;
-      if (k >= lim) {  // past this request's limit: key 0, never kept
-        S.keys[idx] = 0ull;
-        continue;
+    for (int k0 = 0; k0 < D; k0 += 8) {
+      float cv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        cv[j] = (k0 + j < lim) ? __uint_as_float((uint32_t)S.keys[r * D + k0 + j]) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = k0 + j;
+        if (k >= D) break;
+        const int idx = r * D + k;
+        if (k >= lim) {  // past this request's limit: key 0, never kept
+          S.keys[idx] = 0ull;
+          continue;
+        }
+        float c = cv[j];
+        if (!(c >= 0.0f)) c = 0.0f;  // NaN and negatives read as 0
+        if (c > 1.0f) c = 1.0f;
+        sc = sc * c;
+        total += sc;
+        S.keys[idx] = ((uint64_t)__float_as_uint(sc) << 32) | (uint64_t)(~(uint32_t)idx);
       }
-      float c = __uint_as_float((uint32_t)S.keys[idx]);
-      if (!(c >= 0.0f)) c = 0.0f;  // NaN and negatives read as 0
-      if (c > 1.0f) c = 1.0f;
-      sc = sc * c;
-      total += sc;
-      S.keys[idx] = ((uint64_t)__float_as_uint(sc) << 32) | (uint64_t)(~(uint32_t)idx);
     }
     valid += lim;
   }
-  atomicAdd(&S.s_valid, valid);
+  // one LDS atomic per wavefront (the wavefront's total), not per thread
+  for (int m = 1; m < kWave; m <<= 1) valid += __shfl_xor(valid, m);
+  if ((tid & (kWave - 1)) == 0 && valid) atomicAdd(&S.s_valid, valid);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kKeySlots; ++j) {
@@ -406,6 +418,7 @@ hipError_t launch_budget_ratio(const float* conf, int32_t B, int32_t D, const in
 // partials are then added in a fixed order.
 constexpr int kStatsThreads = 1024;
 constexpr int kStatsWaves = kStatsThreads / kWave;
+constexpr int kStatsBatch = 4;  // requests per wavefront whose loads are issued together
 
 __global__ __launch_bounds__(kStatsThreads) void k_accept_stats(
     const int32_t* depth, const float* alpha, const int32_t* accepted_len, int32_t B, int32_t D,
@@ -420,48 +433,53 @@ __global__ __launch_bounds__(kStatsThreads) void k_accept_stats(
   float tested = 0.0f, kept = 0.0f, asum = 0.0f;
   int32_t with_k = 0;
   float st = 0.0f, sn = 0.0f, se = 0.0f;  // lane 0 only
-  // A request's depth, accepted length and acceptance rates are loaded one
-  // request ahead (the rates of all D positions, whatever the depth).
-  auto load_req = [&](int r, int& n, int& tau, float& a) {
-    n = 0;
-    tau = 0;
-    a = 1.0f;
-    if (r < B) {
-      n = depth[r];
-      tau = accepted_len[r];
-      if (alpha && lane < D) a = alpha[(int64_t)r * D + lane];
-    }
-  };
-  int n_next, tau_next;
-  float a_next;
-  load_req(wave, n_next, tau_next, a_next);
-  for (int r = wave; r < B; r += kStatsWaves) {
-    int n = n_next;
-    const int tau = tau_next;
-    const float a_raw = a_next;
-    load_req(r + kStatsWaves, n_next, tau_next, a_next);
-    n = n < 0 ? 0 : (n > D ? D : n);
-    const bool in = lane < n;
-    const float a = (in && alpha) ? a_raw : 1.0f;
-    // inclusive prefix product over lanes (fixed Hillis-Steele order)
-    float pref = a;
+  // A wavefront's requests are taken kStatsBatch at a time, the depths,
+  // accepted lengths and acceptance rates (all D positions, whatever the
+  // depth) of the batch loaded at once.
+  for (int r0 = wave; r0 < B; r0 += kStatsWaves * kStatsBatch) {
+    int nb[kStatsBatch], taub[kStatsBatch];
+    float ab[kStatsBatch];
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const float o = __shfl_up(pref, d);
-      if (lane >= d) pref *= o;
+    for (int i = 0; i < kStatsBatch; ++i) {
+      const int r = r0 + i * kStatsWaves;
+      nb[i] = 0;
+      taub[i] = 0;
+      ab[i] = 1.0f;
+      if (r < B) {
+        nb[i] = depth[r];
+        taub[i] = accepted_len[r];
+        if (alpha && lane < D) ab[i] = alpha[(int64_t)r * D + lane];
+      }
     }
-    const float e = wave_sum((in && alpha) ? pref : 0.0f);
-    if (in) {
-      with_k += 1;
-      if (tau >= lane) tested += 1.0f;
-      if (tau > lane) kept += 1.0f;
-      if (alpha) asum += a;
-    }
-    if (lane == 0) {
-      if (expected_len) expected_len[r] = e;
-      st += (float)tau;
-      sn += (float)n;
-      se += e;
+#pragma unroll
+    for (int i = 0; i < kStatsBatch; ++i) {
+      const int r = r0 + i * kStatsWaves;
+      if (r >= B) break;  // uniform
+      int n = nb[i];
+      const int tau = taub[i];
+      n = n < 0 ? 0 : (n > D ? D : n);
+      const bool in = lane < n;
+      const float a = (in && alpha) ? ab[i] : 1.0f;
+      // inclusive prefix product over lanes (fixed Hillis-Steele order)
+      float pref = a;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const float o = __shfl_up(pref, d);
+        if (lane >= d) pref *= o;
+      }
+      const float e = wave_sum((in && alpha) ? pref : 0.0f);
+      if (in) {
+        with_k += 1;
+        if (tau >= lane) tested += 1.0f;
+        if (tau > lane) kept += 1.0f;
+        if (alpha) asum += a;
+      }
+      if (lane == 0) {
+        if (expected_len) expected_len[r] = e;
+        st += (float)tau;
+        sn += (float)n;
+        se += e;
+      }
     }
   }
   s_tested[wave][lane] = tested;
