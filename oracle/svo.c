@@ -526,7 +526,13 @@ int svo_fixed_depth_budget(const float* conf, int32_t B, int32_t D_max, int64_t 
 /* ------------------------------------------------------------------------- */
 /* Statistics: equation L_e2e (expected accepted length) and the MAL /
  * mean-acceptance figures of "The MTP path" (tradepoint.io page), whose
- * printed values satisfy MAL = 1 + D * mean acceptance. */
+ * printed values satisfy MAL = 1 + D * mean acceptance.  A request has at
+ * most D_max draft positions, so a depth outside [0, D_max] counts as the
+ * nearest end of that range. */
+static int32_t svo_clamp_depth(int32_t n, int32_t D_max) {
+  return n < 0 ? 0 : (n > D_max ? D_max : n);
+}
+
 int svo_accept_stats(const int32_t* depth, const double* alpha, const int32_t* accepted_len,
                      int32_t B, int32_t D_max, double* expected_len, double* per_depth,
                      double* summary) {
@@ -535,7 +541,7 @@ int svo_accept_stats(const int32_t* depth, const double* alpha, const int32_t* a
     for (int32_t i = 0; i < 3 * D_max; ++i) per_depth[i] = 0.0;
   double sum_tau = 0.0, sum_n = 0.0, sum_e = 0.0;
   for (int32_t r = 0; r < B; ++r) {
-    int32_t n = depth[r], tau = accepted_len[r];
+    int32_t n = svo_clamp_depth(depth[r], D_max), tau = accepted_len[r];
     double e = alpha ? svo_expected_accepted(alpha + (int64_t)r * D_max, n) : 0.0;
     if (expected_len) expected_len[r] = e;
     sum_e += e;
@@ -553,7 +559,7 @@ int svo_accept_stats(const int32_t* depth, const double* alpha, const int32_t* a
     for (int32_t k = 0; k < D_max; ++k) {
       int32_t with_k = 0;
       for (int32_t r = 0; r < B; ++r)
-        if (depth[r] > k) ++with_k;
+        if (svo_clamp_depth(depth[r], D_max) > k) ++with_k;
       per_depth[2 * D_max + k] = with_k ? per_depth[2 * D_max + k] / with_k : 0.0;
     }
   }
@@ -583,9 +589,7 @@ int svo_accept_accumulate(const int32_t* depth, const double* alpha, const int32
   if (B < 0 || D_max < 0 || !accum || (B > 0 && (!depth || !accepted_len)))
     return SVO_ERR_INVALID_ARGUMENT;
   for (int32_t r = 0; r < B; ++r) {
-    int32_t n = depth[r];
-    if (n < 0) n = 0;
-    if (n > D_max) n = D_max;
+    const int32_t n = svo_clamp_depth(depth[r], D_max);
     const int32_t tau = accepted_len[r];
     accum[0] += (double)(tau + 1);
     accum[1] += 1.0;

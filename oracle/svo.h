@@ -197,7 +197,8 @@ int svo_select_budget_ratio(const float* conf, int32_t B, int32_t D_max, const i
  * per_depth[k] = #requests that tested position k, per_depth[D_max + k] =
  * #requests that accepted position k, per_depth[2 D_max + k] = mean alpha at k
  * over requests with depth > k;
- * summary = (mean(tau + 1), 1 + mean expected_len, sum tau / sum n, sum n). */
+ * summary = (mean(tau + 1), 1 + mean expected_len, sum tau / sum n, sum n);
+ * n_r = depth[r] clamped to [0, D_max]. */
 int svo_accept_stats(const int32_t* depth, const double* alpha, const int32_t* accepted_len,
                      int32_t B, int32_t D_max, double* expected_len, double* per_depth,
                      double* summary);

@@ -328,3 +328,22 @@ def test_accept_stats_definitions(svo):
     assert s[1] == pytest.approx(1 + (0.875 + 1.5 + 0.3) / 4)
     assert s[2] == pytest.approx(4 / 7)
     assert s[3] == 7
+
+
+def test_accept_stats_clamps_depth(svo):
+    """A depth outside [0, D_max] counts as the nearest end: the request with
+    depth 5 at D_max = 3 has three positions (its prefix products stop at the
+    row's end), the one with depth -2 has none; nothing past a row is read."""
+    depth = np.array([5, -2, 2], np.int32)
+    tau = np.array([0, 0, 2], np.int32)
+    alpha = np.array([[0.5, 0.5, 0.5], [0.9, 0.9, 0.9], [1.0, 0.25, 0.7]])
+    st = svo.accept_stats(depth, alpha, tau, 3)
+    assert list(st["expected_len"]) == pytest.approx([0.875, 0.0, 1.25])
+    assert list(st["per_depth"][0]) == [2, 1, 0]   # tested at k (tau >= k)
+    assert list(st["per_depth"][1]) == [1, 1, 0]   # kept at k (tau > k)
+    assert list(st["per_depth"][2]) == pytest.approx([0.75, 0.375, 0.5])
+    s = st["summary"]
+    assert s[0] == pytest.approx(1 + 2 / 3)
+    assert s[1] == pytest.approx(1 + (0.875 + 1.25) / 3)
+    assert s[2] == pytest.approx(2 / 5)
+    assert s[3] == 5
