@@ -4,8 +4,9 @@ roofline of the dominant kernel and the CPU oracle timed beside it.
 
 One step = the whole hot path on one batch already resident in HBM:
   sv_allocate_budget (prefix-confidence products + radix select of the top K)
-  -> sv_verify_batch (row statistics, acceptance rates, accept scan, draw)
-  -> sv_accept_stats.
+  -> sv_verify_batch (row statistics, acceptance rates, accept scan, draw,
+     and the batch's acceptance statistics, the outputs of sv_accept_stats,
+     from one spare workgroup of its last kernel).
 Default workload: the 64 x 16 x 151936 bf16 batch at T = 1 with the budget
 keeping every position (K = 1024).  Inputs are synthetic (seeded Gaussian
 logits shaped like the AngelSpec pages' block-drafting workload).  Four input
@@ -380,7 +381,7 @@ def main():
     row_kernel = "k_rowpass" if args.row_pass == "stream" else "k_rowteam"
     verifiers = []
     for tgt, dft in copies:
-        v = sv.Verifier(B, D, V, dev, alpha=True, diag=True)
+        v = sv.Verifier(B, D, V, dev, alpha=True, diag=True, stats=True)
         v.prepare(tgt, dft, bud["target_row0"], dr0, w.draft_tokens, bud["depth"], w.temperature,
                   seed=0, step=0, flags=row_flags)
         verifiers.append(v)
@@ -400,8 +401,7 @@ def main():
     def step(v):
         nonlocal stats_out
         sv.allocate_budget(conf, K, out=bud)
-        out = v.run()
-        stats_out = sv.accept_stats(bud["depth"], out.alpha, out.accepted_len, D)
+        stats_out = v.run().stats  # the batch statistics come with the verification
 
     for i in range(args.warmup):
         step(verifiers[i % len(verifiers)])

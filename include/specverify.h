@@ -228,6 +228,15 @@ typedef struct sv_verify_args {
    * and acceptance rates), [3] after the accept scan, [4] after the draw.
    * An entry may be NULL (not recorded).  For timing only. */
   void* const* stage_events;
+  /* Acceptance statistics of this batch, each optional (NULL: not written):
+   * exactly what sv_accept_stats(depth, alpha, accepted_len, B, D_max,
+   * stats_expected_len, stats_per_depth, stats_summary) would write after
+   * the call returns, the same bits, without a launch of their own (one
+   * extra workgroup of the last verification kernel computes them).  Sizes
+   * [B], [3 * D_max] and [4] floats on the device; see sv_accept_stats. */
+  float* stats_expected_len;
+  float* stats_per_depth;
+  float* stats_summary;
 } sv_verify_args;
 
 /* ---------------------------------------------------------------------------
@@ -297,7 +306,8 @@ sv_status sv_verify_batch_noalloc(const sv_verify_args* args, void* stream);
  * MAL / mean-acceptance figures of the tradepoint.io page, "The MTP path",
  * which satisfy MAL = 1 + D * mean acceptance).
  *
- * Inputs (device): depth[B], alpha[B, D_max] (may be NULL), accepted_len[B].
+ * Inputs (device): depth[B] (n_r, clamped to [0, D_max]), alpha[B, D_max]
+ * (may be NULL), accepted_len[B].
  * Outputs (device float, each optional):
  *   expected_len[B]    E[tau_r] = sum_{m < n_r} prod_{k <= m} alpha[r][k]
  *   per_depth[3*D_max] #requests that tested position k, #that kept it,

@@ -157,6 +157,9 @@ sv_status run_verify(const sv_verify_args* a, int32_t nshard, int64_t shard_w,
   p.num_out = a->num_out;
   p.alpha = a->alpha;
   p.diag = a->diag;
+  p.stats_expected_len = a->stats_expected_len;
+  p.stats_per_depth = a->stats_per_depth;
+  p.stats_summary = a->stats_summary;
   p.events = a->stage_events;
   const sv::WorkspaceLayout L = sv::workspace_layout(p.B, p.D, p.V);
   char* ws = static_cast<char*>(a->workspace);

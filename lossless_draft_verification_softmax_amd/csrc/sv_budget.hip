@@ -15,6 +15,7 @@
 #include "specverify.h"
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
+#include "sv_stats.hpp"
 
 namespace sv {
 
@@ -409,114 +410,17 @@ hipError_t launch_budget_ratio(const float* conf, int32_t B, int32_t D, const in
 }
 
 // ---------------------------------------------------------------------------
-// Acceptance statistics (equation L_e2e of "AngelSpec: specialize the
-// drafter...", section "MTP"; MAL and mean acceptance of the tradepoint.io
-// page, "The MTP path").  One workgroup of 16 wavefronts; wavefront w takes
-// requests w, w + 16, ...: lane k holds position k (D_max <= 64), a
-// wavefront prefix product gives prod_{j<=k} alpha_j and a wavefront sum
-// gives E[tau_r].  Per-depth counters stay in the lanes; the 16 wavefront
-// partials are then added in a fixed order.
+// Acceptance statistics of one batch (sv_stats.hpp): one workgroup of 16
+// wavefronts, four requests of each wavefront loaded together.
 constexpr int kStatsThreads = 1024;
 constexpr int kStatsWaves = kStatsThreads / kWave;
-constexpr int kStatsBatch = 4;  // requests per wavefront whose loads are issued together
 
 __global__ __launch_bounds__(kStatsThreads) void k_accept_stats(
     const int32_t* depth, const float* alpha, const int32_t* accepted_len, int32_t B, int32_t D,
     float* expected_len, float* per_depth, float* summary) {
-  __shared__ float s_tested[kStatsWaves][kWave];
-  __shared__ float s_kept[kStatsWaves][kWave];
-  __shared__ float s_asum[kStatsWaves][kWave];
-  __shared__ int32_t s_with[kStatsWaves][kWave];
-  __shared__ float s_sum[kStatsWaves][3];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  float tested = 0.0f, kept = 0.0f, asum = 0.0f;
-  int32_t with_k = 0;
-  float st = 0.0f, sn = 0.0f, se = 0.0f;  // lane 0 only
-  // A wavefront's requests are taken kStatsBatch at a time, the depths,
-  // accepted lengths and acceptance rates (all D positions, whatever the
-  // depth) of the batch loaded at once.
-  for (int r0 = wave; r0 < B; r0 += kStatsWaves * kStatsBatch) {
-    int nb[kStatsBatch], taub[kStatsBatch];
-    float ab[kStatsBatch];
-#pragma unroll
-    for (int i = 0; i < kStatsBatch; ++i) {
-      const int r = r0 + i * kStatsWaves;
-      nb[i] = 0;
-      taub[i] = 0;
-      ab[i] = 1.0f;
-      if (r < B) {
-        nb[i] = depth[r];
-        taub[i] = accepted_len[r];
-        if (alpha && lane < D) ab[i] = alpha[(int64_t)r * D + lane];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kStatsBatch; ++i) {
-      const int r = r0 + i * kStatsWaves;
-      if (r >= B) break;  // uniform
-      int n = nb[i];
-      const int tau = taub[i];
-      n = n < 0 ? 0 : (n > D ? D : n);
-      const bool in = lane < n;
-      const float a = (in && alpha) ? ab[i] : 1.0f;
-      // inclusive prefix product over lanes (fixed Hillis-Steele order)
-      float pref = a;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const float o = __shfl_up(pref, d);
-        if (lane >= d) pref *= o;
-      }
-      const float e = wave_sum((in && alpha) ? pref : 0.0f);
-      if (in) {
-        with_k += 1;
-        if (tau >= lane) tested += 1.0f;
-        if (tau > lane) kept += 1.0f;
-        if (alpha) asum += a;
-      }
-      if (lane == 0) {
-        if (expected_len) expected_len[r] = e;
-        st += (float)tau;
-        sn += (float)n;
-        se += e;
-      }
-    }
-  }
-  s_tested[wave][lane] = tested;
-  s_kept[wave][lane] = kept;
-  s_asum[wave][lane] = asum;
-  s_with[wave][lane] = with_k;
-  if (lane == 0) {
-    s_sum[wave][0] = st;
-    s_sum[wave][1] = sn;
-    s_sum[wave][2] = se;
-  }
-  __syncthreads();
-  if (per_depth && wave == 0 && lane < D) {
-    float t = 0.0f, k = 0.0f, a = 0.0f;
-    int32_t w = 0;
-    for (int v = 0; v < kStatsWaves; ++v) {
-      t += s_tested[v][lane];
-      k += s_kept[v][lane];
-      a += s_asum[v][lane];
-      w += s_with[v][lane];
-    }
-    per_depth[lane] = t;
-    per_depth[D + lane] = k;
-    per_depth[2 * D + lane] = w ? a / (float)w : 0.0f;
-  }
-  if (summary && threadIdx.x == 0) {
-    float t = 0.0f, n = 0.0f, e = 0.0f;
-    for (int v = 0; v < kStatsWaves; ++v) {
-      t += s_sum[v][0];
-      n += s_sum[v][1];
-      e += s_sum[v][2];
-    }
-    summary[0] = B ? 1.0f + t / (float)B : 0.0f;
-    summary[1] = B ? 1.0f + e / (float)B : 0.0f;
-    summary[2] = n > 0.0f ? t / n : 0.0f;
-    summary[3] = n;
-  }
+  __shared__ StatsLds S;
+  accept_stats_block<kStatsWaves, 4>(depth, alpha, accepted_len, B, D, expected_len, per_depth,
+                                     summary, S);
 }
 
 // Statistics over many verified batches (the decode loop's steps; MAL,

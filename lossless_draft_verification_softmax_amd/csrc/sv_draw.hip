@@ -11,7 +11,9 @@
 //                   normaliser partials and the one-pass split of the tile
 //                   residual masses
 //   k_draw_pick64   one workgroup per queued draw: tile masses from the
-//                   partials, the crossing tile and the scan inside it
+//                   partials, the crossing tile and the scan inside it;
+//                   one more workgroup, when asked for, writes the batch's
+//                   acceptance statistics (sv_stats.hpp)
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -22,6 +24,7 @@
 #include "sv_drawrow.hpp"
 #include "sv_exp64.hpp"
 #include "sv_shard.hpp"
+#include "sv_stats.hpp"
 
 namespace sv {
 
@@ -290,7 +293,7 @@ __device__ InTile scan_in_tile(const double (&w)[kPer], int64_t i0, double c0, d
 constexpr double kTau64 = 1e-4;
 
 struct Draw64Lds {
-  double tab[kExp64Table];  // 2^(j/64) for exp64_tab
+  double tab[kExp64Table];  // 2^(j/256) for exp64_tab
   double red[kDrawThreads / kWave][5];
   int32_t redu[kDrawThreads / kWave];
   double z2[kDrawThreads / kWave][2];
@@ -636,22 +639,35 @@ __global__ __launch_bounds__(kDrawThreads, kTileBlocksPerCu) void k_draw_tile64(
   }
 }
 
-// Pick: workgroup j draws queue entry j.
+// Pick: workgroup j < B draws queue entry j.  Workgroup B, launched only
+// when the caller asked for them, writes the batch's acceptance statistics
+// (accepted lengths and rates are final once k_accept_draw has run).
 template <typename E, bool SH>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
-  __shared__ Draw64Lds L;
+  __shared__ union {
+    Draw64Lds d;
+    StatsLds s;
+  } L;
   const int slot = blockIdx.x;
+  if (slot >= p.B) {
+    accept_stats_block<kDrawThreads / kWave, 4>(p.depth, p.alpha, p.accepted_len, p.B, p.D,
+                                                p.stats_expected_len, p.stats_per_depth,
+                                                p.stats_summary, L.s);
+    return;
+  }
   const DrawJob jb = p.fb_jobs[slot];
   if (slot >= *p.fb_count) return;
-  load_exp_table(L);
-  pick64<E, SH>(p, jb, slot, L);
+  load_exp_table(L.d);
+  pick64<E, SH>(p, jb, slot, L.d);
 }
 
 template <typename E, bool SH>
 static void launch_draw_t(const VerifyParams& p, int cus, hipStream_t stream) {
   hipLaunchKernelGGL((k_draw_tile64<E, SH>), dim3(cus * kTileBlocksPerCu), dim3(kDrawThreads), 0,
                      stream, p);
-  hipLaunchKernelGGL((k_draw_pick64<E, SH>), dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
+  const bool stats = p.stats_expected_len || p.stats_per_depth || p.stats_summary;
+  hipLaunchKernelGGL((k_draw_pick64<E, SH>), dim3((unsigned)p.B + (stats ? 1u : 0u)),
+                     dim3(kDrawThreads), 0, stream, p);
 }
 
 void launch_draw(const VerifyParams& p, int cus, hipStream_t stream) {

@@ -103,6 +103,11 @@ struct VerifyParams {
   int32_t* num_out;
   float* alpha;
   sv_diag* diag;
+  // acceptance statistics of the batch (sv_accept_stats outputs), each
+  // optional; computed by one extra workgroup of k_draw_pick64
+  float* stats_expected_len;  // [B]
+  float* stats_per_depth;     // [3 D]
+  float* stats_summary;       // [4]
   void* const* events;     // SV_NUM_STAGE_EVENTS hipEvent_t or null
   // workspace
   float2* part_p;    // [U][S1]  (max, sum) or (max, arg max bits) at T = 0

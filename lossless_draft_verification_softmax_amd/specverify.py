@@ -69,7 +69,8 @@ class SvVerifyArgs(ctypes.Structure):
         ("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
         ("num_out", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("diag", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-        ("stage_events", ctypes.c_void_p),
+        ("stage_events", ctypes.c_void_p), ("stats_expected_len", ctypes.c_void_p),
+        ("stats_per_depth", ctypes.c_void_p), ("stats_summary", ctypes.c_void_p),
     ]
 
 
@@ -323,6 +324,8 @@ class VerifyOutputs:
     num_out: torch.Tensor
     alpha: torch.Tensor | None
     diag: torch.Tensor | None  # (B, 4) int32 view of sv_diag: margins as float bits, bits
+    # acceptance statistics of the batch, as accept_stats returns them, or None
+    stats: dict | None = None
 
     def margins(self):
         d = self.diag.view(torch.float32)
@@ -337,7 +340,10 @@ class Verifier:
     for repeated verification of batches with the same shapes."""
 
     def __init__(self, B: int, D_max: int, V: int, device, alpha: bool = True,
-                 diag: bool = True):
+                 diag: bool = True, stats: bool = False):
+        """stats=True asks the call for the batch's acceptance statistics
+        (the stats_* outputs of sv_verify_args, the bits of accept_stats on
+        the call's depth, alpha and accepted lengths) in out.stats."""
         self.B, self.D_max, self.V = B, D_max, V
         self.device = torch.device(device)
         dev = self.device
@@ -346,7 +352,11 @@ class Verifier:
             out_tokens=torch.empty((B, D_max + 1), dtype=torch.int32, device=dev),
             num_out=torch.empty(B, dtype=torch.int32, device=dev),
             alpha=torch.empty((B, D_max), dtype=torch.float32, device=dev) if alpha else None,
-            diag=torch.empty((B, 4), dtype=torch.int32, device=dev) if diag else None)
+            diag=torch.empty((B, 4), dtype=torch.int32, device=dev) if diag else None,
+            stats=dict(expected_len=torch.empty(B, dtype=torch.float32, device=dev),
+                       per_depth=torch.empty(3 * max(D_max, 1), dtype=torch.float32, device=dev),
+                       summary=torch.empty(4, dtype=torch.float32, device=dev))
+            if stats else None)
         self.ws_bytes = workspace_bytes(B, D_max, V)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.args = SvVerifyArgs()
@@ -386,6 +396,12 @@ class Verifier:
         a.num_out = o.num_out.data_ptr()
         a.alpha = _ptr(o.alpha) if o.alpha is not None and o.alpha.numel() else None
         a.diag = _ptr(o.diag)
+        if o.stats is not None:
+            a.stats_expected_len = _ptr(o.stats["expected_len"])
+            a.stats_per_depth = _ptr(o.stats["per_depth"])
+            a.stats_summary = _ptr(o.stats["summary"])
+        else:
+            a.stats_expected_len = a.stats_per_depth = a.stats_summary = None
         a.workspace = self.workspace.data_ptr()
         a.workspace_bytes = self.workspace.numel()
         self._keep = [target, draft, target_row0, draft_row0, draft_tokens, depth, temperature,

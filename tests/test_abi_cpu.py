@@ -231,3 +231,30 @@ def test_noalloc_and_stream_read_validation_codes(sv):
     assert lib.sv_stream_read(fake, 1024, 33, sink, None) == sv.SV_ERR_INVALID_ARGUMENT
     assert lib.sv_stream_read(fake, 1024, 4, None, None) == sv.SV_ERR_INVALID_ARGUMENT
     assert lib.sv_stream_read(fake, 0, 4, sink, None) == sv.SV_OK
+
+
+def _c_layout(struct, fields):
+    """sizeof and offsetof of a header struct, from a C program built with gcc."""
+    import subprocess
+    import tempfile
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "specverify.h"',
+             'int main(void) {', f'  printf("%zu\\n", sizeof({struct}));']
+    lines += [f'  printf("%zu\\n", offsetof({struct}, {f}));' for f in fields]
+    lines += ['  return 0;', '}']
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        open(src, "w").write("\n".join(lines) + "\n")
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), src, "-o", exe],
+                       check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()
+    return [int(x) for x in out]
+
+
+@pytest.mark.parametrize("name", ["SvVerifyArgs", "SvDiag"])
+def test_binding_struct_layout_matches_header(sv, name):
+    cls = getattr(sv, name)
+    struct = {"SvVerifyArgs": "sv_verify_args", "SvDiag": "sv_diag"}[name]
+    fields = [f[0] for f in cls._fields_]
+    c = _c_layout(struct, fields)
+    assert c[0] == ctypes.sizeof(cls)
+    assert c[1:] == [getattr(cls, f).offset for f in fields]

@@ -283,6 +283,102 @@ def test_accept_stats_match_oracle():
         assert np.allclose(g["summary"].cpu().numpy(), o["summary"], rtol=1e-5)
 
 
+STATS_CASES = {  # B, D, V, dtype, options
+    "tiny": (1, 1, 7, torch.float32, {}),
+    "ragged": (37, 5, 1001, torch.bfloat16, {}),
+    "wide": (300, 3, 512, torch.float32, {}),
+    "depth0": (5, 0, 64, torch.bfloat16, {}),
+    "deep": (20, 64, 200, torch.float32, {}),
+    "no_alpha": (37, 5, 1001, torch.bfloat16, {"alpha": False}),
+    "invalid": (24, 6, 333, torch.float32, {"invalid": True}),
+    "stream": (37, 5, 1001, torch.bfloat16, {"flags": sv.SV_FLAG_STREAMING_ROW_PASS}),
+    "noalloc": (37, 5, 1001, torch.bfloat16, {"noalloc": True}),
+    "sharded": (19, 4, 3000, torch.bfloat16, {"shard": 1024}),
+}
+
+
+def _stats_inputs(case):
+    B, D, V, dtype, opt = STATS_CASES[case]
+    rng = np.random.default_rng(sum(map(ord, case)))
+    vec = 8 if dtype == torch.bfloat16 else 4
+    stride = (V + vec - 1) // vec * vec + vec
+    temps = rng.choice(np.array([0.0, 0.6, 1.0], np.float32), size=B)
+    P, Q, tokens = random_batch(rng, B, D, V, stride, dtype, temps)
+    depth = rng.integers(0, D + 1, size=B).astype(np.int32)
+    if opt.get("invalid"):
+        temps[1] = np.nan     # invalid temperature
+        depth[2] = D + 3      # depth beyond D_max
+        depth[3] = -1
+        tokens[4, 0] = V + 5  # token out of range
+    return B, D, V, dtype, opt, P, Q, tokens, depth, temps
+
+
+@pytest.mark.parametrize("case", list(STATS_CASES))
+def test_verify_stats_outputs_equal_accept_stats(case):
+    """The statistics a verification call leaves in its stats_* outputs are
+    the bits sv_accept_stats writes afterwards on the call's own depths,
+    acceptance rates and accepted lengths (and agree with the oracle's
+    statistics of the same inputs)."""
+    B, D, V, dtype, opt, P, Q, tokens, depth, temps = _stats_inputs(case)
+    Pd, Qd = to_dev(P, dtype), to_dev(Q, dtype)
+    tr0, dr0 = padded_offsets(B, D, DEV)
+    tok = torch.from_numpy(tokens).to(DEV).reshape(B, D)
+    dep = torch.from_numpy(depth).to(DEV)
+    T = torch.from_numpy(temps).to(DEV)
+    v = sv.Verifier(B, D, V, DEV, alpha=opt.get("alpha", True), stats=True)
+    if "shard" in opt:
+        W = opt["shard"]
+
+        def shard(rows):  # buffers of W columns at stride W, the last one narrower
+            out = []
+            for c in range(0, V, W):
+                buf = torch.full((rows.shape[0], W), float("nan"), dtype=dtype, device=DEV)
+                part = rows[:, c:min(c + W, V)]
+                buf[:, :part.shape[1]] = part
+                out.append(buf)
+            return out
+
+        v.prepare_sharded(shard(Pd), shard(Qd), W, tr0, dr0, tok, dep, T, seed=5, step=2)
+    else:
+        v.prepare(Pd, Qd, tr0, dr0, tok, dep, T, seed=5, step=2, flags=opt.get("flags", 0))
+    for s in v.out.stats.values():
+        s.fill_(float("nan"))
+    out = v.run(noalloc=opt.get("noalloc", False))
+    ref = sv.accept_stats(dep, out.alpha, out.accepted_len, D)
+    torch.cuda.synchronize()
+    n = 3 * D
+    assert torch.equal(out.stats["expected_len"], ref["expected_len"])
+    assert torch.equal(out.stats["per_depth"][:n], ref["per_depth"][:n])
+    assert torch.equal(out.stats["summary"], ref["summary"])
+    if opt.get("invalid"):
+        assert np.all(out.accepted_len.cpu().numpy()[1:5] == 0)
+    alpha = out.alpha.cpu().numpy().astype(np.float64) if out.alpha is not None else None
+    o = oracle.accept_stats(depth, alpha, out.accepted_len.cpu().numpy(), D)
+    g = {k: t.cpu().numpy() for k, t in out.stats.items()}
+    assert np.allclose(g["expected_len"], o["expected_len"], rtol=1e-5, atol=1e-6)
+    assert np.allclose(g["per_depth"][:n].reshape(3, D), o["per_depth"], rtol=1e-5, atol=1e-6)
+    assert np.allclose(g["summary"], o["summary"], rtol=1e-5)
+
+
+@pytest.mark.parametrize("name", ["c4full", "c5"])
+def test_verify_stats_outputs_full_batch(name):
+    """The same at the two full batch sizes (64 x 16 at V = 151936 bf16 and
+    V = 262144 fp32, mixed temperatures on the second), depths from the
+    budget as the verification step uses them."""
+    w = synth.make(name, device=DEV)
+    B, D, V = w.B, w.D, w.V
+    bud = sv.allocate_budget(w.conf.to(DEV), w.K)
+    v = sv.Verifier(B, D, V, DEV, stats=True)
+    v.prepare(w.target.reshape(B * (D + 1), V), w.draft.reshape(B * D, V),
+              bud["target_row0"], bud["draft_row0"], w.draft_tokens, bud["depth"],
+              w.temperature, seed=11, step=1)
+    out = v.run()
+    ref = sv.accept_stats(bud["depth"], out.alpha, out.accepted_len, D)
+    torch.cuda.synchronize()
+    for k in ("expected_len", "per_depth", "summary"):
+        assert torch.equal(out.stats[k], ref[k]), k
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("row_pass", ["team", "stream"])
 def test_extreme_logit_ranges(dtype, row_pass):
