@@ -348,15 +348,25 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
     float carry = L.c0;
     const int64_t lo = (int64_t)j * slen;
     const int64_t hi = min(p.V, lo + slen);
+    // Each round's raw logits are loaded one round ahead, and the barriers
+    // inside the loop order LDS only, so the next round's loads stay in
+    // flight while this round is scanned.
+    Raw8<E> cur, nxt;
+    if (lo + (int64_t)k * kPer < hi)
+      load_raw8<E, SH>(wt.prow, wt.qrow, wt.has_q, lo + (int64_t)k * kPer, hi, cur);
     for (int64_t base = lo; base < hi; base += kChunk) {
       const int64_t i0 = base + (int64_t)k * kPer;
+      if (i0 + kChunk < hi) load_raw8<E, SH>(wt.prow, wt.qrow, wt.has_q, i0 + kChunk, hi, nxt);
       float w[kPer];
       if (i0 < hi) {
-        wt(i0, hi, w);
+        float a[kPer], b[kPer];
+        unpack_raw8<E, SH>(cur, wt.prow, wt.qrow, wt.has_q, i0, hi, a, b);
+        wt.from(a, b, w);
       } else {
 #pragma unroll
         for (int e = 0; e < kPer; ++e) w[e] = 0.0f;
       }
+      cur = nxt;
       float run = 0.0f;
 #pragma unroll
       for (int e = 0; e < kPer; ++e) run += w[e];
@@ -369,7 +379,7 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
         if (lane >= dd) incl += o;
       }
       if (lane == kWave - 1) L.wtot[wave] = incl;
-      __syncthreads();
+      lds_barrier();
       float wbase = 0.0f, total = 0.0f;
       for (int v = 0; v < kAcceptDrawWaves; ++v) {
         const float x = L.wtot[v];
@@ -393,7 +403,7 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
       }
       const uint64_t hit = __ballot(first >= 0);
       if (lane == 0) L.wfirst[wave] = hit ? (int)__builtin_ctzll(hit) : -1;
-      __syncthreads();
+      lds_barrier();
       int winner = -1;
       for (int v = 0; v < kAcceptDrawWaves; ++v)
         if (L.wfirst[v] >= 0) {
@@ -406,12 +416,12 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
           L.before = bprev;
           L.at = bat;
         }
-        __syncthreads();
+        lds_barrier();
         found = true;
         break;
       }
       carry += total;
-      __syncthreads();  // wtot / wfirst reused by the next round
+      lds_barrier();  // wtot / wfirst reused by the next round
     }
   }
   if (k == 0) {
