@@ -21,10 +21,12 @@
 // its own partial slot.
 //
 // Workgroup layout: waves 0..14 are data waves, wave 15 is the communication
-// wave.  The data waves only load rows and reduce them to per-wave states
-// in LDS; the communication wave combines those states, writes the partial
-// slots, publishes to the team, waits for the team and hands the row
-// normalisers back through LDS.  Loads complete in order per wave, so any
+// wave.  The data waves load rows and reduce them to per-wave states in LDS;
+// the last of them to finish a row pair's first pass combines the states,
+// writes the partial slots and publishes the pair to the team.  The
+// communication wave waits for the team (its polls queue behind no stores
+// of its own) and hands the row normalisers back through LDS; it also
+// combines single rows' states.  Loads complete in order per wave, so any
 // wave that waited on a fresh global load (a poll) would also wait for all
 // of its earlier row loads; keeping polls out of the data waves keeps their
 // prefetches in flight.  For the same reason every data wave issues exactly
@@ -46,9 +48,10 @@
 // Team exchange: member m publishes its slice states of its n-th row pair as
 // four 64-bit words (value bits | (n + 1) << 32) in ring slot n mod 4; a
 // reader accepts a word only if its tag is n + 1, so no fences are needed.
-// A member publishes n only after it has read every member's n - 1, which
-// every member published only after reading all of n - 2, so by then every
-// reader is done with n - 4, the previous user of the ring slot.  The words
+// A member publishes n at the end of its data step n, after its barrier
+// n - 1, so after its communication wave has read every member's n - 2;
+// each of those was published after that member's barrier n - 3, by when
+// that member had read n - 4, the previous user of the ring slot.  The words
 // are cleared before each launch.  The wait is bounded.  A team needs all of
 // its members resident at once, which holds when the kernel has the device to
 // itself (one workgroup per CU); when other work holds CUs a member may not
@@ -166,6 +169,7 @@ struct TeamLds {
   float ep[2];                       // 2^-lz of the target row
   float rq[2];                       // 2^(lz_p - lz_q)
   int ok[2];
+  int arrived[2];                    // data waves done with a row pair's first pass
 };
 
 // Work items are read-only here and uniform across the workgroup: read them
@@ -458,6 +462,42 @@ __device__ __forceinline__ void single_first(const VerifyParams& p, const Slice&
   if (lane == 0) L.sm[b][wave][slot] = sp;
 }
 
+// The member's slice state of row pair u from the data waves' states (a
+// fixed reduction tree over the lanes; `sum` is reduced alongside), into its
+// partial slots, and its publication to the team: four 64-bit words (value
+// bits | (ordinal + 1) << 32) in ring slot ordinal mod 4.  Run by the
+// communication wave after the step's barrier, or (kDataPublish) by the last
+// data wave to finish the pair's first pass.
+__device__ __forceinline__ void publish_pair(const VerifyParams& p, const UnitDesc& u,
+                                             const TeamLds& L, int b, int team, int member,
+                                             float& sum) {
+  // The lane index is taken afresh here (mbcnt, in a volatile asm the
+  // compiler cannot hoist): the data waves' registers are full, and a
+  // long-lived copy would be spilled and its reload would wait for every row
+  // load in flight.
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const float sl = u.sl;
+  SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
+  if (lane < kDataWaves) {
+    sp = L.sm[b][lane][0];
+    sq = L.sm[b][lane][1];
+  }
+  wave_merge_ref2(sp, sq, true, sum, sl);
+  const int64_t slot = unit_slot(p, u, member);
+  if (lane == 0) {
+    p.part_p[slot] = make_float2(sp.m, sp.z);
+    p.part_q[slot] = make_float2(sq.m, sq.z);
+  }
+  if (lane < 4) {
+    const float v = lane == 0 ? sp.m : lane == 1 ? sp.z : lane == 2 ? sq.m : sq.z;
+    const uint64_t tag = (uint64_t)(uint32_t)(u.ordinal + 1) << 32;
+    const int64_t rec = ((int64_t)team * 4 + (u.ordinal & 3)) * p.team + member;
+    __hip_atomic_store(&p.team_xch[rec * 4 + lane], tag | (uint64_t)__float_as_uint(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // First pass of a unit over this thread's vectors: for a row pair the slice
 // (max, sum) of p and q, keeping the exponentials; for a single unit each of
 // its rows by single_first (the second row's temperature is read from its
@@ -505,6 +545,23 @@ __device__ __forceinline__ void first_pass_data(const VerifyParams& p, const Uni
   if (lane == 0) {
     L.sm[b][wave][0] = sp;
     L.sm[b][wave][1] = sq;
+  }
+}
+
+// After a row pair's first pass: the last data wave to arrive publishes the
+// pair (the fetch-add orders every wave's states before it) and resets the
+// counter, which is next used two steps later, after a barrier.
+__device__ __forceinline__ void arrive_pair(const VerifyParams& p, const UnitDesc& u, TeamLds& L,
+                                            int b, int team, int member) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int order = 0;
+  if (lane == 0)
+    order = __hip_atomic_fetch_add(&L.arrived[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  order = __builtin_amdgcn_readfirstlane(order);
+  if (order == kDataWaves - 1) {
+    float none = 0.0f;
+    publish_pair(p, u, L, b, team, member, none);
+    if (lane == 0) L.arrived[b] = 0;
   }
 }
 
@@ -612,7 +669,10 @@ __device__ __forceinline__ void comm_single_argmax(const VerifyParams& p, const 
 }
 
 // Combines the data waves' first-pass states of a unit (a fixed reduction
-// tree over the lanes), writes the partial slots and publishes a pair.
+// tree over the lanes) into the partial slots and publishes a row pair (DP:
+// the last data wave has done that already), with the second-pass sums of
+// unit ua reduced alongside.
+template <bool DP>
 __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const UnitDesc& u,
                                                 const SecondRow& u2, const TeamLds& L, int b,
                                                 int team, int member, const UnitDesc& ua, int ba) {
@@ -639,26 +699,14 @@ __device__ __forceinline__ void first_pass_comm(const VerifyParams& p, const Uni
     }
     return;
   }
-  const int64_t slot = unit_slot(p, u, member);
-  const float sl = u.sl;
-  SoftmaxPart sp{-INFINITY, 0.0f}, sq{-INFINITY, 0.0f};
-  if (lane < kDataWaves) {
-    sp = L.sm[b][lane][0];
-    sq = L.sm[b][lane][1];
+  if constexpr (DP) {
+    // a row pair: merged and published by the last data wave; only the
+    // second-pass sums of unit ua remain
+    if (fin) acc = wave_sum(acc);
+  } else {
+    publish_pair(p, u, L, b, team, member, acc);
   }
-  wave_merge_ref2(sp, sq, true, acc, sl);
-  if (lane == 0) {
-    p.part_p[slot] = make_float2(sp.m, sp.z);
-    p.part_q[slot] = make_float2(sq.m, sq.z);
-    if (fin) p.part_a[unit_slot(p, ua, member)] = acc;
-  }
-  if (wants_alpha(p, u) && lane < 4) {
-    const float v = lane == 0 ? sp.m : lane == 1 ? sp.z : lane == 2 ? sq.m : sq.z;
-    const uint64_t tag = (uint64_t)(uint32_t)(u.ordinal + 1) << 32;
-    const int64_t rec = ((int64_t)team * 4 + (u.ordinal & 3)) * p.team + member;
-    __hip_atomic_store(&p.team_xch[rec * 4 + lane], tag | (uint64_t)__float_as_uint(v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (fin && lane == 0) p.part_a[unit_slot(p, ua, member)] = acc;
 }
 
 // Loads of one member's exchange record (lane m < T reads member m's record
@@ -823,6 +871,20 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
   constexpr int PS = SH ? 1 : 2;  // single rows per unit
   const int64_t n = my_pairs + single_units(my_singles, PS);
   const Slice sc = make_slice<E, SH>(p, member);
+  // Who publishes a row pair to the team.  The communication wave, after
+  // the step's barrier, waits for its own stores before its first poll
+  // returns (vector memory operations complete in order); the last data wave
+  // to finish the pair publishes before the barrier and leaves the polls
+  // free, but its stores queue behind its row loads.  Measured on one
+  // MI355X: fp32 rows (V = 262144, rows at 3.9 TB/s) 249 -> 198 us with the
+  // data wave publishing and the next unit's loads issued after it; bf16
+  // rows (V = 151936, 4.4 TB/s) 147 -> 166 us, so bf16 keeps the
+  // communication wave.
+  constexpr bool kDataPublish = E::kPerVec == 4;
+  if constexpr (kDataPublish) {
+    if (threadIdx.x == 0) L.arrived[0] = L.arrived[1] = 0;
+    lds_barrier();
+  }
 
   // Both roles run steps s = 0 .. n with one barrier each, then a last one.
   // Data step s: loads of unit s + 2, first pass of unit s, the
@@ -849,9 +911,11 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
     // Step s: first pass on buffer s mod 3, loads into buffer s + 2 mod 3.
     auto step = [&](int64_t s, const Regs<NV>& Rf, const UnitDesc& Uf, Regs<NV>& Rl,
                     UnitDesc& Ul) {
-      Ul = un;
-      load_unit<E, NV, SH, PS>(p, Ul, sc, lp, Rl, dummy);
-      un = unit_at(p, s + 3, n, team, my_pairs, my_singles, PS);
+      if constexpr (!kDataPublish) {
+        Ul = un;
+        load_unit<E, NV, SH, PS>(p, Ul, sc, lp, Rl, dummy);
+        un = unit_at(p, s + 3, n, team, my_pairs, my_singles, PS);
+      }
       float e[2 * NV * E::kPerVec];
       float mslp = 0.0f, mslq = 0.0f;
       first_pass_data<E, NV, PS>(p, Uf, sc, Rf, L, (int)(s & 1), e, mslp, mslq,
@@ -870,6 +934,14 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
           park[k][threadIdx.x] = make_uint4(__float_as_uint(e[4 * k]), __float_as_uint(e[4 * k + 1]),
                                             __float_as_uint(e[4 * k + 2]),
                                             __float_as_uint(e[4 * k + 3]));
+        if constexpr (kDataPublish) arrive_pair(p, Uf, L, (int)(s & 1), team, member);
+      }
+      if constexpr (kDataPublish) {
+        // the next unit's loads after the publication, which would otherwise
+        // queue behind them
+        Ul = un;
+        load_unit<E, NV, SH, PS>(p, Ul, sc, lp, Rl, dummy);
+        un = unit_at(p, s + 3, n, team, my_pairs, my_singles, PS);
       }
       lds_barrier();
       if (wants_alpha(p, up))
@@ -947,7 +1019,7 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
       lds_barrier();
       if ((s & 63) == 0) load_block(s);
       const UnitDesc u = comm_unit(s);
-      first_pass_comm(p, u, comm_second(s), L, (int)(s & 1), team, member, um2,
+      first_pass_comm<kDataPublish>(p, u, comm_second(s), L, (int)(s & 1), team, member, um2,
                       (int)((s - 2) & 1));
       if (wants_alpha(p, u)) team_wait_comm<E, SH>(p, u, L, (int)(s & 1), team, member, failed);
       um2 = um1;
