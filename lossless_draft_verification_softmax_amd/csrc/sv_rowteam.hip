@@ -318,7 +318,7 @@ __device__ __forceinline__ SoftmaxPart softmax_keep(const float (&x)[N], float s
   msl = ref_of(ms, sl);
 #pragma unroll
   for (int i = 0; i < N; ++i) e[i] = exp2_fast(__builtin_fmaf(x[i], sl, -msl));
-  constexpr int C = N < 8 ? N : 8;
+  constexpr int C = N % 8 == 0 ? 8 : (N < 8 ? N : 4);
   static_assert(N % C == 0, "group size must be a multiple of the chunk");
   float acc = 0.0f;
 #pragma unroll
@@ -584,7 +584,7 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
                                                  TeamLds& L, int b, float mslp, float mslq) {
   constexpr int VEC = E::kPerVec;
   constexpr int H = NV * VEC / 4;  // 16-byte vectors of one row's exponentials
-  static_assert(H == 1 || H % 2 == 0, "row exponentials are 1 or an even number of vectors");
+
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const float sl = u.sl;
@@ -597,7 +597,7 @@ __device__ __forceinline__ void second_pass_data(const VerifyParams& p, const Un
     const float kp = ip > -60 ? __builtin_ldexpf(L.ep[b], ip) : 0.0f;
     const float r = ip > -60 ? __builtin_ldexpf(L.rq[b], iq - ip) : 0.0f;
     // chunks of G 16-byte vectors of each row
-    constexpr int G = H >= 2 ? 2 : 1;
+    constexpr int G = H % 2 == 0 ? 2 : 1;
     float sum = 0.0f;
 #pragma unroll
     for (int c = 0; c < H; c += G) {
@@ -1031,9 +1031,10 @@ __global__ __launch_bounds__(kTeamThreads) void k_rowteam(VerifyParams p) {
   }
 }
 
-// Team geometry for a row of V elements: NV <= 2 16-byte vectors per data
-// thread per row (three buffers of two rows stay in registers, the
-// exponentials of one more row pair are parked in LDS), T members per row.
+// Team geometry for a row of V elements: NV <= 2 (bf16) or 3 (fp32) 16-byte
+// vectors per data thread per row (three buffers of two rows stay in
+// registers, the exponentials of one more row pair are parked in LDS), T
+// members per row.
 // Returns false if a row needs more than 64 members (the caller then uses
 // the streaming row pass).  Vocabulary shards do not change it: the members
 // tile the concatenated row.
@@ -1041,8 +1042,11 @@ bool team_geometry(sv_dtype dtype, int64_t V, int grid, int32_t* T, int32_t* NV,
                    int32_t* slice_len) {
   const int64_t vec = (dtype == SV_DTYPE_BF16) ? 8 : 4;
   const int64_t rowvec = (V + vec - 1) / vec;
+  // fp32 rows take up to three vectors per thread (the registers and the
+  // parked exponentials of three 4-element vectors fit), bf16 rows two
+  const int64_t nv_max = (dtype == SV_DTYPE_FP32) ? 3 : 2;
   int64_t nv = (rowvec + kDataThreads - 1) / kDataThreads;
-  if (nv > 2) nv = 2;
+  if (nv > nv_max) nv = nv_max;
   if (nv < 1) nv = 1;
   const int64_t t = (rowvec + kDataThreads * nv - 1) / (kDataThreads * nv);
   if (t > 64 || t > grid) return false;
@@ -1082,6 +1086,7 @@ static hipError_t launch_rowteam_sh(VerifyParams& p, int grid, int nv, hipStream
   if (p.dtype == SV_DTYPE_BF16)
     return nv == 1 ? launch_team_t<Bf16, 1, SH>(p, grid, stream)
                    : launch_team_t<Bf16, 2, SH>(p, grid, stream);
+  if (nv == 3) return launch_team_t<F32, 3, SH>(p, grid, stream);
   return nv == 1 ? launch_team_t<F32, 1, SH>(p, grid, stream)
                  : launch_team_t<F32, 2, SH>(p, grid, stream);
 }
