@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -56,20 +57,28 @@ def parse():
 
 
 # Sources each row-pass kernel is built from: a counter summary stays valid
-# while these are unchanged.
+# while their code (comments aside) is unchanged.
 KERNEL_SOURCES = {
     "k_rowteam": ["sv_rowteam.hip", "sv_block.hpp", "sv_device.hpp", "sv_internal.hpp"],
     "k_rowpass": ["sv_rowpass.hip", "sv_block.hpp", "sv_device.hpp", "sv_internal.hpp"],
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines: a comment edit leaves
+    the compiled kernel, and so its counters, unchanged."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_digest(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lossless_draft_verification_softmax_amd", "csrc")
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

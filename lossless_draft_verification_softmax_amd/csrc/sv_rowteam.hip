@@ -22,11 +22,13 @@
 //
 // Workgroup layout: waves 0..14 are data waves, wave 15 is the communication
 // wave.  The data waves load rows and reduce them to per-wave states in LDS;
-// the last of them to finish a row pair's first pass combines the states,
-// writes the partial slots and publishes the pair to the team.  The
-// communication wave waits for the team (its polls queue behind no stores
-// of its own) and hands the row normalisers back through LDS; it also
-// combines single rows' states.  Loads complete in order per wave, so any
+// the communication wave combines those states, writes the partial slots,
+// publishes a row pair to the team, waits for the team and hands the row
+// normalisers back through LDS.  For fp32 rows the last data wave to finish
+// a pair's first pass combines and publishes it instead, before the step's
+// barrier, so that the communication wave's polls queue behind no stores of
+// its own (bf16 rows keep the communication wave: there a data wave's stores
+// queue behind its row loads).  Loads complete in order per wave, so any
 // wave that waited on a fresh global load (a poll) would also wait for all
 // of its earlier row loads; keeping polls out of the data waves keeps their
 // prefetches in flight.  For the same reason every data wave issues exactly
@@ -48,10 +50,11 @@
 // Team exchange: member m publishes its slice states of its n-th row pair as
 // four 64-bit words (value bits | (n + 1) << 32) in ring slot n mod 4; a
 // reader accepts a word only if its tag is n + 1, so no fences are needed.
-// A member publishes n at the end of its data step n, after its barrier
-// n - 1, so after its communication wave has read every member's n - 2;
-// each of those was published after that member's barrier n - 3, by when
-// that member had read n - 4, the previous user of the ring slot.  The words
+// A member publishes n after its barrier n - 1 (at the end of its data step
+// n, or after barrier n from the communication wave), so after its
+// communication wave has read every member's n - 2; each of those was
+// published after that member's barrier n - 3, by when that member had read
+// n - 4, the previous user of the ring slot.  The words
 // are cleared before each launch.  The wait is bounded.  A team needs all of
 // its members resident at once, which holds when the kernel has the device to
 // itself (one workgroup per CU); when other work holds CUs a member may not
