@@ -192,8 +192,9 @@ sv_status sv_allocate_fixed_depth(const float* conf, int32_t B, int32_t D_max, i
  *
  * Layout requirements: logits base pointers 16-byte aligned and row_stride
  * a multiple of 8 elements (bf16) / 4 elements (fp32), row_stride >= V;
- * 1 <= V < 2^31; 0 <= D_max <= SV_MAX_DEPTH; row indices must address rows
- * inside the caller's buffers.  workspace: device memory of at least
+ * 1 <= V < 2^31; 0 <= D_max <= SV_MAX_DEPTH; B (D_max + 1) <= (2^31 - 1) / 64
+ * and B ceil(V / 2048) < 2^31 (SV_ERR_INVALID_ARGUMENT otherwise); row
+ * indices must address rows inside the caller's buffers.  workspace: device memory of at least
  * sv_verify_workspace_bytes(B, D_max, V) bytes, 256-byte aligned; its
  * contents need no initialisation and are scratch after the call.
  * ------------------------------------------------------------------------- */

@@ -69,6 +69,9 @@ sv_status validate_verify(const sv_verify_args* a, int64_t row_width, size_t* ne
                    SV_FLAG_EXACT_FP64_MASSES | SV_FLAG_TEAM_WAIT_GIVE_UP))
     return SV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * (a->D_max + 1) > (int64_t)INT32_MAX / 64) return SV_ERR_INVALID_ARGUMENT;
+  // the float64 draw numbers its (queue entry, tile) items in 32 bits
+  if ((int64_t)a->B * ((a->V + sv::kDrawTile - 1) / sv::kDrawTile) > (int64_t)INT32_MAX)
+    return SV_ERR_INVALID_ARGUMENT;
   if (a->B == 0) {
     *need = 0;
     return SV_OK;

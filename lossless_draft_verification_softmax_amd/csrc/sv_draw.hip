@@ -9,11 +9,11 @@
 // thread of a 256-thread workgroup).
 //   k_draw_tile64   one float64 pass over the (queued draw, tile) items: tile
 //                   normaliser partials and the one-pass split of the tile
-//                   residual masses
+//                   residual masses; one more workgroup, when asked for,
+//                   writes the batch's acceptance statistics meanwhile
+//                   (sv_stats.hpp)
 //   k_draw_pick64   one workgroup per queued draw: tile masses from the
-//                   partials, the crossing tile and the scan inside it;
-//                   one more workgroup, when asked for, writes the batch's
-//                   acceptance statistics (sv_stats.hpp)
+//                   partials, the crossing tile and the scan inside it
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -92,7 +92,7 @@ struct Weights64 {
   bool has_q;         // residual draw: w = max(0, p - q); else w = p
   double invT, cp, cq;  // exponent arguments fma(x, 1/T, c): c = -m / T of the row
   double izp, izq;    // 1 / Zp, 1 / Zq (izp = 1: the unnormalised p of a zero residual)
-  const double* tab;  // 2^(j/64) table of exp64_tab (LDS)
+  const double* tab;  // 2^(j/256) table of exp64_tab (LDS)
   // weights from the unnormalised exponentials
   __device__ __forceinline__ double weight(double ep, double eq) const {
     if (!has_q) return ep * izp;
@@ -294,8 +294,11 @@ constexpr double kTau64 = 1e-4;
 
 struct Draw64Lds {
   double tab[kExp64Table];  // 2^(j/256) for exp64_tab
-  double red[kDrawThreads / kWave][5];
-  int32_t redu[kDrawThreads / kWave];
+  // sums over the 16-lane rows of a tile pass item, and the kept-element
+  // counts of its wavefronts; two sets (item parity), so that one barrier
+  // per item separates a set's writes from its last reads
+  double red[2][kDrawThreads / 16][5];
+  int32_t redu[2][kDrawThreads / kWave];
   double z2[kDrawThreads / kWave][2];
   double mass[kDrawThreads];  // tile masses of a row of at most 256 tiles
   int redo[kDrawThreads];
@@ -303,10 +306,42 @@ struct Draw64Lds {
   unsigned long long last1;
 };
 
-// The exponential table into LDS (read by every exp64_tab of the kernel).
-__device__ __forceinline__ void load_exp_table(Draw64Lds& L) {
-  for (int j = threadIdx.x; j < kExp64Table; j += kDrawThreads) L.tab[j] = kExp2Frac[j];
-  __syncthreads();
+// The exponential table goes to LDS one entry per thread: the entry is
+// loaded at kernel entry, together with the kernel's first other loads, and
+// stored before the first barrier (every exp64_tab comes after it).
+static_assert(kExp64Table == kDrawThreads, "one table entry per thread");
+__device__ __forceinline__ double exp_table_entry() { return kExp2Frac[threadIdx.x]; }
+
+// Float64 sum over the wavefront, the same value on every lane: the fixed
+// tree of wave_allreduce (quad, 8-lane and 16-lane mirrors, then the row and
+// half swaps), both 32-bit halves of an operand moving together.
+template <int kCtrl>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, kCtrl, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), kCtrl, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// Float64 sum over each 16-lane row, the same value on every lane of the row.
+__device__ __forceinline__ double row_sum_d(double v) {
+  v = v + dpp_d<kDppQuadXor1>(v);
+  v = v + dpp_d<kDppQuadXor2>(v);
+  v = v + dpp_d<kDppHalfMirror>(v);
+  return v + dpp_d<kDppMirror>(v);
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v = row_sum_d(v);
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  v = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
+      __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+  const uint64_t c = __builtin_bit_cast(uint64_t, v);
+  lo = __builtin_amdgcn_permlane32_swap((uint32_t)c, (uint32_t)c, false, false);
+  hi = __builtin_amdgcn_permlane32_swap((uint32_t)(c >> 32), (uint32_t)(c >> 32), false, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
+         __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
 }
 
 // Exponentials of the float32 draw's tile, kept by the tile pass for the pick:
@@ -326,7 +361,7 @@ __device__ __forceinline__ void tile_load(const VerifyParams& p, const DrawJob& 
 
 template <typename E, bool SH>
 __device__ __forceinline__ void tile_pass(const VerifyParams& p, const DrawJob& jb, int slot,
-                                          int64_t tile, const Raw8<E>& raw, Draw64Lds& L) {
+                                          int64_t tile, const Raw8<E>& raw, int buf, Draw64Lds& L) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int64_t o = (int64_t)slot * p.S2 + tile;
   const bool residual = jb.mode == kDrawResidual;
@@ -352,35 +387,56 @@ __device__ __forceinline__ void tile_pass(const VerifyParams& p, const DrawJob& 
       const double eq = exp64_tab(fma((double)b[j], invT, cq), L.tab);
       zq += eq;
       if (hinted) hq[j * kDrawThreads] = eq;
+      // the element's class, without branches (the sums of the other
+      // classes add an exact 0)
       const double d = fma(ep, rho_e, -eq);
       const double tol = tau_rho * ep;
-      if (a[j] == b[j]) {
-        S += ep;
-      } else if (d > tol) {
-        D += d;
-        A += ep;
-      } else if (d >= -tol && ep > 0.0) {
-        // (ep = 0 weighs max(0, -eq) = 0: never kept)
-        kmask |= 1u << j;
-      }
+      const bool same = a[j] == b[j];
+      const bool pos = !same && d > tol;
+      // (ep = 0 weighs max(0, -eq) = 0: never kept)
+      const bool keep = !same && !pos && d >= -tol && ep > 0.0;
+      S += same ? ep : 0.0;
+      D += pos ? d : 0.0;
+      A += pos ? ep : 0.0;
+      kmask |= (uint32_t)keep << j;
     }
   }
-  // kept elements: positions by an exclusive scan of the counts in thread
-  // order, so the list is in element order
-  const int32_t U = __builtin_popcount(kmask);
-  int32_t incl = U;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int32_t x = __shfl_up(incl, d);
-    if (lane >= d) incl += x;
+  // kept elements: positions in element order (a lane's eight elements are
+  // consecutive; lanes, then wavefronts, in order), from one ballot per
+  // element slot; usually no element of the wavefront is kept
+  int32_t before = 0, wave_kept = 0;
+  if (__ballot(kmask != 0u) != 0ull) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint64_t bal = __ballot((kmask >> j) & 1u);
+      before += (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      wave_kept += __builtin_popcountll(bal);
+    }
   }
-  if (lane == kWave - 1) L.redu[wave] = incl;
+  zp = row_sum_d(zp);
+  if (residual) {
+    zq = row_sum_d(zq);
+    D = row_sum_d(D);
+    A = row_sum_d(A);
+    S = row_sum_d(S);
+  }
+  if ((lane & 15) == 0) {
+    const int row = wave * (kWave / 16) + lane / 16;
+    L.red[buf][row][0] = zp;
+    L.red[buf][row][1] = zq;
+    L.red[buf][row][2] = D;
+    L.red[buf][row][3] = A;
+    L.red[buf][row][4] = S;
+    if (lane == 0) L.redu[buf][wave] = wave_kept;
+  }
   __syncthreads();
-  int32_t base = 0, total = 0;
+  int32_t base = before, total = 0;
   for (int w = 0; w < kDrawThreads / kWave; ++w) {
-    if (w < wave) base += L.redu[w];
-    total += L.redu[w];
+    const int32_t c = L.redu[buf][w];
+    if (w < wave) base += c;
+    total += c;
   }
-  base += incl - U;
   if (total <= kDrawKeep64 && kmask != 0u) {
     double* keep = p.seg_e64 + o * (kDrawKeep64 * 2);
     int32_t pos = base;
@@ -393,32 +449,18 @@ __device__ __forceinline__ void tile_pass(const VerifyParams& p, const DrawJob& 
       }
     }
   }
-  // block sums in a fixed order
-  for (int m = 1; m < kWave; m <<= 1) {
-    zp += shfl_xor_d(zp, m);
-    zq += shfl_xor_d(zq, m);
-    D += shfl_xor_d(D, m);
-    A += shfl_xor_d(A, m);
-    S += shfl_xor_d(S, m);
-  }
-  if (lane == 0) {
-    L.red[wave][0] = zp;
-    L.red[wave][1] = zq;
-    L.red[wave][2] = D;
-    L.red[wave][3] = A;
-    L.red[wave][4] = S;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double t[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-    for (int w = 0; w < kDrawThreads / kWave; ++w)
-      for (int k = 0; k < 5; ++k) t[k] += L.red[w][k];
-    p.seg_zp64[o] = t[0];
-    p.seg_zq64[o] = t[1];
-    p.seg_w64[o] = t[2];
-    p.seg_a64[o] = t[3];
-    p.seg_t64[o] = t[4];
-    p.seg_u32[o] = total;
+  // block sums in a fixed order, one value per lane of the first wavefront
+  if (threadIdx.x < 6) {
+    const int k = threadIdx.x;
+    if (k == 5) {
+      p.seg_u32[o] = total;
+    } else {
+      double t = 0.0;
+      for (int w = 0; w < kDrawThreads / 16; ++w) t += L.red[buf][w][k];
+      double* dst = k == 0 ? p.seg_zp64 : k == 1 ? p.seg_zq64 : k == 2 ? p.seg_w64
+                                                 : k == 3 ? p.seg_a64 : p.seg_t64;
+      dst[o] = t;
+    }
   }
 }
 
@@ -483,10 +525,8 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
     zps += p.seg_zp64[ro + j];
     if (residual) zqs += p.seg_zq64[ro + j];
   }
-  for (int m = 1; m < kWave; m <<= 1) {
-    zps += shfl_xor_d(zps, m);
-    zqs += shfl_xor_d(zqs, m);
-  }
+  zps = wave_sum_d(zps);
+  zqs = wave_sum_d(zqs);
   if (lane == 0) {
     L.z2[wave][0] = zps;
     L.z2[wave][1] = zqs;
@@ -604,70 +644,86 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
 // Tile pass: the (queue entry, tile) items are dealt to a grid of
 // kTileBlocksPerCu workgroups per CU, all resident at once, item it to
 // workgroup it mod grid.  Each workgroup issues the loads of its next item
-// before it works on the current one, and reads the queue entries of its
-// first two items together with the queue length (an entry is used only
-// once the length shows that it is queued).  An empty queue costs one short
-// dispatch.
+// before it works on the current one.  Its first loads (the queue entries
+// of its first two items, the queue length and its exponential table entry)
+// go out together at entry; an entry is used only once the length shows
+// that it is queued.  An empty queue costs one short dispatch.  Item
+// indices fit 32 bits (the host bounds B times the tiles per row).
 template <typename E, bool SH>
-__global__ __launch_bounds__(kDrawThreads, kTileBlocksPerCu) void k_draw_tile64(VerifyParams p) {
-  __shared__ Draw64Lds L;
-  const int64_t S2 = p.S2, G = gridDim.x, cap = (int64_t)p.B * S2;
-  int64_t it = blockIdx.x;
+__device__ __forceinline__ void tile_items(const VerifyParams& p, uint32_t wg, uint32_t G,
+                                           Draw64Lds& L) {
+  const uint32_t S2 = (uint32_t)p.S2, cap = (uint32_t)p.B * S2;
+  uint32_t it = wg;
   DrawJob jb{}, jn{};
   if (it < cap) jb = p.fb_jobs[it / S2];
   if (it + G < cap) jn = p.fb_jobs[(it + G) / S2];
-  const int64_t items = (int64_t)(*p.fb_count) * S2;
+  const double tab = exp_table_entry();
+  const uint32_t items = (uint32_t)*p.fb_count * S2;
+  // (the table load is issued before the exit test, not sunk below it)
+  asm volatile("" ::"v"(tab));
   if (it >= items) return;
-  load_exp_table(L);
+  L.tab[threadIdx.x] = tab;
   Raw8<E> raw;
   tile_load<E, SH>(p, jb, it % S2, raw);
-  for (; it < items; it += G) {
+  __syncthreads();
+  for (int buf = 0; it < items; it += G, buf ^= 1) {
     // the next item's loads (the current item's again past the end, so
     // that every address is valid and no branch splits the loads)
-    const int64_t nx = it + G;
+    const uint32_t nx = it + G;
     const bool more = nx < items;
     Raw8<E> rawn;
     tile_load<E, SH>(p, more ? jn : jb, more ? nx % S2 : it % S2, rawn);
     DrawJob jnn{};
     if (nx + G < items) jnn = p.fb_jobs[(nx + G) / S2];
-    const int slot = (int)(it / S2);
-    tile_pass<E, SH>(p, jb, slot, it - (int64_t)slot * S2, raw, L);
-    __syncthreads();
+    const uint32_t slot = it / S2;
+    tile_pass<E, SH>(p, jb, (int)slot, (int64_t)(it - slot * S2), raw, buf, L);
     raw = rawn;
     jb = jn;
     jn = jnn;
   }
 }
 
-// Pick: workgroup j < B draws queue entry j.  Workgroup B, launched only
-// when the caller asked for them, writes the batch's acceptance statistics
-// (accepted lengths and rates are final once k_accept_draw has run).
+// When the caller asked for the batch's acceptance statistics (accepted
+// lengths and rates are final once k_accept_draw has run), workgroup 0,
+// dispatched first, writes them while the tile workgroups 1, 2, ... run;
+// the one tile workgroup that finds no free slot at first is the last, which
+// has the fewest items.
 template <typename E, bool SH>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
+__global__ __launch_bounds__(kDrawThreads, kTileBlocksPerCu) void k_draw_tile64(VerifyParams p) {
   __shared__ union {
     Draw64Lds d;
     StatsLds s;
   } L;
-  const int slot = blockIdx.x;
-  if (slot >= p.B) {
+  const bool stats = p.stats_expected_len || p.stats_per_depth || p.stats_summary;
+  if (stats && blockIdx.x == 0) {
     accept_stats_block<kDrawThreads / kWave, 4>(p.depth, p.alpha, p.accepted_len, p.B, p.D,
                                                 p.stats_expected_len, p.stats_per_depth,
                                                 p.stats_summary, L.s);
     return;
   }
+  const uint32_t first = stats ? 1u : 0u;
+  tile_items<E, SH>(p, blockIdx.x - first, gridDim.x - first, L.d);
+}
+
+// Pick: workgroup j draws queue entry j.
+template <typename E, bool SH>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
+  __shared__ Draw64Lds L;
+  const int slot = blockIdx.x;
   const DrawJob jb = p.fb_jobs[slot];
+  const double tab = exp_table_entry();
+  asm volatile("" ::"v"(tab));
   if (slot >= *p.fb_count) return;
-  load_exp_table(L.d);
-  pick64<E, SH>(p, jb, slot, L.d);
+  L.tab[threadIdx.x] = tab;  // visible after pick64's first barrier
+  pick64<E, SH>(p, jb, slot, L);
 }
 
 template <typename E, bool SH>
 static void launch_draw_t(const VerifyParams& p, int cus, hipStream_t stream) {
-  hipLaunchKernelGGL((k_draw_tile64<E, SH>), dim3(cus * kTileBlocksPerCu), dim3(kDrawThreads), 0,
-                     stream, p);
   const bool stats = p.stats_expected_len || p.stats_per_depth || p.stats_summary;
-  hipLaunchKernelGGL((k_draw_pick64<E, SH>), dim3((unsigned)p.B + (stats ? 1u : 0u)),
+  hipLaunchKernelGGL((k_draw_tile64<E, SH>), dim3(cus * kTileBlocksPerCu + (stats ? 1 : 0)),
                      dim3(kDrawThreads), 0, stream, p);
+  hipLaunchKernelGGL((k_draw_pick64<E, SH>), dim3((unsigned)p.B), dim3(kDrawThreads), 0, stream, p);
 }
 
 void launch_draw(const VerifyParams& p, int cus, hipStream_t stream) {

@@ -3,8 +3,11 @@
 // implementation of the exponential function in IEEE floating-point
 // arithmetic", ACM Trans. Math. Software 15(2), 1989.
 //
-// x = n ln2/256 + r with n = rint(256 x / ln2) and |r| <= ln2/512 (plus the
-// rounding of the product); with n = 256 m + j, j in [0, 256),
+// x = n ln2/256 + r with n the integer nearest to 256 x / ln2 and
+// |r| <= ln2/512 (plus the reduction's rounding); n comes from one fused
+// multiply-add against 1.5 2^52, after which the low word of the sum holds
+// n (|n| < 2^31 here) and subtracting 1.5 2^52 again gives n exactly.  With
+// n = 256 m + j, j in [0, 256),
 // exp(x) = 2^m 2^(j/256) e^r.  2^(j/256) is read from a table of the 256
 // values rounded to nearest; e^r is its Taylor polynomial of degree 4, whose
 // truncation is below (ln2/512)^5 / 120 < 4e-17 relative.  r is reduced in
@@ -32,6 +35,7 @@ constexpr double kExp64Lo = 0x1.abc9e3b39803fp-64;    // ln2 / 256 - kExp64Hi, r
 constexpr double kExp64C3 = 0x1.5555555555555p-3;     // 1/6
 constexpr double kExp64C4 = 0x1.5555555555555p-5;     // 1/24
 constexpr double kExp64Min = -746.0;
+constexpr double kExp64Shift = 0x1.8p52;  // rounds a sum below 2^51 in magnitude to an integer
 
 // 2^(j/256), j = 0 .. 255, rounded to nearest.
 constexpr double kExp2Frac[kExp64Table] = {
@@ -126,14 +130,15 @@ constexpr double kExp2Frac[kExp64Table] = {
 // exp(x) with the table `tab` (kExp2Frac, or a copy of it in LDS).
 __host__ __device__ __forceinline__ double exp64_tab(double x, const double* tab) {
   x = fmax(x, kExp64Min);
-  const double n = rint(x * kExp64Scale);
+  const double t = fma(x, kExp64Scale, kExp64Shift);
+  const double n = t - kExp64Shift;
+  const int ni = (int)(uint32_t)__builtin_bit_cast(uint64_t, t);
   double r = fma(-n, kExp64Hi, x);
   r = fma(-n, kExp64Lo, r);
   double q = fma(r, kExp64C4, kExp64C3);
   q = fma(q, r, 0.5);
   q = fma(q, r, 1.0);
   q = fma(q, r, 1.0);
-  const int ni = (int)n;
   return ldexp(tab[ni & (kExp64Table - 1)] * q, ni >> kExp64Bits);
 }
 

@@ -2,9 +2,9 @@
 // L_e2e of "AngelSpec: specialize the drafter...", section "MTP"; MAL and
 // mean acceptance of the tradepoint.io page, "The MTP path") as the routine
 // of one workgroup.  The statistics kernel runs it with 16 wavefronts; the
-// float64 draw kernel runs it with its 4 on one spare workgroup, so that a
-// verification call can leave the statistics of its own batch without a
-// launch of its own.
+// float64 tile pass runs it with its 4 on one extra workgroup, beside its
+// tiles, so that a verification call can leave the statistics of its own
+// batch without a launch of its own.
 //
 // Lane k of a wavefront holds position k (D_max <= 64): a wavefront prefix
 // product gives prod_{j<=k} alpha_j and a wavefront sum gives E[tau_r].
@@ -52,9 +52,7 @@ __device__ __forceinline__ float lane_prefix_product(float a, int D) {
     if (r >= 8) pref *= o;
     return pref;
   }
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    if (d >= D) break;  // uniform
+  for (int d = 1; d < D && d < kWave; d <<= 1) {  // uniform
     const float o = __shfl_up(pref, d);
     if (lane >= d) pref *= o;
   }
