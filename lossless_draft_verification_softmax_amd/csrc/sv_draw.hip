@@ -33,46 +33,118 @@ constexpr int kDrawThreads = 256;
 // up to 128 registers per lane).
 constexpr int kTileBlocksPerCu = 4;
 
-// Fixed-order block scan (Hillis-Steele in each wavefront, wave totals in
-// order).  Returns the inclusive value; *total gets the block total.
-template <typename T>
-__device__ __forceinline__ T scan256(T v, T* lds, T* total) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    T o;
-    if constexpr (sizeof(T) == 8) {
-      int2 q = *reinterpret_cast<int2*>(&v);
-      q.x = __shfl_up(q.x, d);
-      q.y = __shfl_up(q.y, d);
-      o = *reinterpret_cast<T*>(&q);
-    } else {
-      o = __shfl_up(v, d);
-    }
-    if (lane >= d) v = v + o;
-  }
-  if (lane == kWave - 1) lds[wave] = v;
-  __syncthreads();
-  T base = T(0);
-  for (int w = 0; w < wave; ++w) base = base + lds[w];
-  const T out = (wave == 0) ? v : base + v;
-  T tot = lds[0];
-  for (int w = 1; w < kDrawThreads / kWave; ++w) tot = tot + lds[w];
-  __syncthreads();
-  *total = tot;
-  return out;
+// Float64 sum over the wavefront, the same value on every lane: the fixed
+// tree of wave_allreduce (quad, 8-lane and 16-lane mirrors, then the row and
+// half swaps), both 32-bit halves of an operand moving together.
+template <int kCtrl>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, kCtrl, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), kCtrl, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// Float64 sum over each 16-lane row, the same value on every lane of the row.
+__device__ __forceinline__ double row_sum_d(double v) {
+  v = v + dpp_d<kDppQuadXor1>(v);
+  v = v + dpp_d<kDppQuadXor2>(v);
+  v = v + dpp_d<kDppHalfMirror>(v);
+  return v + dpp_d<kDppMirror>(v);
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v = row_sum_d(v);
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  v = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
+      __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+  const uint64_t c = __builtin_bit_cast(uint64_t, v);
+  lo = __builtin_amdgcn_permlane32_swap((uint32_t)c, (uint32_t)c, false, false);
+  hi = __builtin_amdgcn_permlane32_swap((uint32_t)(c >> 32), (uint32_t)(c >> 32), false, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
+         __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
 }
 
-template <typename T>
-__device__ __forceinline__ T shfl_up1(T v) {
-  if constexpr (sizeof(T) == 8) {
-    int2 q = *reinterpret_cast<int2*>(&v);
-    q.x = __shfl_up(q.x, 1);
-    q.y = __shfl_up(q.y, 1);
-    return *reinterpret_cast<T*>(&q);
-  } else {
-    return __shfl_up(v, 1);
+// DPP moves with a row mask (rows left out read 0).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double dpp_d_rows(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, kCtrl, kRowMask, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), kCtrl, kRowMask, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive float64 scan over the wavefront in a fixed order: Hillis-Steele
+// steps inside each 16-lane row (row shifts by 1, 2, 4, 8), then row 0's
+// total into row 1 and row 2's into row 3 (broadcast of lane 15 of a row),
+// then the total of rows 0-1 into rows 2 and 3 (broadcast of lane 31).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppWaveShr1 = 0x138;
+__device__ __forceinline__ double wave_scan_d(double v) {
+  const int lane = threadIdx.x & (kWave - 1), r = lane & 15;
+  double o = dpp_d<kDppRowShr1>(v);
+  if (r >= 1) v = v + o;
+  o = dpp_d<kDppRowShr2>(v);
+  if (r >= 2) v = v + o;
+  o = dpp_d<kDppRowShr4>(v);
+  if (r >= 4) v = v + o;
+  o = dpp_d<kDppRowShr8>(v);
+  if (r >= 8) v = v + o;
+  o = dpp_d_rows<kDppRowBcast15, 0xA>(v);
+  if (lane & 16) v = v + o;
+  o = dpp_d_rows<kDppRowBcast31, 0xC>(v);
+  if (lane >= 32) v = v + o;
+  return v;
+}
+
+// Block-level exchanges of the pick go through two sets of LDS slots used in
+// turn (`buf`, flipped by each exchange): every exchange has one barrier
+// between its writes and its reads, so the set an exchange writes was last
+// read before the previous exchange's barrier.
+struct PickLds {
+  double wtot[2][kDrawThreads / kWave];  // wavefront totals of a block scan
+  int first[2][kDrawThreads / kWave];    // first crossing lane of each wavefront, or -1
+  double c0[2][kDrawThreads / kWave];    // its exclusive cumulative value
+  int64_t y[2][kDrawThreads / kWave];    // (scan in a tile) its token
+  double margin[2][kDrawThreads / kWave];
+};
+
+// Block scan of one float64 per thread: returns the inclusive value, with
+// *excl the previous thread's inclusive value (0 for thread 0) and *total the
+// block total.  The wavefront totals are added in order, the same way for
+// the inclusive and the exclusive values, so a thread's *excl equals the
+// previous thread's return value bit for bit.
+__device__ __forceinline__ double block_scan_d(double v, PickLds& L, int& buf, double* excl,
+                                               double* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const double incl = wave_scan_d(v);
+  const double prev = dpp_d<kDppWaveShr1>(incl);  // lane 0 reads 0
+  if (lane == kWave - 1) L.wtot[buf][wave] = incl;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+  for (int w = 0; w < kDrawThreads / kWave; ++w) {
+    const double x = L.wtot[buf][w];
+    if (w < wave) base = base + x;
+    tot = tot + x;
   }
+  buf ^= 1;
+  *total = tot;
+  if (wave == 0) {
+    *excl = lane == 0 ? 0.0 : prev;
+    return incl;
+  }
+  *excl = lane == 0 ? base : base + prev;
+  return base + incl;
+}
+
+// Block total of one float64 per thread (row sums, then the 16 row totals in
+// order through LDS).
+__device__ __forceinline__ double block_sum_d(double v, PickLds& L, int& buf) {
+  double excl, tot;
+  block_scan_d(v, L, buf, &excl, &tot);
+  return tot;
 }
 
 // ---------------------------------------------------------------------------
@@ -140,17 +212,6 @@ __device__ __forceinline__ double sum8(const double (&w)[kPer]) {
   return s;
 }
 
-struct PickLds {
-  double scan[kDrawThreads / kWave];
-  double last[kDrawThreads / kWave];
-  int wave_first[kDrawThreads / kWave];
-  int64_t y;
-  double margin;
-  int found;
-  int tile;
-  double c0;
-};
-
 // The crossing tile of a draw given the per-tile masses: one scan of the
 // masses (rounds of 256 tiles, carry in order) for the total R, and
 // t = u R; the crossing tile is the first tile of non-zero mass whose
@@ -164,57 +225,47 @@ struct TileFind {
   double R;
 };
 
-__device__ TileFind find_tile(const double* masses, int64_t S2, double u, PickLds& L) {
+__device__ TileFind find_tile(const double* masses, int64_t S2, double u, PickLds& L, int& buf) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  if (tid == 0) L.tile = -1;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   double carry = 0.0;
-  double m1 = 0.0, incl1 = 0.0;  // this thread's tile (single round)
+  double m1 = 0.0, incl1 = 0.0, excl1 = 0.0;  // this thread's tile (single round)
   for (int64_t base = 0; base < S2; base += kDrawThreads) {
     const double m = (base + tid < S2) ? masses[base + tid] : 0.0;
     double tot;
-    const double incl = scan256<double>(m, L.scan, &tot);
+    incl1 = block_scan_d(m, L, buf, &excl1, &tot);
     m1 = m;
-    incl1 = incl;
     carry = carry + tot;
   }
   const double R = carry;
   const double t = u * R;
   carry = 0.0;
+  TileFind f{-1, 0.0, t, R};
   for (int64_t base = 0; base < S2; base += kDrawThreads) {
-    double m = m1, incl = incl1, tot = R;
+    double m = m1, incl = incl1, excl = excl1, tot = R;
     if (S2 > kDrawThreads) {
       m = (base + tid < S2) ? masses[base + tid] : 0.0;
-      incl = carry + scan256<double>(m, L.scan, &tot);
+      incl = carry + block_scan_d(m, L, buf, &excl, &tot);
+      excl = carry + excl;
     }
-    double excl = shfl_up1(incl);
-    // exclusive value across wave boundaries: previous thread's inclusive
-    if (lane == kWave - 1) L.last[tid / kWave] = incl;
-    __syncthreads();
-    if (lane == 0) excl = (tid == 0) ? carry : L.last[tid / kWave - 1];
     const bool cross = (base + tid < S2) && m > 0.0 && incl > t;
     const uint64_t mask = __ballot(cross);
-    if (lane == 0) L.wave_first[tid / kWave] = mask ? (int)__builtin_ctzll(mask) : -1;
+    const int fl = mask ? (int)__builtin_ctzll(mask) : -1;
+    if (lane == 0) L.first[buf][wave] = fl;
+    if (lane == fl) L.c0[buf][wave] = excl;
     __syncthreads();
-    int winner = -1;
-    for (int w = 0; w < kDrawThreads / kWave; ++w)
-      if (L.wave_first[w] >= 0) {
-        winner = w * kWave + L.wave_first[w];
+    for (int w = 0; w < kDrawThreads / kWave; ++w) {
+      const int fw = L.first[buf][w];
+      if (fw >= 0) {
+        f.tile = (int)(base + w * kWave + fw);
+        f.c0 = L.c0[buf][w];
         break;
       }
-    if (winner >= 0) {
-      if (tid == winner) {
-        L.tile = (int)(base + tid);
-        L.c0 = excl;
-      }
-      __syncthreads();
-      break;
     }
+    buf ^= 1;
+    if (f.tile >= 0) break;  // uniform
     carry = carry + tot;
-    __syncthreads();
   }
-  TileFind f{L.tile, L.c0, t, R};
-  __syncthreads();  // L reused by the caller
   return f;
 }
 
@@ -228,16 +279,10 @@ struct InTile {
 };
 
 __device__ InTile scan_in_tile(const double (&w)[kPer], int64_t i0, double c0, double t,
-                               PickLds& L) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  if (tid == 0) L.found = 0;
-  double tot;
-  const double incl = scan256<double>(sum8(w), L.scan, &tot);
-  double excl = shfl_up1(incl);
-  if (lane == kWave - 1) L.last[tid / kWave] = incl;
-  __syncthreads();
-  if (lane == 0) excl = (tid == 0) ? 0.0 : L.last[tid / kWave - 1];
+                               PickLds& L, int& buf) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  double excl, tot;
+  block_scan_d(sum8(w), L, buf, &excl, &tot);
   double run = excl;
   int first = -1;
   double before = 0.0, at = 0.0;
@@ -253,23 +298,22 @@ __device__ InTile scan_in_tile(const double (&w)[kPer], int64_t i0, double c0, d
     }
   }
   const uint64_t mask = __ballot(first >= 0);
-  if (lane == 0) L.wave_first[tid / kWave] = mask ? (int)__builtin_ctzll(mask) : -1;
-  __syncthreads();
-  int winner = -1;
-  for (int wv = 0; wv < kDrawThreads / kWave; ++wv)
-    if (L.wave_first[wv] >= 0) {
-      winner = wv * kWave + L.wave_first[wv];
-      break;
-    }
-  if (winner >= 0 && tid == winner) {
-    L.found = 1;
-    L.y = i0 + first;
+  const int fl = mask ? (int)__builtin_ctzll(mask) : -1;
+  if (lane == 0) L.first[buf][wave] = fl;
+  if (lane == fl) {
+    L.y[buf][wave] = i0 + first;
     const double a = t - before, b = at - t;
-    L.margin = a < b ? a : b;
+    L.margin[buf][wave] = a < b ? a : b;
   }
   __syncthreads();
-  InTile r{L.found, L.y, L.margin};
-  __syncthreads();
+  InTile r{0, -1, 0.0};
+  for (int wv = 0; wv < kDrawThreads / kWave; ++wv) {
+    if (L.first[buf][wv] >= 0) {
+      r = InTile{1, L.y[buf][wv], L.margin[buf][wv]};
+      break;
+    }
+  }
+  buf ^= 1;
   return r;
 }
 
@@ -311,38 +355,6 @@ struct Draw64Lds {
 // stored before the first barrier (every exp64_tab comes after it).
 static_assert(kExp64Table == kDrawThreads, "one table entry per thread");
 __device__ __forceinline__ double exp_table_entry() { return kExp2Frac[threadIdx.x]; }
-
-// Float64 sum over the wavefront, the same value on every lane: the fixed
-// tree of wave_allreduce (quad, 8-lane and 16-lane mirrors, then the row and
-// half swaps), both 32-bit halves of an operand moving together.
-template <int kCtrl>
-__device__ __forceinline__ double dpp_d(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, kCtrl, 0xF, 0xF, false);
-  const uint32_t hi =
-      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), kCtrl, 0xF, 0xF, false);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-// Float64 sum over each 16-lane row, the same value on every lane of the row.
-__device__ __forceinline__ double row_sum_d(double v) {
-  v = v + dpp_d<kDppQuadXor1>(v);
-  v = v + dpp_d<kDppQuadXor2>(v);
-  v = v + dpp_d<kDppHalfMirror>(v);
-  return v + dpp_d<kDppMirror>(v);
-}
-__device__ __forceinline__ double wave_sum_d(double v) {
-  v = row_sum_d(v);
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
-  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
-  v = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
-      __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
-  const uint64_t c = __builtin_bit_cast(uint64_t, v);
-  lo = __builtin_amdgcn_permlane32_swap((uint32_t)c, (uint32_t)c, false, false);
-  hi = __builtin_amdgcn_permlane32_swap((uint32_t)(c >> 32), (uint32_t)(c >> 32), false, false);
-  return __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
-         __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
-}
 
 // Exponentials of the float32 draw's tile, kept by the tile pass for the pick:
 // [entry][row][element j of a thread][thread].
@@ -467,15 +479,13 @@ __device__ __forceinline__ void tile_pass(const VerifyParams& p, const DrawJob& 
 // Mass of tile `tile` of a row, recomputed directly: the block total of the
 // thread sums of its float64 weights.
 template <typename W>
-__device__ __forceinline__ double tile_mass(const W& weights, int64_t tile, int64_t V,
-                                            double* lds) {
+__device__ __forceinline__ double tile_mass(const W& weights, int64_t tile, int64_t V, PickLds& L,
+                                            int& buf) {
   const int64_t lo = tile * kDrawTile;
   const int64_t hi = min(V, lo + (int64_t)kDrawTile);
   double w[kPer];
   weights(lo + (int64_t)threadIdx.x * kPer, hi, w);
-  double tot;
-  scan256<double>(sum8(w), lds, &tot);
-  return tot;
+  return block_sum_d(sum8(w), L, buf);
 }
 
 // The float64 draw of queue entry `slot`: full-row normalisers from the tile
@@ -492,6 +502,7 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
   const int64_t S2 = p.S2;
   const int64_t ro = (int64_t)slot * S2;
   const int64_t htile = jb.y32 >= 0 ? (int64_t)jb.y32 / kDrawTile : -1;
+  int buf = 0;  // LDS slot set of the next block exchange (PickLds)
   double hep[kPer], heq[kPer];
   if (htile >= 0) {
     const double* hp = hint_exps(p, slot, 0) + tid;
@@ -587,20 +598,21 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
     }
     L.redo[tid] = redo;
     // usually no tile needs a direct recompute: skip the walk over the flags
+    // (the barrier of __syncthreads_or also publishes the masses)
     if (__syncthreads_or(redo)) {
       for (int k = 0; k < kDrawThreads && base + k < S2; ++k) {
         if (!L.redo[k]) continue;  // uniform: every thread reads the same flag
-        const double m = tile_mass(w, base + k, p.V, L.pk.scan);
+        const double m = tile_mass(w, base + k, p.V, L.pk, buf);
         if (tid == 0) masses[base + k] = m;
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
   // R = 0 (p = q to float64 precision): draw from p, from the unnormalised
   // tile partials.
-  TileFind f = find_tile(masses, S2, (double)jb.u, L.pk);
+  TileFind f = find_tile(masses, S2, (double)jb.u, L.pk, buf);
   const bool unnorm = !(f.R > 0.0);
-  if (unnorm) f = find_tile(p.seg_zp64 + ro, S2, (double)jb.u, L.pk);
+  if (unnorm) f = find_tile(p.seg_zp64 + ro, S2, (double)jb.u, L.pk, buf);
   const Weights64<E, SH> wd = unnorm ? weights64<E, SH>(p, jb, true, 1.0, 1.0, L.tab) : w;
   InTile res{0, -1, 0.0};
   if (f.tile >= 0) {
@@ -613,7 +625,7 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
     } else {
       wd(i0, hi, wv);
     }
-    res = scan_in_tile(wv, i0, f.c0, f.t, L.pk);
+    res = scan_in_tile(wv, i0, f.c0, f.t, L.pk, buf);
   }
   if (!res.found) {
     // t rounded to or past the total: the last token of non-zero weight.
