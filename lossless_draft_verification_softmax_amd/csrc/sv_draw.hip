@@ -513,7 +513,8 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
       heq[j] = residual ? hq[j * kDrawThreads] : 0.0;
     }
   }
-  // the first round of tile partials
+  // the first round of tile partials, and the request's diagnostic bits
+  // (so that the last step waits on no load)
   const bool have0 = tid < S2;
   double zp0 = 0.0, zq0 = 0.0, d0 = 0.0, a0 = 0.0, s0 = 0.0;
   int32_t nk0 = 0;
@@ -527,9 +528,7 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
       nk0 = p.seg_u32[ro + tid];
     }
   }
-  // residual weight per unit of ep of an equal-logit pair (independent of the
-  // loads: computed while they are in flight)
-  // (equal logits a = b have eq / ep = exp(cq - cp))
+  const uint32_t bits0 = (p.diag && tid == 0) ? p.diag[jb.r].bits : 0u;
   // full-row normalisers: thread sums over the rounds, then a fixed-order tree
   double zps = zp0, zqs = zq0;
   for (int64_t j = tid + kDrawThreads; j < S2; j += kDrawThreads) {
@@ -543,6 +542,17 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
     L.z2[wave][1] = zqs;
   }
   __syncthreads();
+  // the first four kept elements of each tile of the first round (read
+  // whatever their count, only the first nk are used), in flight while the
+  // normalisers are inverted
+  double2 kv0[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) kv0[k] = make_double2(0.0, 0.0);
+  if (have0 && residual) {
+    const double2* keep = reinterpret_cast<const double2*>(p.seg_e64 + (ro + tid) * (kDrawKeep64 * 2));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) kv0[k] = keep[k];
+  }
   double Zp = 0.0, Zq = 0.0;
   for (int w = 0; w < kDrawThreads / kWave; ++w) {
     Zp += L.z2[w][0];
@@ -551,7 +561,8 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
   if (!residual) Zq = 1.0;
   const double izp = 1.0 / Zp, izq = 1.0 / Zq;
   const Weights64<E, SH> w = weights64<E, SH>(p, jb, false, izp, izq, L.tab);
-  const double kappa = exp(w.cq - w.cp);
+  // (equal logits a = b have eq / ep = kappa = exp(cq - cp) for the whole row)
+  const double kappa = exp64_tab(w.cq - w.cp, L.tab);
   // tile masses: from the one-pass split where it is certain, else directly
   double* masses = S2 <= kDrawThreads ? L.mass : p.seg_w64 + ro;
   const double rho = Zq * izp;
@@ -583,7 +594,9 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
             double2 kv[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-              kv[k] = (k0 + k < nk) ? keep[k0 + k] : make_double2(0.0, 0.0);
+              kv[k] = (base == 0 && k0 == 0) ? kv0[k]
+                      : (k0 + k < nk)        ? keep[k0 + k]
+                                             : make_double2(0.0, 0.0);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
               if (k0 + k < nk) m += w.weight(kv[k].x, kv[k].y);
@@ -648,7 +661,7 @@ __device__ void pick64(const VerifyParams& p, const DrawJob& jb, int slot, Draw6
     p.out_tokens[(int64_t)jb.r * (p.D + 1) + jb.tau] = (int32_t)res.y;
     if (p.diag) {
       p.diag[jb.r].draw_margin = (float)res.margin;
-      p.diag[jb.r].bits |= SV_BIT_FP64_DRAW | (unnorm ? SV_BIT_RESIDUAL_ZERO : 0u);
+      p.diag[jb.r].bits = bits0 | SV_BIT_FP64_DRAW | (unnorm ? SV_BIT_RESIDUAL_ZERO : 0u);
     }
   }
 }
