@@ -106,12 +106,41 @@ struct AcceptDrawLds {
   DrawState st;
   int slice;       // crossing slice, or -1
   float c0, t;     // cumulative mass before the slice, target u R
-  float wtot[kAcceptDrawWaves];
-  int wfirst[kAcceptDrawWaves];
-  int found;
-  int32_t y;
-  float before, at;
+  // per scan round (two sets used in turn, so that one barrier per
+  // exchange suffices): wavefront totals, and each wavefront's first
+  // crossing element with the cumulative masses around it
+  float wtot[2][kAcceptDrawWaves];
+  int wfirst[2][kAcceptDrawWaves];
+  int32_t wy[2][kAcceptDrawWaves];
+  float wbefore[2][kAcceptDrawWaves], wat[2][kAcceptDrawWaves];
 };
+
+// Inclusive float32 scan over the wavefront in a fixed order, by DPP moves:
+// Hillis-Steele steps inside each 16-lane row, then row 0's total into row
+// 1 and row 2's into row 3 (broadcast of lane 15 of a row), then the total of
+// rows 0-1 into rows 2 and 3 (broadcast of lane 31).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_rows_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
+__device__ __forceinline__ float wave_scan_f(float v) {
+  const int lane = threadIdx.x & (kWave - 1), r = lane & 15;
+  float o = dpp_f<0x111>(v);  // row_shr:1
+  if (r >= 1) v += o;
+  o = dpp_f<0x112>(v);        // row_shr:2
+  if (r >= 2) v += o;
+  o = dpp_f<0x114>(v);        // row_shr:4
+  if (r >= 4) v += o;
+  o = dpp_f<0x118>(v);        // row_shr:8
+  if (r >= 8) v += o;
+  o = dpp_rows_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  if (lane & 16) v += o;
+  o = dpp_rows_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  if (lane >= 32) v += o;
+  return v;
+}
+// The previous lane's value (wave_shr:1); lane 0 reads 0.
+__device__ __forceinline__ float wave_prev_f(float v) { return dpp_f<0x138>(v); }
 
 template <typename E, bool SH>
 __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams p) {
@@ -320,27 +349,23 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
       w = residual ? fmaxf(ps - a, 0.0f) : ps;
     }
     // inclusive scan over the slices (fixed order)
-    float c = w;
-#pragma unroll
-    for (int dd = 1; dd < kWave; dd <<= 1) {
-      const float o = __shfl_up(c, dd);
-      if (lane >= dd) c += o;
-    }
-    const float R = __shfl(c, ns - 1);
+    const float c = wave_scan_f(w);
+    const float R = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(c), ns > 0 ? ns - 1 : 0));
     const float t = st.u * R;
     const uint64_t cross = __ballot(lane < ns && w > 0.0f && c > t);
     const int j = cross ? (int)__builtin_ctzll(cross) : -1;
-    const float before = __shfl_up(c, 1);
+    const float before = wave_prev_f(c);
     if (lane == 0) {
       L.slice = force64 ? -1 : j;
       L.t = t;
-      L.found = 0;
     }
-    if (j >= 0 && lane == j) L.c0 = (j == 0) ? 0.0f : before;
+    if (j >= 0 && lane == j) L.c0 = before;
   }
   __syncthreads();
   const int j = L.slice;
   bool found = false;
+  int32_t y_hit = -1;
+  float before_hit = 0.0f, at_hit = 0.0f;
   if (j >= 0) {
     // ---- scan inside slice j, kChunk elements per round ----
     Weights32<E, SH> wt = weights32<E, SH>(p, st);
@@ -354,7 +379,8 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
     Raw8<E> cur, nxt;
     if (lo + (int64_t)k * kPer < hi)
       load_raw8<E, SH>(wt.prow, wt.qrow, wt.has_q, lo + (int64_t)k * kPer, hi, cur);
-    for (int64_t base = lo; base < hi; base += kChunk) {
+    int buf = 0;
+    for (int64_t base = lo; base < hi; base += kChunk, buf ^= 1) {
       const int64_t i0 = base + (int64_t)k * kPer;
       if (i0 + kChunk < hi) load_raw8<E, SH>(wt.prow, wt.qrow, wt.has_q, i0 + kChunk, hi, nxt);
       float w[kPer];
@@ -372,21 +398,17 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
       for (int e = 0; e < kPer; ++e) run += w[e];
       // block exclusive scan of the thread sums (wavefront scans, wave
       // totals in order)
-      float incl = run;
-#pragma unroll
-      for (int dd = 1; dd < kWave; dd <<= 1) {
-        const float o = __shfl_up(incl, dd);
-        if (lane >= dd) incl += o;
-      }
-      if (lane == kWave - 1) L.wtot[wave] = incl;
+      const float incl = wave_scan_f(run);
+      const float prev = wave_prev_f(incl);
+      if (lane == kWave - 1) L.wtot[buf][wave] = incl;
       lds_barrier();
       float wbase = 0.0f, total = 0.0f;
       for (int v = 0; v < kAcceptDrawWaves; ++v) {
-        const float x = L.wtot[v];
+        const float x = L.wtot[buf][v];
         if (v < wave) wbase += x;
         total += x;
       }
-      const float excl = carry + (wbase + (incl - run));
+      const float excl = carry + (wbase + prev);
       // the first element of this thread whose cumulative mass passes t
       float cum = excl;
       int first = -1;
@@ -402,33 +424,31 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
         }
       }
       const uint64_t hit = __ballot(first >= 0);
-      if (lane == 0) L.wfirst[wave] = hit ? (int)__builtin_ctzll(hit) : -1;
+      const int fl = hit ? (int)__builtin_ctzll(hit) : -1;
+      if (lane == 0) L.wfirst[buf][wave] = fl;
+      if (lane == fl) {
+        L.wy[buf][wave] = (int32_t)(i0 + first);
+        L.wbefore[buf][wave] = bprev;
+        L.wat[buf][wave] = bat;
+      }
       lds_barrier();
-      int winner = -1;
       for (int v = 0; v < kAcceptDrawWaves; ++v)
-        if (L.wfirst[v] >= 0) {
-          winner = v * kWave + L.wfirst[v];
+        if (L.wfirst[buf][v] >= 0) {
+          found = true;
+          y_hit = L.wy[buf][v];
+          before_hit = L.wbefore[buf][v];
+          at_hit = L.wat[buf][v];
           break;
         }
-      if (winner >= 0) {
-        if (k == winner) {
-          L.y = (int32_t)(i0 + first);
-          L.before = bprev;
-          L.at = bat;
-        }
-        lds_barrier();
-        found = true;
-        break;
-      }
+      if (found) break;  // uniform
       carry += total;
-      lds_barrier();  // wtot / wfirst reused by the next round
     }
   }
   if (k == 0) {
     float m = 0.0f;
-    if (found) m = fminf(L.t - L.before, L.at - L.t);
+    if (found) m = fminf(L.t - before_hit, at_hit - L.t);
     if (found && m >= kDrawMargin32) {
-      p.out_tokens[(int64_t)r * (D + 1) + st.tau] = L.y;
+      p.out_tokens[(int64_t)r * (D + 1) + st.tau] = y_hit;
       if (p.diag) p.diag[r].draw_margin = m;
     } else {
       const bool residual = st.mode == kDrawResidual;
@@ -443,7 +463,7 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
       jb.mode = st.mode;
       jb.r = r;
       jb.tau = st.tau;
-      jb.y32 = found ? L.y : -1;
+      jb.y32 = found ? y_hit : -1;
       jb.pad = 0;
       p.fb_jobs[atomicAdd(p.fb_count, 1)] = jb;
     }
