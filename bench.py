@@ -6,7 +6,7 @@ One step = the whole hot path on one batch already resident in HBM:
   sv_allocate_budget (prefix-confidence products + radix select of the top K)
   -> sv_verify_batch (row statistics, acceptance rates, accept scan, draw,
      and the batch's acceptance statistics, the outputs of sv_accept_stats,
-     from one spare workgroup of its last kernel).
+     from one extra workgroup of its float64 tile kernel).
 Default workload: the 64 x 16 x 151936 bf16 batch at T = 1 with the budget
 keeping every position (K = 1024).  Inputs are synthetic (seeded Gaussian
 logits shaped like the AngelSpec pages' block-drafting workload).  Four input

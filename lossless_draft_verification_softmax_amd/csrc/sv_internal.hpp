@@ -104,7 +104,7 @@ struct VerifyParams {
   float* alpha;
   sv_diag* diag;
   // acceptance statistics of the batch (sv_accept_stats outputs), each
-  // optional; computed by one extra workgroup of k_draw_pick64
+  // optional; computed by one extra workgroup of k_draw_tile64
   float* stats_expected_len;  // [B]
   float* stats_per_depth;     // [3 D]
   float* stats_summary;       // [4]
