@@ -23,6 +23,7 @@
 #include "sv_internal.hpp"
 #include "sv_drawrow.hpp"
 #include "sv_exp64.hpp"
+#include "sv_params.hpp"
 #include "sv_shard.hpp"
 #include "sv_stats.hpp"
 
@@ -719,6 +720,7 @@ __global__ __launch_bounds__(kDrawThreads, kTileBlocksPerCu) void k_draw_tile64(
     Draw64Lds d;
     StatsLds s;
   } L;
+  warm_params(p);
   const bool stats = p.stats_expected_len || p.stats_per_depth || p.stats_summary;
   if (stats && blockIdx.x == 0) {
     accept_stats_block<kDrawThreads / kWave, 4>(p.depth, p.alpha, p.accepted_len, p.B, p.D,
@@ -734,6 +736,7 @@ __global__ __launch_bounds__(kDrawThreads, kTileBlocksPerCu) void k_draw_tile64(
 template <typename E, bool SH>
 __global__ __launch_bounds__(kDrawThreads) void k_draw_pick64(VerifyParams p) {
   __shared__ Draw64Lds L;
+  warm_params(p);
   const int slot = blockIdx.x;
   const DrawJob jb = p.fb_jobs[slot];
   const double tab = exp_table_entry();
