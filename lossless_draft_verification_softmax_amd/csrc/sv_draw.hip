@@ -140,8 +140,7 @@ __device__ __forceinline__ double block_scan_d(double v, PickLds& L, int& buf, d
   return base + incl;
 }
 
-// Block total of one float64 per thread (row sums, then the 16 row totals in
-// order through LDS).
+// Block total of one float64 per thread (the total of block_scan_d).
 __device__ __forceinline__ double block_sum_d(double v, PickLds& L, int& buf) {
   double excl, tot;
   block_scan_d(v, L, buf, &excl, &tot);
