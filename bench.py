@@ -181,12 +181,12 @@ def cpu_model() -> str:
 def read_ceiling(sv, torch, dev, nbytes: int, reps: int = 10):
     """The chip's plain streaming-read rate (sv_stream_read) over two buffers
     of the row pass's algorithmic size, read alternately so that neither is
-    served from the 256 MB Infinity Cache: the best of three launch shapes."""
+    served from the 256 MB Infinity Cache: the best of four launch shapes."""
     n = (nbytes + 15) // 16 * 16
     bufs = [torch.full((n // 4,), 1.0, dtype=torch.float32, device=dev) for _ in range(2)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     best = None
-    for per_cu in (2, 4, 8):
+    for per_cu in (1, 2, 4, 8):
         for b in bufs:
             sv.stream_read(b, sink, per_cu)
         torch.cuda.synchronize()

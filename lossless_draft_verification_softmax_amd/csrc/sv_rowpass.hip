@@ -140,8 +140,8 @@ __device__ __forceinline__ void load_batch(Batch<E, kPair>& b, const typename E:
 #pragma unroll
   for (int u = 0; u < kPassUnroll; ++u) {
     const int64_t i = base + u * step;
-    b.p[u] = (i < vhi) ? load16(prow + i) : pad;
-    if constexpr (kPair) b.q[u] = (i < vhi) ? load16(qrow + i) : pad;
+    b.p[u] = (i < vhi) ? load16_keep(prow + i) : pad;
+    if constexpr (kPair) b.q[u] = (i < vhi) ? load16_keep(qrow + i) : pad;
   }
 }
 
@@ -333,7 +333,7 @@ __device__ void single_item(const VerifyParams& p, const PlanItem& it, int seg,
   ArgMax a{best, INT32_MAX};
   if (best == best && bvec >= 0) {
     float x[VEC];
-    E::unpack(load16(prow + bvec), x);
+    E::unpack(load16_keep(prow + bvec), x);
 #pragma unroll
     for (int j = VEC - 1; j >= 0; --j)
       if (x[j] == best) a.i = (int32_t)(bvec + j);
