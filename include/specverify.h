@@ -283,9 +283,9 @@ sv_status sv_verify_batch(const sv_verify_args* args, void* stream);
  * args->workspace and args->workspace_bytes are ignored; every other field,
  * the outputs and the errors are those of sv_verify_batch.  A batch whose
  * sv_verify_workspace_bytes(B, D_max, V) exceeds SV_NOALLOC_SCRATCH_BYTES is
- * rejected with SV_ERR_SCRATCH_TOO_SMALL before any GPU work (32 MiB covers,
- * for example, B = 256 requests x D_max = 16 at V = 262144, or B = 512 x 16
- * at V = 151936).  The call allocates nothing: no hipMalloc, no hipFree and
+ * rejected with SV_ERR_SCRATCH_TOO_SMALL before any GPU work (32 MiB covers
+ * D_max = 16 up to B = 354 requests at V = 262144 and up to B = 426 at
+ * V = 151936).  The call allocates nothing: no hipMalloc, no hipFree and
  * no allocating library routine.  The first call on a device resolves the
  * array's device address there (hipGetSymbolAddress, with that device
  * current), which also loads the library's code object on that device if no

@@ -58,6 +58,15 @@ def test_workspace_bytes(sv):
     assert sv.workspace_bytes(4, 3, 0) == 0
 
 
+def test_noalloc_scratch_limits(sv):
+    # the batch sizes the header states for the no-allocation entry point's
+    # 32 MiB array: the largest B at D_max = 16 fits, one more does not
+    lim = sv.SV_NOALLOC_SCRATCH_BYTES
+    for B, V in ((354, 262144), (426, 151936)):
+        assert sv.workspace_bytes(B, 16, V) <= lim
+        assert sv.workspace_bytes(B + 1, 16, V) > lim
+
+
 def _args(sv, **kw):
     a = sv.SvVerifyArgs()
     a.dtype = sv.SV_DTYPE_BF16
