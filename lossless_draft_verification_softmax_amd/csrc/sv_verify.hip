@@ -97,7 +97,8 @@ __device__ __forceinline__ bool finite_f(float x) { return x == x && x != INFINI
 // the slice, the request joins the float64 queue (sv_draw.hip).
 constexpr int kAcceptDrawThreads = 1024;
 constexpr int kAcceptDrawWaves = kAcceptDrawThreads / kWave;
-constexpr int kChunk = kAcceptDrawThreads * kPer;  // elements per scan round
+constexpr int kChunk = kAcceptDrawThreads * kPer;  // elements per scan span
+constexpr int kScanSpans = 2;                       // spans per scan round
 
 struct AcceptDrawLds {
   uint32_t bits;
@@ -107,12 +108,12 @@ struct AcceptDrawLds {
   int slice;       // crossing slice, or -1
   float c0, t;     // cumulative mass before the slice, target u R
   // per scan round (two sets used in turn, so that one barrier per
-  // exchange suffices): wavefront totals, and each wavefront's first
-  // crossing element with the cumulative masses around it
-  float wtot[2][kAcceptDrawWaves];
-  int wfirst[2][kAcceptDrawWaves];
-  int32_t wy[2][kAcceptDrawWaves];
-  float wbefore[2][kAcceptDrawWaves], wat[2][kAcceptDrawWaves];
+  // exchange suffices) and span: wavefront totals, and each wavefront's
+  // first crossing element with the cumulative masses around it
+  float wtot[2][kScanSpans][kAcceptDrawWaves];
+  int wfirst[2][kScanSpans][kAcceptDrawWaves];
+  int32_t wy[2][kScanSpans][kAcceptDrawWaves];
+  float wbefore[2][kScanSpans][kAcceptDrawWaves], wat[2][kScanSpans][kAcceptDrawWaves];
 };
 
 // Inclusive float32 scan over the wavefront in a fixed order, by DPP moves:
@@ -367,81 +368,108 @@ __global__ __launch_bounds__(kAcceptDrawThreads) void k_accept_draw(VerifyParams
   int32_t y_hit = -1;
   float before_hit = 0.0f, at_hit = 0.0f;
   if (j >= 0) {
-    // ---- scan inside slice j, kChunk elements per round ----
+    // ---- scan inside slice j, kScanSpans spans of kChunk elements per round ----
     Weights32<E, SH> wt = weights32<E, SH>(p, st);
     const float t = L.t;
     float carry = L.c0;
     const int64_t lo = (int64_t)j * slen;
     const int64_t hi = min(p.V, lo + slen);
-    // Each round's raw logits are loaded one round ahead, and the barriers
-    // inside the loop order LDS only, so the next round's loads stay in
-    // flight while this round is scanned.
-    Raw8<E> cur, nxt;
-    if (lo + (int64_t)k * kPer < hi)
-      load_raw8<E, SH>(wt.prow, wt.qrow, wt.has_q, lo + (int64_t)k * kPer, hi, cur);
+    // Thread k takes kPer elements of each span.  Span g is scanned as a
+    // round of its own would be (wave totals in order, then the carry of the
+    // spans before it), so the cumulative masses and the first crossing are
+    // those of single-span rounds one after another; the spans share the
+    // loads' latency and the round's two barriers.  Each round's raw logits
+    // are loaded one round ahead, and the barriers order LDS only, so those
+    // loads stay in flight while this round is scanned.
+    constexpr int64_t kRound = (int64_t)kScanSpans * kChunk;
+    Raw8<E> cur[kScanSpans], nxt[kScanSpans];
+#pragma unroll
+    for (int g = 0; g < kScanSpans; ++g) {
+      const int64_t i0 = lo + g * kChunk + (int64_t)k * kPer;
+      if (i0 < hi) load_raw8<E, SH>(wt.prow, wt.qrow, wt.has_q, i0, hi, cur[g]);
+    }
     int buf = 0;
-    for (int64_t base = lo; base < hi; base += kChunk, buf ^= 1) {
-      const int64_t i0 = base + (int64_t)k * kPer;
-      if (i0 + kChunk < hi) load_raw8<E, SH>(wt.prow, wt.qrow, wt.has_q, i0 + kChunk, hi, nxt);
-      float w[kPer];
-      if (i0 < hi) {
-        float a[kPer], b[kPer];
-        unpack_raw8<E, SH>(cur, wt.prow, wt.qrow, wt.has_q, i0, hi, a, b);
-        wt.from(a, b, w);
-      } else {
+    for (int64_t base = lo; base < hi; base += kRound, buf ^= 1) {
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) w[e] = 0.0f;
+      for (int g = 0; g < kScanSpans; ++g) {
+        const int64_t i0 = base + g * kChunk + (int64_t)k * kPer;
+        if (i0 + kRound < hi)
+          load_raw8<E, SH>(wt.prow, wt.qrow, wt.has_q, i0 + kRound, hi, nxt[g]);
       }
-      cur = nxt;
-      float run = 0.0f;
+      float w[kScanSpans][kPer], prev[kScanSpans];
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) run += w[e];
-      // block exclusive scan of the thread sums (wavefront scans, wave
-      // totals in order)
-      const float incl = wave_scan_f(run);
-      const float prev = wave_prev_f(incl);
-      if (lane == kWave - 1) L.wtot[buf][wave] = incl;
-      lds_barrier();
-      float wbase = 0.0f, total = 0.0f;
-      for (int v = 0; v < kAcceptDrawWaves; ++v) {
-        const float x = L.wtot[buf][v];
-        if (v < wave) wbase += x;
-        total += x;
-      }
-      const float excl = carry + (wbase + prev);
-      // the first element of this thread whose cumulative mass passes t
-      float cum = excl;
-      int first = -1;
-      float bprev = 0.0f, bat = 0.0f;
+      for (int g = 0; g < kScanSpans; ++g) {
+        const int64_t i0 = base + g * kChunk + (int64_t)k * kPer;
+        if (i0 < hi) {
+          float a[kPer], b[kPer];
+          unpack_raw8<E, SH>(cur[g], wt.prow, wt.qrow, wt.has_q, i0, hi, a, b);
+          wt.from(a, b, w[g]);
+        } else {
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const float prev = cum;
-        cum += w[e];
-        if (first < 0 && w[e] > 0.0f && cum > t) {
-          first = e;
-          bprev = prev;
-          bat = cum;
+          for (int e = 0; e < kPer; ++e) w[g][e] = 0.0f;
         }
-      }
-      const uint64_t hit = __ballot(first >= 0);
-      const int fl = hit ? (int)__builtin_ctzll(hit) : -1;
-      if (lane == 0) L.wfirst[buf][wave] = fl;
-      if (lane == fl) {
-        L.wy[buf][wave] = (int32_t)(i0 + first);
-        L.wbefore[buf][wave] = bprev;
-        L.wat[buf][wave] = bat;
+        cur[g] = nxt[g];
+        float run = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) run += w[g][e];
+        // block exclusive scan of the thread sums (wavefront scans, wave
+        // totals in order)
+        const float incl = wave_scan_f(run);
+        prev[g] = wave_prev_f(incl);
+        if (lane == kWave - 1) L.wtot[buf][g][wave] = incl;
       }
       lds_barrier();
-      for (int v = 0; v < kAcceptDrawWaves; ++v)
-        if (L.wfirst[buf][v] >= 0) {
-          found = true;
-          y_hit = L.wy[buf][v];
-          before_hit = L.wbefore[buf][v];
-          at_hit = L.wat[buf][v];
-          break;
+      float gcarry = carry;
+#pragma unroll
+      for (int g = 0; g < kScanSpans; ++g) {
+        const int64_t i0 = base + g * kChunk + (int64_t)k * kPer;
+        float wbase = 0.0f, total = 0.0f;
+        for (int v = 0; v < kAcceptDrawWaves; ++v) {
+          const float x = L.wtot[buf][g][v];
+          if (v < wave) wbase += x;
+          total += x;
         }
+        const float excl = gcarry + (wbase + prev[g]);
+        // the first element of this thread whose cumulative mass passes t
+        float cum = excl;
+        int first = -1;
+        float bprev = 0.0f, bat = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const float before = cum;
+          cum += w[g][e];
+          if (first < 0 && w[g][e] > 0.0f && cum > t) {
+            first = e;
+            bprev = before;
+            bat = cum;
+          }
+        }
+        const uint64_t hit = __ballot(first >= 0);
+        const int fl = hit ? (int)__builtin_ctzll(hit) : -1;
+        if (lane == 0) L.wfirst[buf][g][wave] = fl;
+        if (lane == fl) {
+          L.wy[buf][g][wave] = (int32_t)(i0 + first);
+          L.wbefore[buf][g][wave] = bprev;
+          L.wat[buf][g][wave] = bat;
+        }
+        gcarry += total;
+      }
+      lds_barrier();
+      // the first span with a crossing, and in it the first wavefront
+#pragma unroll
+      for (int g = 0; g < kScanSpans; ++g) {
+        if (found) break;
+        for (int v = 0; v < kAcceptDrawWaves; ++v)
+          if (L.wfirst[buf][g][v] >= 0) {
+            found = true;
+            y_hit = L.wy[buf][g][v];
+            before_hit = L.wbefore[buf][g][v];
+            at_hit = L.wat[buf][g][v];
+            break;
+          }
+      }
       if (found) break;  // uniform
-      carry += total;
+      carry = gcarry;
     }
   }
   if (k == 0) {
